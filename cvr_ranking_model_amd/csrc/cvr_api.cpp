@@ -1,0 +1,599 @@
+// Host side of the libcvr C ABI: spec validation, weight packing, workspace planning and the
+// per-batch launch sequence.  All device work goes to the caller's stream; no device memory is
+// allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/cvr.h"
+#include "kernels.h"
+#include "model.h"
+
+using namespace cvr;
+
+static thread_local std::string g_last_error;
+
+static cvr_status fail(cvr_model* m, cvr_status s, const std::string& msg) {
+  if (m) m->err = msg;
+  g_last_error = msg;
+  return s;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------------ spec checks
+
+static bool supported_dim(int d) { return d == 4 || d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+static cvr_status check_spec(const cvr_spec* s, const cvr_table* tables, int32_t n_tables, std::string& why) {
+  if (!s) { why = "spec is null"; return CVR_ERR_ARG; }
+  if (!tables || n_tables <= 0) { why = "no tables"; return CVR_ERR_ARG; }
+  if (s->model != CVR_MODEL_DLRM && s->model != CVR_MODEL_HYFORMER) { why = "unknown model"; return CVR_ERR_SPEC; }
+  if (s->lowp != CVR_LOWP_FP16 && s->lowp != CVR_LOWP_BF16) { why = "unknown lowp type"; return CVR_ERR_SPEC; }
+  if (!(s->clamp > 0.f) || !std::isfinite(s->clamp)) { why = "clamp bound must be positive"; return CVR_ERR_SPEC; }
+  if (s->n_features <= 0 || !s->features) { why = "no features"; return CVR_ERR_SPEC; }
+  if (s->n_features > kMaxGatherFeatures) { why = "too many features (max 32)"; return CVR_ERR_UNSUPPORTED; }
+  for (int i = 0; i < n_tables; ++i) {
+    if (tables[i].rows <= 0 || tables[i].rows > INT32_MAX) { why = "table rows must be in [1, 2^31)"; return CVR_ERR_SPEC; }
+    if (!supported_dim(tables[i].dim)) { why = "table dim must be one of 4, 8, 16, 32, 64, 128, 256"; return CVR_ERR_UNSUPPORTED; }
+  }
+  for (int f = 0; f < s->n_features; ++f) {
+    const cvr_feature& F = s->features[f];
+    if (F.table < 0 || F.table >= n_tables) { why = "feature table index out of range"; return CVR_ERR_SPEC; }
+    if (F.side != CVR_SIDE_USER && F.side != CVR_SIDE_ITEM && F.side != CVR_SIDE_CONTEXT) { why = "bad feature side"; return CVR_ERR_SPEC; }
+  }
+  if (s->model == CVR_MODEL_DLRM) {
+    if (s->lowp != CVR_LOWP_FP16 && s->lowp != CVR_LOWP_BF16) { why = "bad lowp"; return CVR_ERR_SPEC; }
+    if (s->n_hidden < 0 || (s->n_hidden > 0 && !s->hidden)) { why = "bad hidden layer list"; return CVR_ERR_SPEC; }
+    for (int i = 0; i < s->n_hidden; ++i)
+      if (s->hidden[i] <= 0 || s->hidden[i] % 32) { why = "hidden widths must be positive multiples of 32"; return CVR_ERR_UNSUPPORTED; }
+  } else {
+    if (s->d != 128) { why = "token width d must be 128"; return CVR_ERR_UNSUPPORTED; }
+    if (s->n_tokens <= 0 || s->n_layers <= 0 || s->n_seq <= 0 || s->n_seq > 4) { why = "bad token/layer/sequence counts"; return CVR_ERR_SPEC; }
+    if (s->n_seq_cols <= 0 || !s->seq_tables || s->n_seq_cols > 8) { why = "bad sequence columns"; return CVR_ERR_SPEC; }
+    int sd = 0;
+    for (int c = 0; c < s->n_seq_cols; ++c) {
+      if (s->seq_tables[c] < 0 || s->seq_tables[c] >= n_tables) { why = "sequence table index out of range"; return CVR_ERR_SPEC; }
+      sd += tables[s->seq_tables[c]].dim;
+    }
+    if (sd != s->d) { why = "sequence column dims must sum to d"; return CVR_ERR_SPEC; }
+    const int T = s->n_tokens + s->n_seq;
+    if (s->mixer_heads <= 0 || s->d % s->mixer_heads || (s->d / s->mixer_heads) % 8) { why = "mixer heads must split d into chunks of a multiple of 8"; return CVR_ERR_UNSUPPORTED; }
+    if ((T * (s->d / s->mixer_heads)) % 32) { why = "mixed-token width must be a multiple of 32"; return CVR_ERR_UNSUPPORTED; }
+    if (s->swiglu_hidden != 256) { why = "SwiGLU hidden width must be 256"; return CVR_ERR_UNSUPPORTED; }
+    if (s->mixer_hidden <= 0 || s->mixer_hidden % 32 || s->expert_dim <= 0 || s->expert_dim % 32 ||
+        s->head_hidden <= 0 || s->head_hidden % 32) { why = "mixer/expert/head widths must be multiples of 32"; return CVR_ERR_UNSUPPORTED; }
+    if (s->n_experts <= 0 || s->n_experts > 8 || s->n_tasks <= 0 || s->n_tasks > 8) { why = "bad expert/task counts"; return CVR_ERR_SPEC; }
+    if (!(s->tau > 0.f) || !std::isfinite(s->tau)) { why = "tau must be positive"; return CVR_ERR_SPEC; }
+  }
+  return CVR_OK;
+}
+
+// ------------------------------------------------------------------ derived layout
+
+static void derive(cvr_model* m) {
+  const cvr_spec& s = m->spec;
+  m->fcol.assign(s.n_features, 0);
+  m->D_req = m->D_item = 0;
+  m->e_dim = 0;
+  for (int f = 0; f < s.n_features; ++f) {
+    const int dim = m->tables[m->feats[f].table].dim;
+    if (m->feats[f].side == CVR_SIDE_ITEM) { m->fcol[f] = m->D_item; m->D_item += dim; }
+    else { m->fcol[f] = m->D_req; m->D_req += dim; }
+    m->e_dim += dim;
+  }
+  m->ld_req = (m->D_req + 7) / 8 * 8;
+  m->ld_item = (m->D_item + 7) / 8 * 8;
+  // K-segments of the model input, merging neighbouring features of the same side.
+  m->segs.clear();
+  int k = 0;
+  for (int f = 0; f < s.n_features; ++f) {
+    const int dim = m->tables[m->feats[f].table].dim;
+    const bool item = m->feats[f].side == CVR_SIDE_ITEM;
+    if (!m->segs.empty() && m->segs.back().item == item) m->segs.back().k_end += dim;
+    else m->segs.push_back({item, k + dim, m->fcol[f]});
+    k += dim;
+  }
+}
+
+// Weight arena plan.  Entries listed together are placed back to back so that grouped GEMMs
+// can step through them with one stride.
+static void plan_weights(cvr_model* m) {
+  const cvr_spec& s = m->spec;
+  m->w.clear();
+  m->widx.clear();
+  size_t off = 0;
+  auto add = [&](const std::string& name, int64_t rows, int64_t cols, bool matrix) {
+    WEntry e{name, rows, cols, matrix, off};
+    off = align256(off + (size_t)rows * cols * (matrix ? 2 : 4));
+    m->widx[name] = (int)m->w.size();
+    m->w.push_back(e);
+  };
+  if (s.model == CVR_MODEL_DLRM) {
+    int in = m->e_dim;
+    for (int i = 0; i <= s.n_hidden; ++i) {
+      const int out = i < s.n_hidden ? m->hidden[i] : 1;
+      add("mlp." + std::to_string(i) + ".weight", out, in, true);
+      add("mlp." + std::to_string(i) + ".bias", out, 1, false);
+      in = out;
+    }
+  } else {
+    const int d = s.d, N = s.n_tokens, S = s.n_seq, T = N + S, hs = s.swiglu_hidden;
+    const int mw = T * d / s.mixer_heads;
+    add("tok.weight", (int64_t)N * d, m->e_dim, true);
+    add("tok.bias", (int64_t)N * d, 1, false);
+    for (int q = 0; q < S; ++q) {
+      // gate and up back to back: one [2*hs][d] matrix per sequence
+      add("seq." + std::to_string(q) + ".gate.weight", hs, d, true);
+      add("seq." + std::to_string(q) + ".up.weight", hs, d, true);
+      add("seq." + std::to_string(q) + ".gate.bias", hs, 1, false);
+      add("seq." + std::to_string(q) + ".up.bias", hs, 1, false);
+      add("seq." + std::to_string(q) + ".down.weight", d, hs, true);
+      add("seq." + std::to_string(q) + ".down.bias", d, 1, false);
+    }
+    for (int l = 0; l < s.n_layers; ++l) {
+      const std::string L = "layer." + std::to_string(l);
+      for (int q = 0; q < S; ++q) add(L + ".query." + std::to_string(q) + ".weight", d, (int64_t)(N + 1) * d, true);
+      for (int q = 0; q < S; ++q) add(L + ".query." + std::to_string(q) + ".bias", d, 1, false);
+      for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc1.weight", s.mixer_hidden, mw, true);
+      for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc1.bias", s.mixer_hidden, 1, false);
+      for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc2.weight", mw, s.mixer_hidden, true);
+      for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc2.bias", mw, 1, false);
+    }
+    const int zd = T * d;
+    for (int e = 0; e < s.n_experts; ++e) add("ple.expert." + std::to_string(e) + ".weight", s.expert_dim, zd, true);
+    for (int e = 0; e < s.n_experts; ++e) add("ple.expert." + std::to_string(e) + ".bias", s.expert_dim, 1, false);
+    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".weight", s.n_experts, zd, true);
+    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".bias", s.n_experts, 1, false);
+    for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc1.weight", s.head_hidden, s.expert_dim, true);
+    for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc1.bias", s.head_hidden, 1, false);
+    for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc2.weight", 1, s.head_hidden, true);
+    for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc2.bias", 1, 1, false);
+  }
+  m->arena_bytes = align256(off);
+}
+
+static cvr_model* new_model(const cvr_spec* spec, const cvr_table* tables, int32_t n_tables) {
+  cvr_model* m = new cvr_model();
+  m->spec = *spec;
+  m->feats.assign(spec->features, spec->features + spec->n_features);
+  m->spec.features = m->feats.data();
+  if (spec->model == CVR_MODEL_DLRM && spec->n_hidden > 0) m->hidden.assign(spec->hidden, spec->hidden + spec->n_hidden);
+  m->spec.hidden = m->hidden.data();
+  if (spec->model == CVR_MODEL_HYFORMER) m->seq_tables.assign(spec->seq_tables, spec->seq_tables + spec->n_seq_cols);
+  m->spec.seq_tables = m->seq_tables.data();
+  m->tables.assign(tables, tables + n_tables);
+  derive(m);
+  plan_weights(m);
+  return m;
+}
+
+static cvr_status check_segments(const cvr_model* m, std::string& why) {
+  if (m->segs.size() > (size_t)kMaxASegments) { why = "model input alternates sides too often (max 4 runs)"; return CVR_ERR_UNSUPPORTED; }
+  for (const auto& sg : m->segs)
+    if (sg.k_end % 8 || sg.col0 % 8) { why = "each run of same-side features must be a multiple of 8 columns"; return CVR_ERR_UNSUPPORTED; }
+  if (m->e_dim % 32) { why = "model input width must be a multiple of 32"; return CVR_ERR_UNSUPPORTED; }
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_weight_arena_bytes(const cvr_spec* spec, const cvr_table* tables, int32_t n_tables,
+                                             size_t* bytes) {
+  std::string why;
+  if (!bytes) return fail(nullptr, CVR_ERR_ARG, "bytes is null");
+  cvr_status st = check_spec(spec, tables, n_tables, why);
+  if (st != CVR_OK) return fail(nullptr, st, why);
+  cvr_model* m = new_model(spec, tables, n_tables);
+  *bytes = m->arena_bytes;
+  delete m;
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, int32_t n_tables,
+                                 const cvr_weight* weights, int32_t n_weights, void* weight_arena,
+                                 size_t arena_bytes, void* hip_stream, cvr_handle* out) {
+  if (!out) return fail(nullptr, CVR_ERR_ARG, "out is null");
+  *out = nullptr;
+  std::string why;
+  cvr_status st = check_spec(spec, tables, n_tables, why);
+  if (st != CVR_OK) return fail(nullptr, st, why);
+  for (int i = 0; i < n_tables; ++i)
+    if (!tables[i].data || ((uintptr_t)tables[i].data & 15)) return fail(nullptr, CVR_ERR_ARG, "table data must be non-null and 16-byte aligned");
+  cvr_model* m = new_model(spec, tables, n_tables);
+  st = check_segments(m, why);
+  if (st != CVR_OK) { delete m; return fail(nullptr, st, why); }
+  if (!weight_arena || ((uintptr_t)weight_arena & 255)) { delete m; return fail(nullptr, CVR_ERR_ARG, "weight arena must be non-null and 256-byte aligned"); }
+  if (arena_bytes < m->arena_bytes) { delete m; return fail(nullptr, CVR_ERR_WORKSPACE, "weight arena too small"); }
+  if (!weights || n_weights <= 0) { delete m; return fail(nullptr, CVR_ERR_SPEC, "no weights given"); }
+  m->arena = (char*)weight_arena;
+  hipStream_t s = (hipStream_t)hip_stream;
+  std::vector<int> seen(m->w.size(), 0);
+  for (int i = 0; i < n_weights; ++i) {
+    if (!weights[i].name) { delete m; return fail(nullptr, CVR_ERR_ARG, "weight without a name"); }
+    auto it = m->widx.find(weights[i].name);
+    if (it == m->widx.end()) { std::string n = weights[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "unexpected weight " + n); }
+    const WEntry& e = m->w[it->second];
+    if (weights[i].numel != e.rows * e.cols) {
+      std::string n = weights[i].name; delete m;
+      return fail(nullptr, CVR_ERR_SPEC, "weight " + n + " has " + std::to_string(weights[i].numel) + " elements, expected " + std::to_string(e.rows * e.cols));
+    }
+    if (!weights[i].data) { delete m; return fail(nullptr, CVR_ERR_ARG, "weight data is null"); }
+    if (seen[it->second]++) { std::string n = weights[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "weight given twice: " + n); }
+    hipError_t he;
+    if (e.matrix) he = launch_convert(weights[i].data, m->arena + e.off, e.rows * e.cols, m->spec.lowp, s);
+    else he = hipMemcpyAsync(m->arena + e.off, weights[i].data, (size_t)e.rows * 4, hipMemcpyDeviceToDevice, s);
+    if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("packing weights: ") + hipGetErrorString(he)); }
+  }
+  for (size_t i = 0; i < seen.size(); ++i)
+    if (!seen[i]) { std::string n = m->w[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "missing weight " + n); }
+  hipError_t he = hipStreamSynchronize(s);
+  if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("create sync: ") + hipGetErrorString(he)); }
+  *out = m;
+  return CVR_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+
+WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) {
+  const cvr_spec& s = m->spec;
+  WsPlan w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t lp = 2;
+  w.flag = take(256);
+  w.cand_req = take((size_t)n * 4);
+  w.x_req = take((size_t)R * m->ld_req * lp);
+  w.x_item = take((size_t)n * m->ld_item * lp);
+  const int ntasks = s.model == CVR_MODEL_DLRM ? 1 : s.n_tasks;
+  w.logits = take((size_t)n * ntasks * 4);
+  size_t pooled = 0;
+  for (int f = 0; f < s.n_features; ++f)
+    pooled += (size_t)(m->feats[f].side == CVR_SIDE_ITEM ? n : R) * m->tables[m->feats[f].table].dim * 4;
+  w.pooled = m->debug ? take(pooled) : 0;
+  w.pooled_bytes = m->debug ? pooled : 0;
+  if (s.model == CVR_MODEL_DLRM) {
+    int maxw = 1;
+    for (int i = 0; i < s.n_hidden; ++i) maxw = std::max(maxw, m->hidden[i]);
+    w.h[0] = take((size_t)n * maxw * lp);
+    w.h[1] = take((size_t)n * maxw * lp);
+  } else {
+    const int64_t d = s.d, S = s.n_seq, T = s.n_tokens + s.n_seq;
+    w.tok[0] = take((size_t)n * T * d * lp);
+    w.tok[1] = take((size_t)n * T * d * lp);
+    w.hseq = take((size_t)P * d * lp);
+    w.chunk_off = take((size_t)(S * R + 1) * 4);
+    w.pool_part = take((size_t)(P / kSeqChunk + S * R + 1) * d * 4);
+    w.seq_pool = take((size_t)S * R * d * 4);
+    w.seq_pool_lp = take((size_t)S * R * d * lp);
+    w.query = take((size_t)S * n * d * lp);
+    w.mixhid = take((size_t)s.mixer_heads * n * s.mixer_hidden * lp);
+    w.experts = take((size_t)n * s.n_experts * s.expert_dim * lp);
+    w.gates = take((size_t)n * s.n_tasks * s.n_experts * 4);
+    w.task_in = take((size_t)s.n_tasks * n * s.expert_dim * lp);
+    w.head_hid = take((size_t)s.n_tasks * n * s.head_hidden * lp);
+  }
+  w.total = align256(off);
+  return w;
+}
+
+extern "C" cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_candidates, int64_t max_ids,
+                                          int64_t max_positions, size_t* bytes) {
+  if (!h || !bytes) return fail(h, CVR_ERR_ARG, "null argument");
+  if (max_requests < 0 || max_candidates < 0 || max_ids < 0 || max_positions < 0) return fail(h, CVR_ERR_ARG, "negative size");
+  *bytes = plan_workspace(h, max_requests, max_candidates, h->spec.model == CVR_MODEL_DLRM ? 0 : max_positions).total;
+  return CVR_OK;
+}
+
+// ------------------------------------------------------------------ timing
+
+void Timing::reset() {
+  for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  ev.clear();
+  stage.clear();
+  armed = false;
+  calls = 0;
+  max_calls = 0;
+  launch_in_call = 0;
+}
+
+extern "C" cvr_status cvr_timing_begin(cvr_handle h, int32_t max_calls) {
+  if (!h || max_calls <= 0 || max_calls > 100000) return fail(h, CVR_ERR_ARG, "bad timing request");
+  h->timing.reset();
+  h->timing.ev.resize((size_t)max_calls * kMaxLaunchesPerCall * 2);
+  h->timing.stage.assign((size_t)max_calls * kMaxLaunchesPerCall, -1);
+  for (auto& e : h->timing.ev)
+    if (hipEventCreate(&e) != hipSuccess) { h->timing.ev.clear(); return fail(h, CVR_ERR_HIP, "hipEventCreate failed"); }
+  h->timing.max_calls = max_calls;
+  h->timing.armed = true;
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_timing_end(cvr_handle h, double* stage_ms, int32_t* stage_launches, int32_t max_stages,
+                                     int32_t* n_stages, int32_t* n_calls) {
+  if (!h) return fail(h, CVR_ERR_ARG, "null handle");
+  Timing& t = h->timing;
+  std::vector<double> ms(kNumStages, 0.0);
+  std::vector<int> cnt(kNumStages, 0);
+  for (int c = 0; c < t.calls; ++c)
+    for (int l = 0; l < kMaxLaunchesPerCall; ++l) {
+      const size_t slot = (size_t)c * kMaxLaunchesPerCall + l;
+      const int st = t.stage[slot];
+      if (st < 0) continue;
+      if (hipEventSynchronize(t.ev[2 * slot + 1]) != hipSuccess) return fail(h, CVR_ERR_HIP, "event sync failed");
+      float f = 0.f;
+      if (hipEventElapsedTime(&f, t.ev[2 * slot], t.ev[2 * slot + 1]) != hipSuccess) return fail(h, CVR_ERR_HIP, "elapsed time failed");
+      ms[st] += f;
+      cnt[st] += 1;
+    }
+  for (int i = 0; i < kNumStages && i < max_stages; ++i) {
+    if (stage_ms) stage_ms[i] = ms[i];
+    if (stage_launches) stage_launches[i] = cnt[i];
+  }
+  if (n_stages) *n_stages = kNumStages;
+  if (n_calls) *n_calls = t.calls;
+  t.reset();
+  return CVR_OK;
+}
+
+extern "C" const char* cvr_stage_name(cvr_handle, int32_t stage) {
+  static const char* names[kNumStages] = {"expand", "gather_pool", "mlp_gemm", "dlrm_output", "tokenize_gemm",
+                                          "swiglu", "seq_pool", "query_gemm", "attention", "mixer_gemm",
+                                          "ple_gemm", "ple_gate", "head_gemm", "head_out"};
+  return (stage >= 0 && stage < kNumStages) ? names[stage] : "";
+}
+
+// ------------------------------------------------------------------ scoring
+
+
+static cvr_status check_batch(cvr_model* m, const cvr_batch* b, void* ws, size_t ws_bytes, float* out, WsPlan& plan) {
+  if (!b || !ws || !out) return fail(m, CVR_ERR_ARG, "null batch, workspace or output");
+  if ((uintptr_t)ws & 255) return fail(m, CVR_ERR_ARG, "workspace must be 256-byte aligned");
+  if (b->n_requests <= 0) return fail(m, CVR_ERR_ARG, "n_requests must be >= 1");
+  if (b->n_candidates < 0 || b->n_ids < 0 || b->n_positions < 0) return fail(m, CVR_ERR_ARG, "negative size");
+  if (b->n_ids > INT32_MAX || b->n_positions > INT32_MAX) return fail(m, CVR_ERR_ARG, "ids/positions must fit int32");
+  if (!b->cand_offsets || !b->bag_offsets || (b->n_ids > 0 && !b->ids)) return fail(m, CVR_ERR_ARG, "null CSR array");
+  if (m->spec.model == CVR_MODEL_HYFORMER && (!b->seq_offsets || (b->n_positions > 0 && !b->seq_ids)))
+    return fail(m, CVR_ERR_ARG, "CVR model needs seq_offsets and seq_ids");
+  plan = plan_workspace(m, b->n_requests, b->n_candidates, m->spec.model == CVR_MODEL_DLRM ? 0 : b->n_positions);
+  if (ws_bytes < plan.total) return fail(m, CVR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.total) + " bytes");
+  return CVR_OK;
+}
+
+// Shared front of both models: flag clear, expand, gather-pool into the two input matrices.
+static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan& w, Launcher& L, hipStream_t s) {
+  const cvr_spec& sp = m->spec;
+  int32_t* flag = (int32_t*)(ws + w.flag);
+  int64_t total_bags = 0;
+  for (int f = 0; f < sp.n_features; ++f) total_bags += sp.features[f].side == CVR_SIDE_ITEM ? b->n_candidates : b->n_requests;
+  hipError_t e = L(STAGE_EXPAND, [&] { return launch_clear_flag(flag, s); });
+  if (e != hipSuccess) return e;
+  ExpandParams ep{};
+  ep.cand_offsets = b->cand_offsets;
+  ep.R = b->n_requests;
+  ep.n = b->n_candidates;
+  ep.bag_offsets = b->bag_offsets;
+  ep.total_bags = total_bags;
+  ep.n_ids = b->n_ids;
+  ep.seq_offsets = sp.model == CVR_MODEL_HYFORMER ? b->seq_offsets : nullptr;
+  ep.S = sp.model == CVR_MODEL_HYFORMER ? sp.n_seq : 0;
+  ep.n_positions = b->n_positions;
+  ep.cand_req = (int32_t*)(ws + w.cand_req);
+  ep.flag = flag;
+  e = L(STAGE_EXPAND, [&] { return launch_expand(ep, s); });
+  if (e != hipSuccess) return e;
+
+  GatherParams gp{};
+  gp.nf = sp.n_features;
+  gp.bag_offsets = b->bag_offsets;
+  gp.ids = b->ids;
+  gp.n_ids = b->n_ids;
+  gp.clamp = sp.clamp;
+  gp.lowp = sp.lowp;
+  gp.flag = flag;
+  int64_t base = 0;
+  size_t dbg = w.pooled;
+  for (int f = 0; f < sp.n_features; ++f) {
+    const cvr_table& t = m->tables[sp.features[f].table];
+    const bool item = sp.features[f].side == CVR_SIDE_ITEM;
+    GatherFeature& F = gp.f[f];
+    F.table = t.data;
+    F.rows = t.rows;
+    F.dim = t.dim;
+    F.nbags = item ? b->n_candidates : b->n_requests;
+    F.bag_base = base;
+    F.out = ws + (item ? w.x_item : w.x_req);
+    F.ldo = item ? m->ld_item : m->ld_req;
+    F.col = m->fcol[f];
+    F.dbg = m->debug ? (float*)(ws + dbg) : nullptr;
+    dbg += (size_t)F.nbags * t.dim * 4;
+    base += F.nbags;
+  }
+  return L(STAGE_GATHER, [&] { return launch_gather_pool(gp, s); });
+}
+
+// The model input as GEMM K-segments (request-side runs read through cand_req).
+static void input_segments(const cvr_model* m, char* ws, const WsPlan& w, GemmParams& g) {
+  g.nseg = (int)m->segs.size();
+  for (size_t i = 0; i < m->segs.size(); ++i) {
+    const InputSeg& sg = m->segs[i];
+    ASeg& a = g.seg[i];
+    a.ptr = ws + (sg.item ? w.x_item : w.x_req);
+    a.rowmap = sg.item ? nullptr : (const int32_t*)(ws + w.cand_req);
+    a.ld = sg.item ? m->ld_item : m->ld_req;
+    a.gstride = 0;
+    a.k_end = sg.k_end;
+    a.kstride8 = 8;
+    a.col0 = sg.col0;
+  }
+}
+
+static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan& w, float* out, Launcher& L,
+                           hipStream_t s) {
+  const cvr_spec& sp = m->spec;
+  const int n = b->n_candidates;
+  hipError_t e = hipSuccess;
+  int in = m->e_dim;
+  int cur = -1;
+  for (int i = 0; i < sp.n_hidden; ++i) {
+    const int width = m->hidden[i];
+    GemmParams g{};
+    g.M = n;
+    g.N = width;
+    g.K = in;
+    g.groups = 1;
+    if (i == 0) input_segments(m, ws, w, g);
+    else {
+      g.nseg = 1;
+      g.seg[0] = ASeg{ws + w.h[cur], nullptr, (int64_t)in, 0, in, 8, 0, 0};
+    }
+    g.W = m->wptr("mlp." + std::to_string(i) + ".weight");
+    g.bias = (const float*)m->wptr("mlp." + std::to_string(i) + ".bias");
+    const int nxt = cur == 0 ? 1 : 0;
+    g.C = ws + w.h[nxt];
+    g.ldc = width;
+    g.c_nstride8 = 8;
+    g.relu = 1;
+    e = L(STAGE_MLP_GEMM, [&] { return launch_gemm(g, sp.lowp, s); });
+    if (e != hipSuccess) return e;
+    cur = nxt;
+    in = width;
+  }
+  m->last_hidden_buf = cur < 0 ? 0 : cur;
+  const void* H = cur < 0 ? nullptr : ws + w.h[cur];
+  if (cur < 0) return hipErrorInvalidValue;  // zero hidden layers: not supported by the output kernel
+  const int L_ = sp.n_hidden;
+  return L(STAGE_DLRM_OUTPUT, [&] {
+    return launch_dlrm_output(H, n, in, m->wptr("mlp." + std::to_string(L_) + ".weight"),
+                              (const float*)m->wptr("mlp." + std::to_string(L_) + ".bias"),
+                              (float*)(ws + w.logits), out, sp.lowp, s);
+  });
+}
+
+extern "C" cvr_status cvr_score(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes, float* out_scores,
+                                void* hip_stream) {
+  if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
+  WsPlan plan;
+  cvr_status st = check_batch(h, b, workspace, ws_bytes, out_scores, plan);
+  if (st != CVR_OK) return st;
+  if (h->spec.model == CVR_MODEL_DLRM && h->spec.n_hidden == 0) return fail(h, CVR_ERR_UNSUPPORTED, "DLRM without hidden layers");
+  hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  h->last_ws = ws;
+  h->last_plan = plan;
+  h->last_R = b->n_requests;
+  h->last_n = b->n_candidates;
+  h->last_P = b->n_positions;
+  h->last_debug = h->debug;
+  Launcher L(h, s);
+  hipError_t e = run_front(h, b, ws, plan, L, s);
+  if (e == hipSuccess && b->n_candidates > 0) {
+    if (h->spec.model == CVR_MODEL_DLRM) e = run_dlrm(h, b, ws, plan, out_scores, L, s);
+    else e = run_hyformer(h, b, ws, plan, out_scores, L, s);
+  }
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_sync_status(cvr_handle h, void* hip_stream) {
+  if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
+  hipStream_t s = (hipStream_t)hip_stream;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("stream sync: ") + hipGetErrorString(e));
+  if (!h->last_ws) return CVR_OK;
+  int32_t flag = 0;
+  e = hipMemcpy(&flag, h->last_ws + h->last_plan.flag, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("reading status: ") + hipGetErrorString(e));
+  if (flag) {
+    std::string why = "device check failed:";
+    if (flag & ERRF_CAND_OFFSETS) why += " cand_offsets malformed;";
+    if (flag & ERRF_BAG_OFFSETS) why += " bag_offsets malformed;";
+    if (flag & ERRF_ID_RANGE) why += " id outside its table;";
+    if (flag & ERRF_SEQ_OFFSETS) why += " seq_offsets malformed;";
+    if (flag & ERRF_SEQ_ID_RANGE) why += " sequence id outside its table;";
+    return fail(h, CVR_ERR_RANGE, why);
+  }
+  return CVR_OK;
+}
+
+// ------------------------------------------------------------------ debug export
+
+extern "C" cvr_status cvr_set_debug(cvr_handle h, int32_t debug) {
+  if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
+  h->debug = debug ? 1 : 0;
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, size_t dst_bytes, size_t* written,
+                                       void* hip_stream) {
+  if (!h || !dst) return fail(h, CVR_ERR_ARG, "null argument");
+  if (!h->last_ws) return fail(h, CVR_ERR_ARG, "nothing scored yet");
+  const WsPlan& w = h->last_plan;
+  const cvr_spec& sp = h->spec;
+  const size_t R = h->last_R, n = h->last_n, P = h->last_P;
+  size_t off = 0, bytes = 0;
+  const bool cvr = sp.model == CVR_MODEL_HYFORMER;
+  const size_t d = sp.d, S = sp.n_seq, T = sp.n_tokens + sp.n_seq;
+  switch (what) {
+    case CVR_DBG_CAND_REQ: off = w.cand_req; bytes = n * 4; break;
+    case CVR_DBG_POOLED:
+      if (!h->last_debug) return fail(h, CVR_ERR_ARG, "pooled values need cvr_set_debug(1) before scoring");
+      off = w.pooled; bytes = w.pooled_bytes; break;
+    case CVR_DBG_INPUT_REQ: off = w.x_req; bytes = R * h->ld_req * 2; break;
+    case CVR_DBG_INPUT_ITEM: off = w.x_item; bytes = n * h->ld_item * 2; break;
+    case CVR_DBG_LOGITS: off = w.logits; bytes = n * (cvr ? sp.n_tasks : 1) * 4; break;
+    case CVR_DBG_HSEQ: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.hseq; bytes = P * d * 2; break;
+    case CVR_DBG_SEQ_POOL: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.seq_pool; bytes = S * R * d * 4; break;
+    case CVR_DBG_TOKENS: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_tok]; bytes = n * T * d * 2; break;
+    case CVR_DBG_QUERY: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.query; bytes = S * n * d * 2; break;
+    case CVR_DBG_ATTN: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_attn_tok]; bytes = n * T * d * 2; break;
+    case CVR_DBG_HIDDEN:
+      if (cvr || sp.n_hidden == 0) return fail(h, CVR_ERR_ARG, "DLRM with hidden layers only");
+      off = w.h[h->last_hidden_buf]; bytes = n * h->hidden[sp.n_hidden - 1] * 2; break;
+    default: return fail(h, CVR_ERR_ARG, "unknown export");
+  }
+  if (dst_bytes < bytes) return fail(h, CVR_ERR_ARG, "destination too small: need " + std::to_string(bytes));
+  if (bytes) {
+    hipError_t e = hipMemcpyAsync(dst, h->last_ws + off, bytes, hipMemcpyDeviceToDevice, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("export copy: ") + hipGetErrorString(e));
+  }
+  if (written) *written = bytes;
+  return CVR_OK;
+}
+
+// ------------------------------------------------------------------ misc
+
+extern "C" cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed, double halfwidth,
+                                     void* hip_stream) {
+  if (!table || ((uintptr_t)table & 15)) return fail(nullptr, CVR_ERR_ARG, "table must be non-null and 16-byte aligned");
+  if (rows <= 0 || dim <= 0 || dim % 4) return fail(nullptr, CVR_ERR_ARG, "rows > 0 and dim a positive multiple of 4 required");
+  if (!(halfwidth > 0.0) || !std::isfinite(halfwidth)) return fail(nullptr, CVR_ERR_ARG, "halfwidth must be positive");
+  const double step = (2.0 * halfwidth) / 16777216.0;
+  hipError_t e = launch_fill_table(table, rows * (int64_t)dim, seed, step, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(nullptr, CVR_ERR_HIP, std::string("fill: ") + hipGetErrorString(e));
+  return CVR_OK;
+}
+
+extern "C" const char* cvr_last_error(cvr_handle h) { return h ? h->err.c_str() : g_last_error.c_str(); }
+
+extern "C" const char* cvr_status_string(cvr_status s) {
+  switch (s) {
+    case CVR_OK: return "ok";
+    case CVR_ERR_ARG: return "invalid argument";
+    case CVR_ERR_SPEC: return "invalid spec or weights";
+    case CVR_ERR_RANGE: return "id or offset out of range (device check)";
+    case CVR_ERR_WORKSPACE: return "workspace or arena too small";
+    case CVR_ERR_HIP: return "HIP runtime error";
+    case CVR_ERR_UNSUPPORTED: return "unsupported by the kernels";
+  }
+  return "unknown status";
+}
+
+extern "C" void cvr_destroy(cvr_handle h) {
+  if (!h) return;
+  h->timing.reset();
+  delete h;
+}

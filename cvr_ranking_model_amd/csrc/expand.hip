@@ -1,0 +1,107 @@
+// Batch expansion and validation (step A0/B0), weight conversion and the synthetic table fill.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace cvr {
+
+__global__ void clear_flag_kernel(int32_t* flag) {
+  if (threadIdx.x == 0) flag[0] = 0;
+}
+
+hipError_t launch_clear_flag(int32_t* flag, hipStream_t st) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(64), 0, st, flag);
+  return hipGetLastError();
+}
+
+// One thread per index i over max(n, total_bags+1, S*(R+1), R+1):
+//  - i < n: cand_req[i] = the request owning candidate i (largest r with cand_offsets[r] <= i);
+//  - offsets checks: monotone, first 0, last equal to the declared totals.
+// Every read stays inside the arrays whatever their contents.
+__global__ void expand_kernel(ExpandParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int32_t bad = 0;
+  if (i < p.n) {
+    int lo = 0, hi = p.R - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cand_offsets[mid] <= (int32_t)i) lo = mid; else hi = mid - 1;
+    }
+    p.cand_req[i] = lo;
+  }
+  if (i <= p.R) {
+    const int32_t v = p.cand_offsets[i];
+    if ((i == 0 && v != 0) || v < 0 || v > p.n) bad |= ERRF_CAND_OFFSETS;
+    if (i == p.R && v != p.n) bad |= ERRF_CAND_OFFSETS;
+    if (i < p.R && p.cand_offsets[i + 1] < v) bad |= ERRF_CAND_OFFSETS;
+  }
+  if (i <= p.total_bags) {
+    const int64_t v = p.bag_offsets[i];
+    if ((i == 0 && v != 0) || v < 0 || v > p.n_ids) bad |= ERRF_BAG_OFFSETS;
+    if (i == p.total_bags && v != p.n_ids) bad |= ERRF_BAG_OFFSETS;
+    if (i < p.total_bags && (int64_t)p.bag_offsets[i + 1] < v) bad |= ERRF_BAG_OFFSETS;
+  }
+  if (p.seq_offsets != nullptr && i < (int64_t)p.S * (p.R + 1)) {
+    const int64_t r = i % (p.R + 1);
+    const int64_t v = p.seq_offsets[i];
+    if (v < 0 || v > p.n_positions) bad |= ERRF_SEQ_OFFSETS;
+    if (r < p.R && (int64_t)p.seq_offsets[i + 1] < v) bad |= ERRF_SEQ_OFFSETS;
+  }
+  if (bad) raise_flag(p.flag, bad);
+}
+
+hipError_t launch_expand(const ExpandParams& p, hipStream_t st) {
+  int64_t work = p.n;
+  if (p.total_bags + 1 > work) work = p.total_bags + 1;
+  if ((int64_t)p.R + 1 > work) work = (int64_t)p.R + 1;
+  if (p.seq_offsets && (int64_t)p.S * (p.R + 1) > work) work = (int64_t)p.S * (p.R + 1);
+  const int threads = 256;
+  const int64_t blocks = (work + threads - 1) / threads;
+  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ conversion
+template <typename T>
+__global__ void convert_kernel(const float* __restrict__ src, T* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = Lowp<T>::from_f32(src[i]);
+}
+
+hipError_t launch_convert(const float* src, void* dst, int64_t n, int lowp, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (lowp == 0)
+    hipLaunchKernelGGL(convert_kernel<f16>, dim3((unsigned)blocks), dim3(256), 0, st, src, (f16*)dst, n);
+  else
+    hipLaunchKernelGGL(convert_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st, src, (bf16*)dst, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ synthetic table fill
+// Element i gets (k - 2^23) * step (fp64 product, rounded to fp32), k = top 24 bits of the
+// (i+1)-th SplitMix64 output for the given seed.  Four consecutive elements per thread.
+__global__ void fill_kernel(float* __restrict__ t, int64_t quads, uint64_t seed, double step) {
+  const uint64_t gamma = 0x9E3779B97F4A7C15ull;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (int64_t)gridDim.x * blockDim.x) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t i = (uint64_t)(q * 4 + j);
+      const uint64_t x = splitmix64_mix(seed + (i + 1) * gamma);
+      const int64_t k = (int64_t)(x >> 40) - (int64_t)(1 << 23);
+      v[j] = (float)((double)k * step);
+    }
+    *reinterpret_cast<float4*>(t + q * 4) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+hipError_t launch_fill_table(float* t, int64_t total, uint64_t seed, double step, hipStream_t st) {
+  const int64_t quads = total / 4;
+  int64_t blocks = (quads + 255) / 256;
+  if (blocks > 262144) blocks = 262144;
+  if (blocks > 0) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, t, quads, seed, step);
+  return hipGetLastError();
+}
+
+}  // namespace cvr

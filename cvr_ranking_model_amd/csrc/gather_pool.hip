@@ -1,0 +1,107 @@
+// Multi-table embedding gather with mean pooling, clamp and low-precision cast (steps A1-A2 / B1).
+//
+// One launch covers every sparse feature of the batch.  Blocks are assigned to
+// features in contiguous ranges; inside a block, a group of dim/4 lanes owns one
+// bag and each lane owns four consecutive columns (one 16-byte load per row), so
+// a 64-dim row is one 256-byte coalesced access and a wave serves 4 (dim 64) or
+// 8 (dim 32) bags at once.  Up to kUnroll rows of a bag are loaded before any is
+// added, so many row fetches are in flight, but the adds happen in bag order:
+// acc = 0; acc += row_0; acc += row_1; ...; pooled = acc / len (one correctly
+// rounded fp32 division), matching the mean pooling of the CVR article
+// (section 3.1, item 2) on fp32 embeddings (CTR article, section 三) bit for bit.
+// The pooled value is clamped to +-clamp (NaN passes) and rounded to nearest-even
+// into fp16/bf16 (CTR article, section 三), then written at the feature's column
+// of the request-side or item-side input matrix.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace cvr {
+
+constexpr int kGatherThreads = 256;
+constexpr int kUnroll = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kGatherThreads) void gather_pool_kernel(const GatherParams p) {
+  const int b = blockIdx.x;
+  int fi = 0;
+#pragma unroll 1
+  for (int k = 1; k < p.nf; ++k)
+    if (p.f[k].block_begin <= b) fi = k;
+  const GatherFeature& F = p.f[fi];
+  const int lpb = F.dim >> 2;                       // lanes per bag
+  const int bags_per_block = kGatherThreads / lpb;
+  const int local = (b - F.block_begin) * bags_per_block + (int)threadIdx.x / lpb;
+  const int lane = (int)threadIdx.x % lpb;
+  if (local >= F.nbags) return;
+
+  const int64_t g = F.bag_base + local;
+  int64_t lo = p.bag_offsets[g];
+  int64_t hi = p.bag_offsets[g + 1];
+  // Malformed offsets are reported by the expand step; here they only must not lead outside ids.
+  lo = lo < 0 ? 0 : (lo > p.n_ids ? p.n_ids : lo);
+  hi = hi < lo ? lo : (hi > p.n_ids ? p.n_ids : hi);
+
+  const float* __restrict__ tab = F.table + lane * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  bool bad = false;
+#pragma unroll 1
+  for (int64_t j = lo; j < hi; j += kUnroll) {
+    float4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j + u < hi) {
+        const int32_t id = p.ids[j + u];
+        if (id >= 0 && (int64_t)id < F.rows)
+          r[u] = *reinterpret_cast<const float4*>(tab + (int64_t)id * F.dim);
+        else
+          bad = true;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (j + u < hi) {
+        acc.x += r[u].x;
+        acc.y += r[u].y;
+        acc.z += r[u].z;
+        acc.w += r[u].w;
+      }
+    }
+  }
+  if (bad) raise_flag(p.flag, ERRF_ID_RANGE);
+  const int64_t len = hi - lo;
+  if (len > 0) {
+    const float fl = (float)len;
+    acc.x = acc.x / fl;
+    acc.y = acc.y / fl;
+    acc.z = acc.z / fl;
+    acc.w = acc.w / fl;
+  }
+  if (F.dbg) *reinterpret_cast<float4*>(F.dbg + (int64_t)local * F.dim + lane * 4) = acc;
+  typedef typename Lowp<T>::vec4 V4;
+  V4 o;
+  o[0] = Lowp<T>::from_f32(clamp_keep_nan(acc.x, p.clamp));
+  o[1] = Lowp<T>::from_f32(clamp_keep_nan(acc.y, p.clamp));
+  o[2] = Lowp<T>::from_f32(clamp_keep_nan(acc.z, p.clamp));
+  o[3] = Lowp<T>::from_f32(clamp_keep_nan(acc.w, p.clamp));
+  T* out = reinterpret_cast<T*>(F.out) + (int64_t)local * F.ldo + F.col + lane * 4;
+  *reinterpret_cast<V4*>(out) = o;
+}
+
+hipError_t launch_gather_pool(GatherParams& p, hipStream_t st) {
+  int blocks = 0;
+  for (int k = 0; k < p.nf; ++k) {
+    p.f[k].block_begin = blocks;
+    const int bags_per_block = kGatherThreads / (p.f[k].dim / 4);
+    blocks += (p.f[k].nbags + bags_per_block - 1) / bags_per_block;
+  }
+  p.total_blocks = blocks;
+  if (blocks == 0) return hipSuccess;
+  if (p.lowp == 0)
+    hipLaunchKernelGGL(gather_pool_kernel<f16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(gather_pool_kernel<bf16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace cvr

@@ -1,0 +1,127 @@
+// Internal state of a libcvr model handle and of one call's workspace layout.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/cvr.h"
+
+namespace cvr {
+
+enum Stage {
+  STAGE_EXPAND = 0,
+  STAGE_GATHER,
+  STAGE_MLP_GEMM,
+  STAGE_DLRM_OUTPUT,
+  STAGE_TOKENIZE_GEMM,
+  STAGE_SWIGLU,
+  STAGE_SEQ_POOL,
+  STAGE_QUERY_GEMM,
+  STAGE_ATTENTION,
+  STAGE_MIXER_GEMM,
+  STAGE_PLE_GEMM,
+  STAGE_PLE_GATE,
+  STAGE_HEAD_GEMM,
+  STAGE_HEAD_OUT,
+  kNumStages
+};
+constexpr int kMaxLaunchesPerCall = 64;
+
+// One packed dense parameter in the weight arena: a Linear weight matrix [rows][cols] in the
+// low-precision type, or a bias vector [rows] in fp32.
+struct WEntry {
+  std::string name;
+  int64_t rows, cols;
+  bool matrix;
+  size_t off;
+};
+
+// A run of consecutive same-side features in the model input.
+struct InputSeg {
+  bool item;     // true: item-side matrix; false: request-side matrix read through cand_req
+  int k_end;     // end column of the run in the model input
+  int col0;      // first column of the run in its side's matrix
+};
+
+// Byte offsets of every buffer inside one call's workspace.
+struct WsPlan {
+  size_t flag = 0, cand_req = 0, x_req = 0, x_item = 0, logits = 0, pooled = 0, pooled_bytes = 0;
+  size_t h[2] = {0, 0};
+  size_t tok[2] = {0, 0}, hseq = 0, chunk_off = 0, pool_part = 0, seq_pool = 0, seq_pool_lp = 0, query = 0,
+         mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0;
+  size_t total = 0;
+};
+
+struct Timing {
+  bool armed = false;
+  int max_calls = 0;
+  int calls = 0;
+  int launch_in_call = 0;
+  std::vector<hipEvent_t> ev;   // [call][launch][begin,end]
+  std::vector<int> stage;       // [call][launch], -1 = unused
+  void reset();
+};
+
+}  // namespace cvr
+
+struct cvr_model {
+  cvr_spec spec{};
+  std::vector<cvr_feature> feats;
+  std::vector<int32_t> hidden, seq_tables;
+  std::vector<cvr_table> tables;
+  // derived layout
+  std::vector<int> fcol;
+  int D_req = 0, D_item = 0, ld_req = 0, ld_item = 0, e_dim = 0;
+  std::vector<cvr::InputSeg> segs;
+  // weights
+  std::vector<cvr::WEntry> w;
+  std::map<std::string, int> widx;
+  size_t arena_bytes = 0;
+  char* arena = nullptr;
+  const void* wptr(const std::string& name) const { return arena + w[widx.at(name)].off; }
+  // state
+  int debug = 0;
+  std::string err;
+  char* last_ws = nullptr;
+  cvr::WsPlan last_plan;
+  int64_t last_R = 0, last_n = 0, last_P = 0;
+  int last_debug = 0, last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0;
+  cvr::Timing timing;
+};
+
+namespace cvr {
+WsPlan plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P);
+
+// Brackets each kernel launch of one scoring call with a pair of HIP events when timing is armed.
+struct Launcher {
+  cvr_model* m;
+  hipStream_t s;
+  int slot_base = -1;
+  int li = 0;
+  Launcher(cvr_model* mm, hipStream_t ss) : m(mm), s(ss) {
+    Timing& t = m->timing;
+    if (t.armed && t.calls < t.max_calls) {
+      slot_base = t.calls * kMaxLaunchesPerCall;
+      t.calls++;
+    }
+  }
+  template <typename F>
+  hipError_t operator()(int stage, F&& fn) {
+    const bool rec = slot_base >= 0 && li < kMaxLaunchesPerCall;
+    const size_t slot = (size_t)slot_base + li;
+    if (rec) (void)hipEventRecord(m->timing.ev[2 * slot], s);
+    hipError_t e = fn();
+    if (rec) {
+      (void)hipEventRecord(m->timing.ev[2 * slot + 1], s);
+      m->timing.stage[slot] = stage;
+    }
+    li++;
+    return e;
+  }
+};
+}  // namespace cvr
+
+hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const cvr::WsPlan& w, float* out,
+                        cvr::Launcher& L, hipStream_t s);

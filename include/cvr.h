@@ -1,0 +1,234 @@
+/*
+ * cvr.h — C ABI of the MI355X candidate-scoring library (libcvr.so).
+ *
+ * What the library computes.  For every candidate item of every ad request it
+ * evaluates one forward pass of a ranking model and writes fp32 probabilities:
+ *
+ *   - DLRM-style model ("GPU inference optimisation for ad CTR models", the
+ *     CTR article): mean-pooled fp32 embeddings, clamp to +-bound, cast to
+ *     fp16, an MLP of fp16 Linear+ReLU layers over all candidates with shared
+ *     weights (sections 三 and 四), a final 1-unit Linear and an fp32 sigmoid.
+ *   - HyFormer-style CVR model (the iQIYI CVR article, section 3.2): the same
+ *     pooled embeddings cast to bf16 and projected into N tokens; three
+ *     behaviour sequences encoded position by position with SwiGLU; per
+ *     sequence one query from the tokens and the sequence's mean pool,
+ *     cross-attending to the encoded sequence with a temperature-scaled
+ *     softmax (Query Decoding); a Split -> Mixing -> Reverting token mixer
+ *     with residual over the N+3 tokens (Query Boosting), stacked n_layers
+ *     times; PLE experts with per-task gates and two-layer heads, each
+ *     ending in an fp32 sigmoid (section 3.2.4).
+ *
+ * Precision plan (CTR article section 三; CVR article section 3.4.3): tables
+ * and pooling fp32; every Linear weight matrix and every activation handed
+ * from one operator to the next in fp16 (DLRM) or bf16 (CVR), rounded to
+ * nearest-even; accumulation, biases, activation functions, softmax, pooling
+ * sums and residual adds in fp32; outputs fp32.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP global memory) unless a
+ *     comment says "host".  Integer tensors are int32, little-endian.
+ *   - The library never allocates device memory.  Weight arena and workspace
+ *     are caller-owned; their sizes come from cvr_weight_arena_bytes and
+ *     cvr_workspace_bytes.  Tables are borrowed, never copied.
+ *   - All device work is enqueued on the caller's stream (a hipStream_t
+ *     passed as void*; NULL is the default stream).  Nothing synchronises
+ *     except cvr_create (which finishes packing weights before it returns),
+ *     cvr_sync_status and cvr_timing_end.
+ *   - Every entry point returns a cvr_status; no C++ exception crosses the
+ *     ABI.  cvr_last_error gives a message for the last failing call on a
+ *     handle (or, with a NULL handle, the last failing call of the thread).
+ *   - A handle is not thread-safe; concurrent scoring needs one handle (or
+ *     at least one workspace and stream) per thread.
+ */
+#ifndef CVR_H
+#define CVR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cvr_model* cvr_handle;
+
+typedef enum {
+  CVR_OK = 0,
+  CVR_ERR_ARG = 1,          /* null/misaligned pointer, bad size or count */
+  CVR_ERR_SPEC = 2,         /* spec inconsistent, weight missing or misshapen */
+  CVR_ERR_RANGE = 3,        /* device found an id/offset out of range (reported by cvr_sync_status) */
+  CVR_ERR_WORKSPACE = 4,    /* workspace or arena too small for the call */
+  CVR_ERR_HIP = 5,          /* a HIP runtime call failed */
+  CVR_ERR_UNSUPPORTED = 6   /* valid spec outside what the kernels implement */
+} cvr_status;
+
+enum { CVR_MODEL_DLRM = 0, CVR_MODEL_HYFORMER = 1 };
+enum { CVR_SIDE_USER = 0, CVR_SIDE_ITEM = 1, CVR_SIDE_CONTEXT = 2 };
+enum { CVR_LOWP_FP16 = 0, CVR_LOWP_BF16 = 1 };
+
+/* One embedding table: fp32, row-major [rows][dim], device memory, BORROWED
+ * until cvr_destroy.  dim must be a multiple of 4 (16-byte rows quarters). */
+typedef struct {
+  const float* data;
+  int64_t rows;
+  int32_t dim;
+} cvr_table;
+
+/* One sparse feature: which table its ids index and whose bag it is.
+ * side = USER or CONTEXT: one bag per request; side = ITEM: one bag per
+ * candidate (CVR article section 3.4.5: user and item features batched
+ * separately, linked by the request). */
+typedef struct {
+  int32_t table;
+  int32_t side;
+} cvr_feature;
+
+/* Fixed model information (CVR article section 3.3: what stays fixed between
+ * requests is configuration; what varies per request is tensor input).
+ * The model input of a candidate is the concat, over features in this order,
+ * of each feature's pooled bag.  Fields marked (CVR) are ignored for DLRM. */
+typedef struct {
+  int32_t model;            /* CVR_MODEL_DLRM or CVR_MODEL_HYFORMER */
+  int32_t lowp;             /* CVR_LOWP_FP16 (DLRM) or CVR_LOWP_BF16 (CVR) */
+  float clamp;              /* clamp bound after pooling (CTR article section 三: 10) */
+  int32_t n_features;
+  const cvr_feature* features;   /* host array [n_features] */
+  int32_t n_hidden;              /* DLRM: hidden Linear+ReLU layers (3-5 in the CTR article) */
+  const int32_t* hidden;         /* host array [n_hidden]: widths (1024) */
+  /* (CVR) */
+  int32_t d;                /* token width (128) */
+  int32_t n_tokens;         /* N non-sequence tokens (13) */
+  int32_t n_layers;         /* stacked interaction layers (1 or 2) */
+  int32_t n_seq;            /* behaviour sequences = queries (3) */
+  int32_t n_seq_cols;       /* columns per sequence position (4: item, action, time bucket, side) */
+  const int32_t* seq_tables;/* host array [n_seq_cols]: table of each column; dims must sum to d */
+  int32_t swiglu_hidden;    /* SwiGLU hidden width (256) */
+  float tau;                /* attention temperature (2*sqrt(d)) */
+  int32_t mixer_heads;      /* token-mixer split count (16) */
+  int32_t mixer_hidden;     /* per-mixed-token FFN hidden width (256) */
+  int32_t n_experts;        /* PLE experts (3) */
+  int32_t expert_dim;       /* expert width (256) */
+  int32_t n_tasks;          /* scenarios / heads (2) */
+  int32_t head_hidden;      /* head hidden width (128) */
+} cvr_spec;
+
+/* One dense parameter, fp32, device memory, read only during cvr_create.
+ * Linear weights are [out][in] row-major.  Names:
+ *   DLRM: mlp.<i>.weight / mlp.<i>.bias for i = 0..n_hidden (the last is the 1-unit output).
+ *   CVR:  tok.{weight,bias}; seq.<s>.{gate,up,down}.{weight,bias};
+ *         layer.<l>.query.<s>.{weight,bias}; layer.<l>.mix.<h>.{fc1,fc2}.{weight,bias};
+ *         ple.expert.<e>.{weight,bias}; ple.gate.<k>.{weight,bias};
+ *         head.<k>.{fc1,fc2}.{weight,bias}. */
+typedef struct {
+  const char* name;         /* host string */
+  const float* data;        /* device */
+  int64_t numel;
+} cvr_weight;
+
+/* One batch of requests in CSR form (all device int32 arrays).
+ *   cand_offsets [n_requests+1]: request r owns candidates cand_offsets[r] ..
+ *     cand_offsets[r+1]-1; cand_offsets[0] = 0, non-decreasing,
+ *     cand_offsets[n_requests] = n_candidates.
+ *   bag_offsets [total_bags+1], ids [n_ids]: bags feature-major in spec order;
+ *     a user/context feature has n_requests bags (request order), an item
+ *     feature n_candidates bags (candidate order); bag_offsets[0] = 0,
+ *     non-decreasing, bag_offsets[total_bags] = n_ids; ids are table rows.
+ *   (CVR) seq_offsets [n_seq][n_requests+1]: positions of sequence s of
+ *     request r are rows seq_offsets[s][r] .. seq_offsets[s][r+1]-1 of
+ *     seq_ids; non-decreasing within each s; all inside [0, n_positions].
+ *   (CVR) seq_ids [n_positions][n_seq_cols]: table rows of each column.
+ * Offsets are per-request metadata passed as tensors (CVR article section
+ * 3.3); the caller packs them on the host and copies them in one transfer
+ * (section 3.4.1).  Malformed offsets or ids never make the kernels read
+ * outside these arrays or the tables: they raise the device error flag. */
+typedef struct {
+  int32_t n_requests;
+  int32_t n_candidates;
+  int64_t n_ids;
+  int64_t n_positions;
+  const int32_t* cand_offsets;
+  const int32_t* bag_offsets;
+  const int32_t* ids;
+  const int32_t* seq_offsets;
+  const int32_t* seq_ids;
+} cvr_batch;
+
+/* Device bytes needed for the packed weights of a spec (tables give dims;
+ * their data pointers are not read). */
+cvr_status cvr_weight_arena_bytes(const cvr_spec* spec, const cvr_table* tables, int32_t n_tables,
+                                  size_t* bytes);
+
+/* Build a model: validate spec, tables and weights; convert the fp32 weights
+ * into the low-precision packed layout inside weight_arena (device memory of
+ * at least cvr_weight_arena_bytes, 256-byte aligned, caller-owned, kept alive
+ * until cvr_destroy).  Synchronises the stream before returning.  On failure
+ * *out is NULL. */
+cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, int32_t n_tables,
+                      const cvr_weight* weights, int32_t n_weights, void* weight_arena,
+                      size_t arena_bytes, void* hip_stream, cvr_handle* out);
+
+/* Device bytes of workspace one cvr_score call needs for batches up to the
+ * given sizes (max_positions is ignored for DLRM). */
+cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_candidates,
+                               int64_t max_ids, int64_t max_positions, size_t* bytes);
+
+/* Score one batch: out_scores[c * n_tasks + k] (device fp32, n_tasks = 1 for
+ * DLRM) for every candidate c and task k.  workspace: device, 256-byte
+ * aligned, at least cvr_workspace_bytes for this batch's sizes.  Host-side
+ * checks return at once; device-side checks are reported by cvr_sync_status.
+ * Enqueued on hip_stream; returns without synchronising. */
+cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
+                     float* out_scores, void* hip_stream);
+
+/* Wait for the stream and report the device error flag of the last
+ * cvr_score on that workspace: CVR_ERR_RANGE if an id was outside its table
+ * or offsets were malformed (the batch's scores must then be discarded). */
+cvr_status cvr_sync_status(cvr_handle h, void* hip_stream);
+
+/* Intermediates kept in the workspace after the last cvr_score, for parity
+ * checks.  Copied (device to device, on hip_stream) into dst of dst_bytes;
+ * *written gets the byte count.  CVR_DBG_POOLED needs debug != 0 at
+ * cvr_set_debug time before the scoring call. */
+enum {
+  CVR_DBG_CAND_REQ = 0,     /* int32 [n]: request of each candidate */
+  CVR_DBG_POOLED = 1,       /* fp32, per feature in spec order: [bags_f][dim_f] pooled means before clamp */
+  CVR_DBG_INPUT_REQ = 2,    /* lowp [n_requests][D_req]: clamped, cast request-side inputs */
+  CVR_DBG_INPUT_ITEM = 3,   /* lowp [n][D_item]: clamped, cast item-side inputs */
+  CVR_DBG_LOGITS = 4,       /* fp32 [n][n_tasks]: pre-sigmoid outputs */
+  CVR_DBG_HSEQ = 5,         /* (CVR) bf16 [n_positions][d]: SwiGLU outputs */
+  CVR_DBG_SEQ_POOL = 6,     /* (CVR) fp32 [n_seq][n_requests][d]: mean pools */
+  CVR_DBG_TOKENS = 7,       /* (CVR) bf16 [n][16][d]: last layer's token matrix Z */
+  CVR_DBG_QUERY = 8,        /* (CVR) bf16 [n_seq][n][d]: last layer's queries */
+  CVR_DBG_ATTN = 9,         /* (CVR) bf16 [n][16][d]: last layer's token matrix before mixing (attention outputs in rows N..N+2) */
+  CVR_DBG_HIDDEN = 10       /* (DLRM) lowp [n][width]: activations of the last hidden layer */
+};
+cvr_status cvr_set_debug(cvr_handle h, int32_t debug);
+cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, size_t dst_bytes, size_t* written,
+                            void* hip_stream);
+
+/* Per-stage kernel timing with HIP events recorded on the scoring stream.
+ * cvr_timing_begin arms up to max_calls subsequent cvr_score calls;
+ * cvr_timing_end waits for them and writes, per stage, the summed
+ * milliseconds and the number of kernel launches.  Stage names come from
+ * cvr_stage_name. */
+cvr_status cvr_timing_begin(cvr_handle h, int32_t max_calls);
+cvr_status cvr_timing_end(cvr_handle h, double* stage_ms, int32_t* stage_launches, int32_t max_stages,
+                          int32_t* n_stages, int32_t* n_calls);
+const char* cvr_stage_name(cvr_handle h, int32_t stage);
+
+/* Fill a device fp32 table [rows][dim] with synthetic values: element
+ * i = row*dim + col is (k - 2^23) * (2*halfwidth / 2^24) in fp64, rounded to
+ * fp32, where k is the top 24 bits of the (i+1)-th output of SplitMix64
+ * (Steele, Lea & Flood 2014) seeded with seed.  An input generator for tests
+ * and benchmarks; not part of scoring. */
+cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed, double halfwidth,
+                          void* hip_stream);
+
+const char* cvr_last_error(cvr_handle h);
+const char* cvr_status_string(cvr_status s);
+void cvr_destroy(cvr_handle h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CVR_H */

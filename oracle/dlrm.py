@@ -26,8 +26,9 @@ def dlrm_forward(spec, tables, weights, batch, requests=None, exact=False):
     """Steps A0-A4 for all candidates (or those of the listed requests).
 
     Returns a dict with ``scores`` (fp32), ``logits`` (fp64), ``inputs`` (the
-    fp64 MLP input rows), ``pooled`` (fp32 per feature), ``cand`` (global
-    candidate indices scored) and the expansion ``ex``.
+    fp64 MLP input rows), ``hidden`` (the last hidden layer's activations),
+    ``pooled`` (fp32 per feature), ``cand`` (global candidate indices scored)
+    and the expansion ``ex``.
     """
     if spec["model"] != "dlrm":
         raise OracleInputError("not a DLRM spec")
@@ -36,6 +37,7 @@ def dlrm_forward(spec, tables, weights, batch, requests=None, exact=False):
     cands = requests_to_candidates(ex, requests)
     x, pooled = candidate_inputs(spec, tables, ex, cands, rnd)
     h = x
+    hidden = None
     L = mlp_layers(spec)
     for i in range(L):
         W = rnd(np.asarray(weights[f"mlp.{i}.weight"], dtype=np.float32).astype(np.float64))
@@ -45,8 +47,9 @@ def dlrm_forward(spec, tables, weights, batch, requests=None, exact=False):
         y = h @ W.T + b
         if i < L - 1:
             h = rnd(np.maximum(y, 0.0))
+            hidden = h
         else:
             z = y[:, 0]
     scores = sigmoid(z).astype(np.float32)
-    return {"scores": scores, "logits": z, "inputs": x, "pooled": pooled,
+    return {"scores": scores, "logits": z, "inputs": x, "hidden": hidden, "pooled": pooled,
             "cand": cands, "ex": ex}

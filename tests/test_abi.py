@@ -1,0 +1,95 @@
+"""The C ABI library loads and exports every entry point include/cvr.h declares; host-only checks.
+
+No test here launches device work: these run without a GPU.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from cvr_ranking_model_amd import synth
+from cvr_ranking_model_amd import cvr as cv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cvr.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|cvr_status|void)\s+(cvr_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["cvr_create", "cvr_score", "cvr_weight_arena_bytes", "cvr_workspace_bytes", "cvr_sync_status",
+                 "cvr_destroy", "cvr_debug_export", "cvr_fill_table"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cv.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(cv._PROTOS) == set(declared_functions())
+
+
+class _FakeTensor:
+    def __init__(self, rows, dim):
+        self.shape = (rows, dim)
+
+    def data_ptr(self):
+        return 0
+
+
+def _spec_c(spec):
+    tabs = [_FakeTensor(t["rows"], t["dim"]) for t in spec["tables"]]
+    return cv.spec_to_c(spec, tabs)
+
+
+def test_arena_size_matches_weight_shapes():
+    for name in ["c1", "c2", "c3", "c4", "c5"]:
+        spec = synth.load_spec(name)
+        s, tabs, keep = _spec_c(spec)
+        nbytes = cv.cvr_weight_arena_bytes(s, tabs, len(spec["tables"]))
+        want = 0
+        for wname, shape in synth.weight_shapes(spec).items():
+            n = int(np.prod(shape))
+            want += ((n * (2 if wname.endswith(".weight") else 4)) + 255) // 256 * 256
+        assert nbytes == want, name
+
+
+def test_bad_specs_are_rejected_on_the_host():
+    spec = synth.load_spec("c1")
+    s, tabs, keep = _spec_c(spec)
+    s.model = 7
+    with pytest.raises(cv.CvrError) as e:
+        cv.cvr_weight_arena_bytes(s, tabs, len(spec["tables"]))
+    assert e.value.status == cv.CVR_ERR_SPEC
+    s, tabs, keep = _spec_c(spec)
+    s.features[0].table = 9
+    with pytest.raises(cv.CvrError, match="table index"):
+        cv.cvr_weight_arena_bytes(s, tabs, len(spec["tables"]))
+    bad = dict(spec, mlp_hidden=[1000])
+    s, tabs, keep = _spec_c(bad)
+    with pytest.raises(cv.CvrError) as e:
+        cv.cvr_weight_arena_bytes(s, tabs, len(spec["tables"]))
+    assert e.value.status == cv.CVR_ERR_UNSUPPORTED
+    cvr = synth.load_spec("c3")
+    s, tabs, keep = _spec_c(dict(cvr, d=64))
+    with pytest.raises(cv.CvrError) as e:
+        cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"]))
+    assert e.value.status == cv.CVR_ERR_UNSUPPORTED
+
+
+def test_fill_and_create_argument_checks():
+    with pytest.raises(cv.CvrError) as e:
+        cv.cvr_fill_table(None, 10, 4, 1, 0.05, None)
+    assert e.value.status == cv.CVR_ERR_ARG
+    spec = synth.load_spec("c1")
+    s, tabs, keep = _spec_c(spec)
+    with pytest.raises(cv.CvrError) as e:   # null table data is refused before any device work
+        cv.cvr_create(s, tabs, len(spec["tables"]), None, 0, None, 0, None)
+    assert e.value.status == cv.CVR_ERR_ARG
+    assert cv.lib().cvr_status_string(cv.CVR_ERR_RANGE).decode().startswith("id or offset")

@@ -1,0 +1,228 @@
+"""GPU parity of the DLRM-style path (A0-A4) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cvr_ranking_model_amd import synth
+from cvr_ranking_model_amd import cvr as cv
+from gpu_common import banner, build_model, run, export_inputs, assemble_inputs, export_pooled, oracle_pooled
+from conftest import tiny_dlrm_spec
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 2e-3   # absolute, on fp32 sigmoid scores
+
+
+def logit_tol(z, spec):
+    """Bound on |z_gpu - z_oracle| derived from the arithmetic.
+
+    Both sides round every hidden activation to fp16 (unit roundoff u = 2^-11).
+    They accumulate in different precisions (fp32 vs fp64), so a few
+    activations round to neighbouring fp16 values, and those 1-ulp differences
+    spread through the following layers: the two results behave like two fp16
+    rounding paths of the same network, whose logits differ by about
+    u * sqrt(L) * rms(z) for L Linear layers.  Allow 4x that.
+    """
+    u = 2.0 ** -11 if spec["lowp"] == "fp16" else 2.0 ** -8
+    L = len(spec["mlp_hidden"]) + 1
+    return 4.0 * u * np.sqrt(L) * max(1.0, float(np.sqrt(np.mean(np.square(z)))))
+
+
+def ulp_diff_lowp(a, b, lowp):
+    """|a - b| in units of the low-precision spacing at max(|a|, |b|).
+
+    Near zero the unit is floored at 2^-20: a pre-activation within the fp32
+    accumulation error (about sqrt(K) * 2^-24 * |terms|, ~1e-6 here) of zero may
+    land on either side of the ReLU, which is not a one-step rounding flip.
+    """
+    mag = np.maximum(np.abs(a), np.abs(b))
+    if lowp == "fp16":
+        sp = np.spacing(mag.astype(np.float16)).astype(np.float64)
+    else:
+        sp = np.ldexp(1.0, np.frexp(mag)[1] - 8)
+    sp = np.maximum(sp, np.float64(2.0 ** -20))
+    return np.abs(a - b) / sp
+
+
+def check_dlrm(spec, m, batch, variant, requests=None, tables_host=None):
+    db, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    tables_host = tables_host or synth.make_tables(spec, variant)
+    weights = synth.make_weights(spec, variant)
+    ref = oracle.score(spec, tables_host, weights, batch, requests=requests)
+    ex = ref["ex"]
+    cands = ref["cand"]
+    # A0: candidate -> request map, bit-exact over the whole batch
+    cand_req = m.export(cv.CVR_DBG_CAND_REQ, torch.int32, (max(db.n_candidates, 1),)).cpu().numpy()[:db.n_candidates]
+    assert np.array_equal(cand_req, ex["cand_req"])
+    # A1: pooled fp32, bit-exact on the bags the sampled candidates use
+    pooled = export_pooled(m, spec, db)
+    for fi, f in enumerate(spec["features"]):
+        bags = cands if f["side"] == "item" else np.unique(ex["cand_req"][cands])
+        want = oracle_pooled(spec, tables_host, ex, fi, bags)
+        got = pooled[fi][bags]
+        assert np.array_equal(got, want), f"feature {fi}: max |d| {np.abs(got - want).max()}"
+    # A2: clamped low-precision inputs, bit-exact
+    xr, xi = export_inputs(m, spec, db)
+    x_gpu = assemble_inputs(spec, xr, xi, cand_req, cands)
+    assert np.array_equal(x_gpu, ref["inputs"])
+    # A3-A4: logits and scores
+    z_gpu = m.export(cv.CVR_DBG_LOGITS, torch.float32, (max(db.n_candidates, 1),)).cpu().numpy()[cands]
+    s_gpu = out.cpu().numpy()[cands]
+    dz = np.abs(z_gpu - ref["logits"]).max() if cands.size else 0.0
+    ds = np.abs(s_gpu - ref["scores"]).max() if cands.size else 0.0
+    banner(f"{spec['name']} {variant}: n={cands.size} max|dz|={dz:.3e} (z std {np.std(ref['logits']):.3e}) "
+           f"max|ds|={ds:.3e} (score std {np.std(ref['scores']):.3e})")
+    assert dz <= logit_tol(ref["logits"], spec)
+    assert ds <= SCORE_TOL
+    if len(spec["mlp_hidden"]) == 1:
+        # one hidden layer: identical fp16 inputs and weights, so every activation must equal the
+        # oracle's or sit one fp16 step away (fp32 vs fp64 accumulation at a rounding boundary)
+        width = spec["mlp_hidden"][0]
+        hid = m.export(cv.CVR_DBG_HIDDEN, torch.float16, (max(db.n_candidates, 1), width)).float().cpu().numpy()
+        ud = ulp_diff_lowp(hid[cands].astype(np.float64), ref["hidden"], spec["lowp"])
+        banner(f"  hidden layer: max ulp diff {ud.max():.2f}, share off by one ulp {np.mean(ud > 0):.2e}")
+        assert ud.max() <= 1.0 and np.mean(ud > 0) < 1e-2
+    return out
+
+
+def test_device_fill_matches_generator():
+    for variant in ["bench", "stress", "clamp"]:
+        t = synth.make_tables(synth.load_spec("c1"), variant)[2]
+        dev = torch.empty((t.rows, t.dim), dtype=torch.float32, device="cuda")
+        cv.cvr_fill_table(cv.C.c_void_p(dev.data_ptr()), t.rows, t.dim, t.seed, t.halfwidth, cv._stream_ptr())
+        torch.cuda.synchronize()
+        rows = np.array([0, 1, 17, 4095, 9999])
+        assert np.array_equal(dev[torch.as_tensor(rows)].cpu().numpy(), t[rows])
+
+
+@pytest.mark.parametrize("variant", ["bench", "stress", "clamp"])
+def test_c1_parity(variant):
+    spec = synth.load_spec("c1")
+    banner(f"c1 {variant}")
+    m, _ = build_model(spec, variant)
+    check_dlrm(spec, m, synth.make_batch(spec), variant)
+
+
+@pytest.mark.parametrize("variant", ["stress"])
+def test_c2_reduced_parity(variant):
+    spec = synth.load_spec("c2")
+    banner(f"c2 reduced {variant}")
+    m, _ = build_model(spec, variant)
+    check_dlrm(spec, m, synth.make_batch(spec, requests=3), variant)
+
+
+@pytest.mark.parametrize("variant", ["bench", "stress"])
+def test_c2_full_sampled(variant):
+    spec = synth.load_spec("c2")
+    banner(f"c2 full {variant}: 64 requests x 500 candidates, oracle on requests 0, 31, 63")
+    m, _ = build_model(spec, variant)
+    check_dlrm(spec, m, synth.make_batch(spec), variant, requests=[0, 31, 63])
+
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_single_hidden_layer_exactness(name):
+    spec = dict(synth.load_spec(name), mlp_hidden=[1024])
+    banner(f"{name} shapes with one hidden layer, stress data")
+    m, _ = build_model(spec, "stress")
+    check_dlrm(spec, m, synth.make_batch(spec, requests=2), "stress")
+
+
+def test_c5_full_sampled():
+    spec = synth.load_spec("c5")
+    banner("c5 full stress: 27 GB of tables, 256 requests x 500 candidates, oracle on requests 0, 255")
+    m, _ = build_model(spec, "stress")
+    check_dlrm(spec, m, synth.make_batch(spec), "stress", requests=[0, 255])
+    del m
+    torch.cuda.empty_cache()
+
+
+def _tiny():
+    return tiny_dlrm_spec(dims=(16, 16, 32, 32), hidden=(64, 32), rows=50, bag_max=5)
+
+
+def test_ragged_and_empty():
+    spec = _tiny()
+    tables = [torch.as_tensor(t).cuda() for t in _host_tables(spec)]
+    banner("tiny ragged: empty requests and empty bags")
+    m, _ = build_model(spec, "stress", tables=tables)
+    for seed in range(3):
+        b = synth.make_batch(spec, requests=6, candidates=5, ragged=True, seed_offset=seed)
+        assert (np.diff(b["bag_offsets"]) == 0).any()
+        check_dlrm(spec, m, b, "stress", tables_host=_host_tables(spec))
+    b = synth.make_batch(spec, cand_counts=[0, 3, 0, 1])
+    check_dlrm(spec, m, b, "stress", tables_host=_host_tables(spec))
+
+
+def _host_tables(spec):
+    return [t.materialize() for t in synth.make_tables(spec, "stress")]
+
+
+def test_request_alone_equals_in_batch_and_determinism():
+    spec = synth.load_spec("c2")
+    banner("c2: request alone vs in batch, run twice")
+    m, _ = build_model(spec, "stress")
+    b = synth.make_batch(spec, requests=4)
+    _, out1, _ = run(m, b)
+    s1 = out1.cpu().numpy().copy()
+    _, out2, _ = run(m, b)
+    assert np.array_equal(s1, out2.cpu().numpy())          # bitwise deterministic
+    ex = oracle.expand(spec, b)
+    lo, hi = ex["cand_offsets"][2], ex["cand_offsets"][3]
+    # request 2 on its own: slice its bags out of every feature
+    bags, ids = [0], []
+    for fi, f in enumerate(spec["features"]):
+        local = np.arange(lo, hi) if f["side"] == "item" else np.array([2])
+        for g in ex["bag_base"][fi] + local:
+            ids.append(ex["ids"][ex["bag_offsets"][g]:ex["bag_offsets"][g + 1]])
+            bags.append(bags[-1] + ids[-1].size)
+    alone = {"cand_offsets": np.array([0, hi - lo], np.int32), "bag_offsets": np.array(bags, np.int32),
+             "ids": np.concatenate(ids).astype(np.int32)}
+    _, out3, _ = run(m, alone)
+    assert np.array_equal(out3.cpu().numpy(), s1[lo:hi])   # rows are computed independently
+
+
+def test_device_errors_are_reported():
+    spec = _tiny()
+    tables = [torch.as_tensor(t).cuda() for t in _host_tables(spec)]
+    m, _ = build_model(spec, "stress", tables=tables)
+    b = synth.make_batch(spec, requests=2, candidates=3)
+    bad = dict(b, ids=b["ids"].copy())
+    bad["ids"][3] = spec["tables"][0]["rows"]          # one past the table
+    _, _, st = run(m, bad)
+    assert st == cv.CVR_ERR_RANGE
+    bad = dict(b, ids=b["ids"].copy())
+    bad["ids"][0] = -5
+    _, _, st = run(m, bad)
+    assert st == cv.CVR_ERR_RANGE
+    bad = dict(b, bag_offsets=b["bag_offsets"].copy())
+    bad["bag_offsets"][2], bad["bag_offsets"][3] = bad["bag_offsets"][3], bad["bag_offsets"][2] - 1
+    _, _, st = run(m, bad)
+    assert st == cv.CVR_ERR_RANGE
+    bad = dict(b, cand_offsets=np.array([0, 4, 3], np.int32))
+    _, _, st = run(m, bad)
+    assert st == cv.CVR_ERR_RANGE
+    _, _, st = run(m, b)                                 # a good batch afterwards is clean again
+    assert st == cv.CVR_OK
+
+
+def test_host_errors():
+    spec = _tiny()
+    tables = [torch.as_tensor(t).cuda() for t in _host_tables(spec)]
+    weights = synth.make_weights(spec, "stress")
+    w2 = dict(weights)
+    del w2["mlp.1.bias"]
+    with pytest.raises(cv.CvrError, match="missing weight"):
+        cv.Model(spec, tables, w2)
+    w3 = dict(weights)
+    w3["mlp.0.weight"] = w3["mlp.0.weight"][:, :-8]
+    with pytest.raises(cv.CvrError, match="elements"):
+        cv.Model(spec, tables, w3)
+    m = cv.Model(spec, tables, weights)
+    db = cv.DeviceBatch(synth.make_batch(spec, requests=2, candidates=3))
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(6, dtype=torch.float32, device="cuda")
+    with pytest.raises(cv.CvrError) as e:
+        cv.cvr_score(m.h, db.c, cv.C.c_void_p(ws.data_ptr()), ws.numel(), cv.C.c_void_p(out.data_ptr()), cv._stream_ptr())
+    assert e.value.status == cv.CVR_ERR_WORKSPACE
