@@ -63,12 +63,13 @@ static cvr_status check_spec(const cvr_spec* s, const cvr_table* tables, int32_t
     }
     if (sd != s->d) { why = "sequence column dims must sum to d"; return CVR_ERR_SPEC; }
     const int T = s->n_tokens + s->n_seq;
-    if (s->mixer_heads <= 0 || s->d % s->mixer_heads || (s->d / s->mixer_heads) % 8) { why = "mixer heads must split d into chunks of a multiple of 8"; return CVR_ERR_UNSUPPORTED; }
+    if (s->mixer_heads <= 0 || s->d % s->mixer_heads || s->d / s->mixer_heads != 8) { why = "mixer heads must split d into chunks of 8"; return CVR_ERR_UNSUPPORTED; }
     if ((T * (s->d / s->mixer_heads)) % 32) { why = "mixed-token width must be a multiple of 32"; return CVR_ERR_UNSUPPORTED; }
     if (s->swiglu_hidden != 256) { why = "SwiGLU hidden width must be 256"; return CVR_ERR_UNSUPPORTED; }
     if (s->mixer_hidden <= 0 || s->mixer_hidden % 32 || s->expert_dim <= 0 || s->expert_dim % 32 ||
         s->head_hidden <= 0 || s->head_hidden % 32) { why = "mixer/expert/head widths must be multiples of 32"; return CVR_ERR_UNSUPPORTED; }
     if (s->n_experts <= 0 || s->n_experts > 8 || s->n_tasks <= 0 || s->n_tasks > 8) { why = "bad expert/task counts"; return CVR_ERR_SPEC; }
+    if (s->expert_dim % 64) { why = "expert width must be a multiple of 64"; return CVR_ERR_UNSUPPORTED; }
     if (!(s->tau > 0.f) || !std::isfinite(s->tau)) { why = "tau must be positive"; return CVR_ERR_SPEC; }
   }
   return CVR_OK;
@@ -262,16 +263,15 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     w.h[1] = take((size_t)n * maxw * lp);
   } else {
     const int64_t d = s.d, S = s.n_seq, T = s.n_tokens + s.n_seq;
-    w.tok[0] = take((size_t)n * T * d * lp);
-    w.tok[1] = take((size_t)n * T * d * lp);
+    w.tok[0] = take((size_t)n * T * d * 4);
+    w.tok[1] = take((size_t)n * T * d * 4);
     w.hseq = take((size_t)P * d * lp);
     w.chunk_off = take((size_t)(S * R + 1) * 4);
     w.pool_part = take((size_t)(P / kSeqChunk + S * R + 1) * d * 4);
     w.seq_pool = take((size_t)S * R * d * 4);
-    w.seq_pool_lp = take((size_t)S * R * d * lp);
-    w.query = take((size_t)S * n * d * lp);
+    w.query = take((size_t)S * n * d * 4);
     w.mixhid = take((size_t)s.mixer_heads * n * s.mixer_hidden * lp);
-    w.experts = take((size_t)n * s.n_experts * s.expert_dim * lp);
+    w.experts = take((size_t)n * s.n_experts * s.expert_dim * 4);
     w.gates = take((size_t)n * s.n_tasks * s.n_experts * 4);
     w.task_in = take((size_t)s.n_tasks * n * s.expert_dim * lp);
     w.head_hid = take((size_t)s.n_tasks * n * s.head_hidden * lp);
@@ -547,9 +547,9 @@ extern "C" cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, si
     case CVR_DBG_LOGITS: off = w.logits; bytes = n * (cvr ? sp.n_tasks : 1) * 4; break;
     case CVR_DBG_HSEQ: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.hseq; bytes = P * d * 2; break;
     case CVR_DBG_SEQ_POOL: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.seq_pool; bytes = S * R * d * 4; break;
-    case CVR_DBG_TOKENS: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_tok]; bytes = n * T * d * 2; break;
-    case CVR_DBG_QUERY: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.query; bytes = S * n * d * 2; break;
-    case CVR_DBG_ATTN: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_attn_tok]; bytes = n * T * d * 2; break;
+    case CVR_DBG_TOKENS: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_tok]; bytes = n * T * d * 4; break;
+    case CVR_DBG_QUERY: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.query; bytes = S * n * d * 4; break;
+    case CVR_DBG_ATTN: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_attn_tok]; bytes = n * T * d * 4; break;
     case CVR_DBG_HIDDEN:
       if (cvr || sp.n_hidden == 0) return fail(h, CVR_ERR_ARG, "DLRM with hidden layers only");
       off = w.h[h->last_hidden_buf]; bytes = n * h->hidden[sp.n_hidden - 1] * 2; break;

@@ -74,9 +74,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
       const ASeg& S = p.seg[s];
       const int kk = k - kb + S.col0;
       const int64_t row = S.rowmap ? (int64_t)S.rowmap[m] : (int64_t)m;
-      const T* src = reinterpret_cast<const T*>(S.ptr) + (int64_t)g * S.gstride + row * S.ld +
-                     (int64_t)(kk >> 3) * S.kstride8;
-      ra[i] = *reinterpret_cast<const u32x4*>(src);
+      const int64_t eoff = (int64_t)g * S.gstride + row * S.ld + (int64_t)(kk >> 3) * S.kstride8;
+      if (S.f32) {
+        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(S.ptr) + eoff);
+        const float4 x0 = src[0], x1 = src[1];
+        V8 v;
+        v[0] = Lowp<T>::from_f32(x0.x); v[1] = Lowp<T>::from_f32(x0.y);
+        v[2] = Lowp<T>::from_f32(x0.z); v[3] = Lowp<T>::from_f32(x0.w);
+        v[4] = Lowp<T>::from_f32(x1.x); v[5] = Lowp<T>::from_f32(x1.y);
+        v[6] = Lowp<T>::from_f32(x1.z); v[7] = Lowp<T>::from_f32(x1.w);
+        ra[i] = *reinterpret_cast<const u32x4*>(&v);
+      } else {
+        ra[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(S.ptr) + eoff);
+      }
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -152,7 +162,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         if (m >= p.M) continue;
         const int64_t addr = (int64_t)m * p.ldc + ncol;
         float x = acc[i][j][v] + bn;
-        if (p.R) x += Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[addr]);
+        if (p.R) x += p.r_f32 ? reinterpret_cast<const float*>(p.R)[addr]
+                              : Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[addr]);
         if (p.relu) x = x > 0.f ? x : 0.f;
         if (p.out_f32)
           reinterpret_cast<float*>(p.C)[addr] = x;

@@ -1,11 +1,289 @@
-// Launch sequence of the HyFormer-style CVR model (steps B2-B11).
+// Launch sequence of the HyFormer-style CVR model (steps B2-B11), after the shared
+// expand and gather-pool front.
+//
+// Token matrices live in two ping-pong buffers of [n][T][d] fp32 (T = N + S tokens); every
+// GEMM that reads them rounds its input rows to bf16 as it loads them:
+//   tokenize GEMM  -> rows 0..N-1 of buffer `cur`              (B2)
+//   SwiGLU + pool  -> H [positions][d], pooled means [S][R][d]   (B3-B5, once per request)
+//   per layer l:
+//     query GEMM (grouped over sequences) <- rows 0..N-1 of `cur` and the pooled mean (B6)
+//     attention                           -> rows N..N+S-1 of `cur`                     (B7)
+//     mixer fc1 (grouped over mixed tokens) reads the Split layout of `cur` in place,
+//     mixer fc2 writes Y + FFN in the Revert layout into the other buffer               (B8)
+//     the other buffer becomes `cur`: its rows 0..N-1 are the next layer's tokens       (B9)
+//   expert GEMM, gates + mixture, head fc1 GEMM, head output + sigmoid                  (B10-B11)
 #include <hip/hip_runtime.h>
+
+#include <string>
 
 #include "kernels.h"
 #include "model.h"
 
-hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const cvr::WsPlan& w, float* out,
-                        cvr::Launcher& L, hipStream_t s) {
-  (void)m; (void)b; (void)ws; (void)w; (void)out; (void)L; (void)s;
-  return hipErrorNotSupported;
+using namespace cvr;
+
+// Element stride between parameters fmt(0), fmt(1), ... in the arena, or -1 if not uniform.
+template <typename F>
+static int64_t group_stride(const cvr_model* m, F&& fmt, int count, int elem_bytes) {
+  if (count <= 1) return 0;
+  const int64_t st = (int64_t)m->w[m->widx.at(fmt(1))].off - (int64_t)m->w[m->widx.at(fmt(0))].off;
+  for (int i = 2; i < count; ++i)
+    if ((int64_t)m->w[m->widx.at(fmt(i))].off - (int64_t)m->w[m->widx.at(fmt(i - 1))].off != st) return -1;
+  return st % elem_bytes ? -1 : st / elem_bytes;
+}
+
+static std::string S_(int i) { return std::to_string(i); }
+
+hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan& w, float* out, Launcher& L,
+                        hipStream_t s) {
+  const cvr_spec& sp = m->spec;
+  const int R = b->n_requests, n = b->n_candidates, S = sp.n_seq, d = sp.d, N = sp.n_tokens, T = N + S;
+  const int H = sp.mixer_heads, mh = sp.mixer_hidden, E = sp.n_experts, ed = sp.expert_dim, K = sp.n_tasks;
+  const int hh = sp.head_hidden;
+  const int64_t P = b->n_positions;
+  const int lowp = CVR_LOWP_BF16;
+  char* tok[2] = {ws + w.tok[0], ws + w.tok[1]};
+  const int32_t* cand_req = (const int32_t*)(ws + w.cand_req);
+  int32_t* flag = (int32_t*)(ws + w.flag);
+  hipError_t e;
+
+  // ---- B2: tokenization, X = E W_tok^T + b into token rows 0..N-1
+  {
+    GemmParams g{};
+    g.M = n;
+    g.N = N * d;
+    g.K = m->e_dim;
+    g.groups = 1;
+    g.nseg = (int)m->segs.size();
+    for (size_t i = 0; i < m->segs.size(); ++i) {
+      const InputSeg& sg = m->segs[i];
+      g.seg[i] = ASeg{ws + (sg.item ? w.x_item : w.x_req), sg.item ? nullptr : cand_req,
+                      (int64_t)(sg.item ? m->ld_item : m->ld_req), 0, sg.k_end, 8, sg.col0, 0};
+    }
+    g.W = m->wptr("tok.weight");
+    g.bias = (const float*)m->wptr("tok.bias");
+    g.C = tok[0];
+    g.ldc = (int64_t)T * d;
+    g.c_nstride8 = 8;
+    g.out_f32 = 1;
+    e = L(STAGE_TOKENIZE_GEMM, [&] { return launch_gemm(g, lowp, s); });
+    if (e != hipSuccess) return e;
+  }
+
+  // ---- B3-B5: sequence encoding and mean pools (per request)
+  int32_t* chunk_off = (int32_t*)(ws + w.chunk_off);
+  e = L(STAGE_SWIGLU, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, s); });
+  if (e != hipSuccess) return e;
+  {
+    SwigluParams p{};
+    p.seq_offsets = b->seq_offsets;
+    p.R = R;
+    p.S = S;
+    p.n_positions = P;
+    p.seq_ids = b->seq_ids;
+    p.ncols = sp.n_seq_cols;
+    int col = 0;
+    for (int c = 0; c < sp.n_seq_cols; ++c) {
+      const cvr_table& t = m->tables[m->seq_tables[c]];
+      p.col_off[c] = col;
+      p.col_dim[c] = t.dim;
+      p.col_rows[c] = t.rows;
+      p.col_table[c] = t.data;
+      col += t.dim;
+    }
+    p.chunk_off = chunk_off;
+    p.Wgu = (const __bf16*)m->wptr("seq.0.gate.weight");
+    p.wgu_gstride = group_stride(m, [](int i) { return "seq." + S_(i) + ".gate.weight"; }, S, 2);
+    p.bgu = (const float*)m->wptr("seq.0.gate.bias");
+    p.bgu_gstride = group_stride(m, [](int i) { return "seq." + S_(i) + ".gate.bias"; }, S, 4);
+    p.Wd = (const __bf16*)m->wptr("seq.0.down.weight");
+    p.wd_gstride = group_stride(m, [](int i) { return "seq." + S_(i) + ".down.weight"; }, S, 2);
+    p.bd = (const float*)m->wptr("seq.0.down.bias");
+    p.bd_gstride = group_stride(m, [](int i) { return "seq." + S_(i) + ".down.bias"; }, S, 4);
+    if (p.wgu_gstride < 0 || p.bgu_gstride < 0 || p.wd_gstride < 0 || p.bd_gstride < 0) return hipErrorInvalidValue;
+    p.clamp = sp.clamp;
+    p.H = (__bf16*)(ws + w.hseq);
+    p.part = (float*)(ws + w.pool_part);
+    p.flag = flag;
+    const int max_chunks = (int)(P / kSeqChunk) + S * R;
+    e = L(STAGE_SWIGLU, [&] { return launch_swiglu(p, max_chunks, s); });
+    if (e != hipSuccess) return e;
+  }
+  e = L(STAGE_SEQ_POOL, [&] {
+    return launch_seq_pool((const float*)(ws + w.pool_part), chunk_off, b->seq_offsets, R, S, P,
+                           (float*)(ws + w.seq_pool), s);
+  });
+  if (e != hipSuccess) return e;
+
+  // ---- B6-B9: stacked interaction layers
+  int cur = 0;
+  for (int l = 0; l < sp.n_layers; ++l) {
+    const std::string Lp = "layer." + S_(l);
+    {
+      GemmParams g{};
+      g.M = n;
+      g.N = d;
+      g.K = (N + 1) * d;
+      g.groups = S;
+      g.nseg = 2;
+      g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, N * d, 8, 0, 1};
+      g.seg[1] = ASeg{ws + w.seq_pool, cand_req, d, (int64_t)R * d, (N + 1) * d, 8, 0, 1};
+      g.W = m->wptr(Lp + ".query.0.weight");
+      g.w_gstride = group_stride(m, [&](int i) { return Lp + ".query." + S_(i) + ".weight"; }, S, 2);
+      g.bias = (const float*)m->wptr(Lp + ".query.0.bias");
+      g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".query." + S_(i) + ".bias"; }, S, 4);
+      if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
+      g.C = ws + w.query;
+      g.ldc = d;
+      g.c_gstride = (int64_t)n * d;
+      g.c_nstride8 = 8;
+      g.out_f32 = 1;
+      e = L(STAGE_QUERY_GEMM, [&] { return launch_gemm(g, lowp, s); });
+      if (e != hipSuccess) return e;
+    }
+    {
+      AttnParams a{};
+      a.H = (const __bf16*)(ws + w.hseq);
+      a.seq_offsets = b->seq_offsets;
+      a.R = R;
+      a.S = S;
+      a.n_positions = P;
+      a.q = (const float*)(ws + w.query);
+      a.cand_req = cand_req;
+      a.n = n;
+      a.inv_tau = 1.0f / sp.tau;
+      a.Y = (float*)tok[cur];
+      a.T = T;
+      a.N = N;
+      e = L(STAGE_ATTENTION, [&] { return launch_attention(a, s); });
+      if (e != hipSuccess) return e;
+    }
+    const int mw = T * d / H;  // mixed-token width; one 8-wide chunk per token
+    {
+      GemmParams g{};
+      g.M = n;
+      g.N = mh;
+      g.K = mw;
+      g.groups = H;
+      g.nseg = 1;
+      // Split: mixed token h, element t*8 + j = token t, column h*8 + j
+      g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, d / H, mw, d, 0, 1};
+      g.W = m->wptr(Lp + ".mix.0.fc1.weight");
+      g.w_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.weight"; }, H, 2);
+      g.bias = (const float*)m->wptr(Lp + ".mix.0.fc1.bias");
+      g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.bias"; }, H, 4);
+      if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
+      g.C = ws + w.mixhid;
+      g.ldc = mh;
+      g.c_gstride = (int64_t)n * mh;
+      g.c_nstride8 = 8;
+      g.relu = 1;
+      e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
+      if (e != hipSuccess) return e;
+    }
+    {
+      GemmParams g{};
+      g.M = n;
+      g.N = mw;
+      g.K = mh;
+      g.groups = H;
+      g.nseg = 1;
+      g.seg[0] = ASeg{ws + w.mixhid, nullptr, mh, (int64_t)n * mh, mh, 8, 0, 0};
+      g.W = m->wptr(Lp + ".mix.0.fc2.weight");
+      g.w_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.weight"; }, H, 2);
+      g.bias = (const float*)m->wptr(Lp + ".mix.0.fc2.bias");
+      g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.bias"; }, H, 4);
+      if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
+      // Revert + residual: output element t*8 + j of mixed token h lands on token t, column h*8 + j
+      g.C = tok[1 - cur];
+      g.R = tok[cur];
+      g.ldc = (int64_t)T * d;
+      g.c_nstride8 = d;
+      g.c_gstride = d / H;
+      g.out_f32 = 1;
+      g.r_f32 = 1;
+      e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
+      if (e != hipSuccess) return e;
+    }
+    m->last_attn_tok = cur;
+    cur = 1 - cur;
+  }
+  m->last_tok = cur;
+
+  // ---- B10: experts over the flattened token matrix, then gates and mixture
+  {
+    GemmParams g{};
+    g.M = n;
+    g.N = E * ed;
+    g.K = T * d;
+    g.groups = 1;
+    g.nseg = 1;
+    g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, T * d, 8, 0, 1};
+    g.W = m->wptr("ple.expert.0.weight");
+    g.bias = (const float*)m->wptr("ple.expert.0.bias");
+    if (group_stride(m, [](int i) { return "ple.expert." + S_(i) + ".weight"; }, E, 2) != (int64_t)ed * T * d ||
+        group_stride(m, [](int i) { return "ple.expert." + S_(i) + ".bias"; }, E, 4) != ed)
+      return hipErrorInvalidValue;
+    g.C = ws + w.experts;
+    g.ldc = (int64_t)E * ed;
+    g.c_nstride8 = 8;
+    g.relu = 1;
+    g.out_f32 = 1;
+    e = L(STAGE_PLE_GEMM, [&] { return launch_gemm(g, lowp, s); });
+    if (e != hipSuccess) return e;
+  }
+  {
+    PleGateParams p{};
+    p.Z = (const float*)tok[cur];
+    p.n = n;
+    p.zdim = T * d;
+    p.Wg = (const __bf16*)m->wptr("ple.gate.0.weight");
+    p.wg_task_stride = group_stride(m, [](int i) { return "ple.gate." + S_(i) + ".weight"; }, K, 2);
+    if (K > 1 && p.wg_task_stride < 0) return hipErrorInvalidValue;
+    for (int k = 0; k < K; ++k) p.bg[k] = (const float*)m->wptr("ple.gate." + S_(k) + ".bias");
+    p.E = E;
+    p.K = K;
+    p.experts = (const float*)(ws + w.experts);
+    p.edim = ed;
+    p.task_in = (__bf16*)(ws + w.task_in);
+    e = L(STAGE_PLE_GATE, [&] { return launch_ple_gate(p, s); });
+    if (e != hipSuccess) return e;
+  }
+  // ---- B11: heads
+  {
+    GemmParams g{};
+    g.M = n;
+    g.N = hh;
+    g.K = ed;
+    g.groups = K;
+    g.nseg = 1;
+    g.seg[0] = ASeg{ws + w.task_in, nullptr, ed, (int64_t)n * ed, ed, 8, 0, 0};
+    g.W = m->wptr("head.0.fc1.weight");
+    g.w_gstride = group_stride(m, [](int i) { return "head." + S_(i) + ".fc1.weight"; }, K, 2);
+    g.bias = (const float*)m->wptr("head.0.fc1.bias");
+    g.bias_gstride = group_stride(m, [](int i) { return "head." + S_(i) + ".fc1.bias"; }, K, 4);
+    if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
+    g.C = ws + w.head_hid;
+    g.ldc = hh;
+    g.c_gstride = (int64_t)n * hh;
+    g.c_nstride8 = 8;
+    g.relu = 1;
+    e = L(STAGE_HEAD_GEMM, [&] { return launch_gemm(g, lowp, s); });
+    if (e != hipSuccess) return e;
+  }
+  {
+    HeadOutParams p{};
+    p.U = (const __bf16*)(ws + w.head_hid);
+    p.n = n;
+    p.K = K;
+    p.hdim = hh;
+    p.w2 = (const __bf16*)m->wptr("head.0.fc2.weight");
+    p.w2_stride = group_stride(m, [](int i) { return "head." + S_(i) + ".fc2.weight"; }, K, 2);
+    if (K > 1 && p.w2_stride < 0) return hipErrorInvalidValue;
+    for (int k = 0; k < K; ++k) p.b2[k] = (const float*)m->wptr("head." + S_(k) + ".fc2.bias");
+    p.logits = (float*)(ws + w.logits);
+    p.out = out;
+    e = L(STAGE_HEAD_OUT, [&] { return launch_head_out(p, s); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }

@@ -67,6 +67,8 @@ hipError_t launch_gather_pool(GatherParams& p, hipStream_t st);
 // C(m, n) = epilogue( sum_k A(m, k) * W(n, k) + bias(n) ) for a group index g.
 // A(m, k): K is split into segments; in segment s (k_begin..k_end) with kk = k - k_begin + col0,
 //   A(m, k) = seg.ptr[g*seg.gstride + row*seg.ld + (kk/8)*seg.kstride8 + kk%8], row = rowmap ? rowmap[m] : m.
+//   A segment flagged f32 holds fp32 values, rounded to the low-precision type as they are loaded
+//   (the rounding every Linear input gets).
 // W(n, k) = W[g*w_gstride + n*K + k].   C(m, n) at C[g*c_gstride + m*ldc + (n/8)*c_nstride8 + n%8];
 // the optional residual R uses the same addressing as C.
 struct ASeg {
@@ -77,7 +79,7 @@ struct ASeg {
   int32_t k_end;
   int32_t kstride8;
   int32_t col0;
-  int32_t pad_;
+  int32_t f32;          // 1: source is fp32
 };
 struct GemmParams {
   int32_t M, N, K;
@@ -92,9 +94,10 @@ struct GemmParams {
   int64_t ldc;
   int64_t c_gstride;
   int32_t c_nstride8;
-  const void* R;        // residual (same type and addressing as C) or null
+  const void* R;        // residual (same addressing as C) or null
   int32_t relu;
   int32_t out_f32;      // 1: C is fp32, else the low-precision type
+  int32_t r_f32;        // 1: R is fp32, else the low-precision type
 };
 hipError_t launch_gemm(const GemmParams& p, int lowp, hipStream_t st);
 
@@ -102,6 +105,83 @@ hipError_t launch_gemm(const GemmParams& p, int lowp, hipStream_t st);
 // z[m] = sum_k H[m][k] * w[k] + b  (fp32 accumulation), out[m] = sigmoid(z[m]).
 hipError_t launch_dlrm_output(const void* H, int32_t M, int32_t K, const void* w, const float* b,
                               float* logits, float* out, int lowp, hipStream_t st);
+
+// ---------------------------------------------------------------- CVR sequences (B3-B5)
+constexpr int kMaxSeqCols = 8;
+constexpr int kMaxTasks = 8;
+constexpr int kMaxExperts = 8;
+
+// Chunk table: chunk_off[g] = number of kSeqChunk-position chunks before segment g = s*R + r.
+hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
+                              hipStream_t st);
+
+struct SwigluParams {
+  const int32_t* seq_offsets;   // [S][R+1]
+  int32_t R, S;
+  int64_t n_positions;
+  const int32_t* seq_ids;       // [n_positions][ncols]
+  int32_t ncols;
+  int32_t col_off[kMaxSeqCols]; // first column of each sequence column in the 128-wide token
+  int32_t col_dim[kMaxSeqCols];
+  int64_t col_rows[kMaxSeqCols];
+  const float* col_table[kMaxSeqCols];
+  const int32_t* chunk_off;     // [S*R+1]
+  const __bf16* Wgu;            // per sequence [2*256][128]: gate rows then up rows
+  int64_t wgu_gstride;
+  const float* bgu;             // per sequence [2*256]
+  int64_t bgu_gstride;
+  const __bf16* Wd;             // per sequence [128][256]
+  int64_t wd_gstride;
+  const float* bd;              // per sequence [128]
+  int64_t bd_gstride;
+  float clamp;
+  __bf16* H;                    // [n_positions][128]
+  float* part;                  // [chunks][128] column sums
+  int32_t* flag;
+};
+hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st);
+hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
+                           int64_t n_positions, float* pool, hipStream_t st);
+
+// ---------------------------------------------------------------- attention (B7)
+struct AttnParams {
+  const __bf16* H;              // [n_positions][128]
+  const int32_t* seq_offsets;   // [S][R+1]
+  int32_t R, S;
+  int64_t n_positions;
+  const float* q;               // [S][n][128]
+  const int32_t* cand_req;      // [n]
+  int32_t n;
+  float inv_tau;
+  float* Y;                     // [n][T][128]: writes token N+s
+  int32_t T, N;
+};
+hipError_t launch_attention(const AttnParams& p, hipStream_t st);
+
+// ---------------------------------------------------------------- PLE gates and heads (B10-B11)
+struct PleGateParams {
+  const float* Z;               // [n][zdim] (rounded to bf16 as the gates' Linear input)
+  int32_t n, zdim;
+  const __bf16* Wg;             // task k, expert e: Wg + k*wg_task_stride + e*zdim
+  int64_t wg_task_stride;
+  const float* bg[kMaxTasks];   // [E] per task
+  int32_t E, K;
+  const float* experts;         // [n][E*edim]
+  int32_t edim;
+  __bf16* task_in;              // [K][n][edim]
+};
+hipError_t launch_ple_gate(const PleGateParams& p, hipStream_t st);
+
+struct HeadOutParams {
+  const __bf16* U;              // [K][n][hdim]
+  int32_t n, K, hdim;
+  const __bf16* w2;             // task k: w2 + k*w2_stride, [hdim]
+  int64_t w2_stride;
+  const float* b2[kMaxTasks];
+  float* logits;                // [n][K]
+  float* out;                   // [n][K]
+};
+hipError_t launch_head_out(const HeadOutParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- fill (input generator)
 hipError_t launch_fill_table(float* t, int64_t total, uint64_t seed, double step, hipStream_t st);

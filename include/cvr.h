@@ -19,10 +19,12 @@
  *     ending in an fp32 sigmoid (section 3.2.4).
  *
  * Precision plan (CTR article section 三; CVR article section 3.4.3): tables
- * and pooling fp32; every Linear weight matrix and every activation handed
- * from one operator to the next in fp16 (DLRM) or bf16 (CVR), rounded to
- * nearest-even; accumulation, biases, activation functions, softmax, pooling
- * sums and residual adds in fp32; outputs fp32.
+ * and pooling fp32; every Linear weight matrix and every Linear input in fp16
+ * (DLRM) or bf16 (CVR), rounded to nearest-even -- in the DLRM model that is
+ * every hidden activation; in the CVR model also the encoded sequence states,
+ * while its token matrix, queries, attention outputs and expert outputs stay
+ * fp32; accumulation, biases, activation functions, softmax, pooling sums and
+ * residual adds in fp32; outputs fp32.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers (HIP global memory) unless a
@@ -197,9 +199,9 @@ enum {
   CVR_DBG_LOGITS = 4,       /* fp32 [n][n_tasks]: pre-sigmoid outputs */
   CVR_DBG_HSEQ = 5,         /* (CVR) bf16 [n_positions][d]: SwiGLU outputs */
   CVR_DBG_SEQ_POOL = 6,     /* (CVR) fp32 [n_seq][n_requests][d]: mean pools */
-  CVR_DBG_TOKENS = 7,       /* (CVR) bf16 [n][16][d]: last layer's token matrix Z */
-  CVR_DBG_QUERY = 8,        /* (CVR) bf16 [n_seq][n][d]: last layer's queries */
-  CVR_DBG_ATTN = 9,         /* (CVR) bf16 [n][16][d]: last layer's token matrix before mixing (attention outputs in rows N..N+2) */
+  CVR_DBG_TOKENS = 7,       /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix Z */
+  CVR_DBG_QUERY = 8,        /* (CVR) fp32 [n_seq][n][d]: last layer's queries */
+  CVR_DBG_ATTN = 9,         /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix before mixing (attention outputs in rows N..) */
   CVR_DBG_HIDDEN = 10       /* (DLRM) lowp [n][width]: activations of the last hidden layer */
 };
 cvr_status cvr_set_debug(cvr_handle h, int32_t debug);

@@ -6,13 +6,16 @@ FP16 weights, returning an FP32 prediction.  The CVR article (section 3.4.3)
 runs the dense network in BF16.  Neither page states a rounding mode; the
 reading taken is round-to-nearest-even, the IEEE default.
 
-Reading of where rounding happens (applied identically to both models):
-every Linear weight matrix is stored in the low-precision type, and every
-activation tensor that one operator hands to the next is stored in it.
-Inside an operator (dot-product accumulation, bias, activation function,
-softmax, pooling sums, residual add) arithmetic is at least fp32 — here fp64.
-Biases stay fp32.  The embedding pooling before the cast and the final
-probabilities are fp32.
+Reading of where rounding happens: every Linear weight matrix and every
+Linear input is in the low-precision type.  In the DLRM-style model that is
+every hidden activation (the CTR article names the MLP's input activations as
+FP16).  In the CVR model the encoded sequence states, which are stored and
+read back by the attention, are also low precision; the other per-candidate
+tensors that are not Linear inputs stay at full precision (see
+:mod:`oracle.hyformer`).  Arithmetic inside an operator (dot-product
+accumulation, bias, activation function, softmax, pooling sums, residual add)
+is at least fp32 — here fp64.  Biases stay fp32.  The embedding pooling
+before the cast and the final probabilities are fp32.
 
 Values are returned as fp64 arrays holding exactly representable
 low-precision numbers, so the rest of the oracle can keep computing in fp64.

@@ -77,3 +77,19 @@ def export_pooled(m, spec, db):
 def oracle_pooled(spec, tables_host, ex, fi, bags):
     f = spec["features"][fi]
     return pool_bags(tables_host[f["table"]], ex["ids"], ex["bag_offsets"], ex["bag_base"][fi] + np.asarray(bags))
+
+
+def ulp_diff_lowp(a, b, lowp, floor=2.0 ** -20):
+    """|a - b| in units of the low-precision spacing at max(|a|, |b|), floored near zero."""
+    mag = np.maximum(np.abs(a), np.abs(b))
+    if lowp == "fp16":
+        sp = np.spacing(mag.astype(np.float16)).astype(np.float64)
+    else:
+        sp = np.ldexp(1.0, np.frexp(mag)[1] - 8)
+    sp = np.maximum(sp, np.float64(floor))
+    return np.abs(a - b) / sp
+
+
+def rms(x):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.sqrt(np.mean(np.square(x)))) if x.size else 0.0

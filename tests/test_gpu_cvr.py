@@ -1,0 +1,168 @@
+"""GPU parity of the HyFormer-style CVR path (B0-B11) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cvr_ranking_model_amd import synth
+from cvr_ranking_model_amd import cvr as cv
+from gpu_common import (banner, build_model, run, export_inputs, assemble_inputs, export_pooled, oracle_pooled,
+                        rms)
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 2e-3
+U_BF16 = 2.0 ** -8   # bf16 unit roundoff
+
+
+def stage_close(a, b, stages, scale=None):
+    """Elementwise bound for a tensor `stages` bf16 rounding steps downstream of bit-exact inputs.
+
+    GPU (fp32 accumulation) and oracle (fp64) round the same values at each step, so a few
+    elements land on neighbouring bf16 values; the element itself may then differ by one
+    rounding (u|b|), and upstream differences spread through later operators like an
+    independent rounding path, about u * sqrt(stages) * rms.  Allow 4x on the spread.
+    """
+    scale = rms(b) if scale is None else scale
+    return np.abs(a - b) <= U_BF16 * np.abs(b) + 4.0 * U_BF16 * np.sqrt(stages) * scale
+
+
+def close_one_step(a, b, scale):
+    """One operator past bit-exact inputs: |a - b| <= u|b| + 8u*scale.  The absolute term
+    covers one upstream flip of a single product term: SiLU(gate)*up is heavy-tailed, so one
+    term of the down projection can be several times the rms of the result."""
+    return np.abs(a - b) <= U_BF16 * np.abs(b) + 8.0 * U_BF16 * scale
+
+
+def bf16_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_cvr(spec, m, batch, variant, requests=None, tables_host=None):
+    db, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    tables_host = tables_host or synth.make_tables(spec, variant)
+    weights = synth.make_weights(spec, variant)
+    ref = oracle.score(spec, tables_host, weights, batch, requests=requests, trace=True)
+    tr = ref["trace"]
+    ex = ref["ex"]
+    cands = ref["cand"]
+    reqs = list(range(ex["R"])) if requests is None else list(requests)
+    R, n, d, N, S = db.n_requests, db.n_candidates, spec["d"], spec["n_tokens"], 3
+    T = N + S
+    # B0: candidate map, bit-exact
+    cand_req = m.export(cv.CVR_DBG_CAND_REQ, torch.int32, (max(n, 1),)).cpu().numpy()[:n]
+    assert np.array_equal(cand_req, ex["cand_req"])
+    # B1: pooled fp32 and bf16 inputs, bit-exact
+    pooled = export_pooled(m, spec, db)
+    for fi, f in enumerate(spec["features"]):
+        bags = cands if f["side"] == "item" else np.unique(ex["cand_req"][cands])
+        assert np.array_equal(pooled[fi][bags], oracle_pooled(spec, tables_host, ex, fi, bags)), fi
+    xr, xi = export_inputs(m, spec, db)
+    assert np.array_equal(assemble_inputs(spec, xr, xi, cand_req, cands), tr["e"])
+    # B3-B5: encoded sequences (one rounding step after the bf16 gate/up input, one after the down projection)
+    so = ex["seq_offsets"]
+    Hg = bf16_np(m.export(cv.CVR_DBG_HSEQ, torch.bfloat16, (max(db.n_positions, 1), d)))
+    pg = m.export(cv.CVR_DBG_SEQ_POOL, torch.float32, (S, R, d)).cpu().numpy().astype(np.float64)
+    worst, share, pool_err, all_close = 0.0, [], 0.0, True
+    for s in range(S):
+        for r in reqs:
+            Hr = tr["H"][(s, r)]
+            if Hr.shape[0] == 0:
+                assert np.array_equal(pg[s, r], np.zeros(d))
+                continue
+            Hgr = Hg[so[s, r]:so[s, r + 1]]
+            worst = max(worst, float(np.abs(Hgr - Hr).max() / max(rms(Hr), 1e-30)))
+            share.append(float(np.mean(Hgr != Hr)))
+            all_close &= bool(close_one_step(Hgr, Hr, rms(Hr)).all())
+            pool_err = max(pool_err, float(np.abs(pg[s, r] - tr["p"][(s, r)]).max() / max(rms(Hr), 1e-30)))
+    banner(f"  H: max |d| / rms {worst:.2e}, share differing {np.mean(share) if share else 0:.2e}; "
+           f"pool max err / rms(H) {pool_err:.2e}")
+    assert all_close and (not share or np.mean(share) < 2e-2)
+    assert pool_err <= U_BF16
+    # B2 + B7 of the last layer: tokens before mixing (rows 0..N-1 are the layer input, N.. the attention outputs)
+    Yg = m.export(cv.CVR_DBG_ATTN, torch.float32, (max(n, 1), T, d)).cpu().numpy().astype(np.float64)[cands]
+    if spec["n_layers"] == 1:
+        # tokens are an fp32 GEMM output over bit-exact bf16 inputs: fp32 vs fp64 accumulation only
+        x0 = tr["X0"]
+        banner(f"  tokens: max |d| / rms {np.abs(Yg[:, :N] - x0).max() / rms(x0):.2e}")
+        assert (np.abs(Yg[:, :N] - x0) <= 2.0 ** -14 * (np.abs(x0) + rms(x0))).all()
+    o_ref = np.stack(tr["o"][-1], axis=1)
+    o_err = float(np.abs(Yg[:, N:] - o_ref).max())
+    banner(f"  attention out: max |d| {o_err:.3e} (rms {rms(o_ref):.3e})")
+    assert stage_close(Yg[:, N:], o_ref, 3 * spec["n_layers"]).all()
+    # B8-B9: final token matrix
+    Zg = m.export(cv.CVR_DBG_TOKENS, torch.float32, (max(n, 1), T, d)).cpu().numpy().astype(np.float64)[cands]
+    z_err = float(np.abs(Zg - tr["Z"][-1]).max())
+    banner(f"  tokens out: max |d| {z_err:.3e} (rms {rms(tr['Z'][-1]):.3e})")
+    assert stage_close(Zg, tr["Z"][-1], 6 * spec["n_layers"]).all()
+    # B10-B11: logits and scores
+    K = spec["n_tasks"]
+    zl = m.export(cv.CVR_DBG_LOGITS, torch.float32, (max(n, 1), K)).cpu().numpy()[cands]
+    sg = out.cpu().numpy().reshape(-1, K)[cands]
+    dz = float(np.abs(zl - ref["logits"]).max())
+    ds = float(np.abs(sg - ref["scores"]).max())
+    banner(f"{spec['name']} {variant}: n={cands.size} max|dz|={dz:.3e} (rms z {rms(ref['logits']):.3e}) "
+           f"max|ds|={ds:.3e} (score std {np.std(ref['scores']):.3e})")
+    assert stage_close(zl, ref["logits"], 6 * spec["n_layers"] + 4).all()
+    assert ds <= SCORE_TOL
+    return out
+
+
+@pytest.mark.parametrize("variant", ["bench", "stress", "clamp"])
+def test_c3_parity(variant):
+    spec = synth.load_spec("c3")
+    banner(f"c3 {variant}: 16 samples, full sequence lengths")
+    m, _ = build_model(spec, variant)
+    check_cvr(spec, m, synth.make_batch(spec, requests=16), variant)
+
+
+def test_c3_full_sampled():
+    spec = synth.load_spec("c3")
+    banner("c3 full: 512 samples, oracle on samples 0, 200, 511")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec), "stress", requests=[0, 200, 511])
+
+
+def test_c4_full_sampled():
+    spec = synth.load_spec("c4")
+    banner("c4 full: 4096 samples, 2 layers, sequences 256/1024/2048, oracle on samples 0, 4095")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec), "stress", requests=[0, 4095])
+
+
+def test_c4_two_layers_small():
+    spec = synth.load_spec("c4")
+    banner("c4 small: 6 samples, 2 layers")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec, requests=6), "stress")
+
+
+def test_ragged_multi_candidate():
+    spec = synth.load_spec("c3")
+    banner("c3 ragged: several candidates per request, empty and length-1 sequences, empty bags")
+    m, _ = build_model(spec, "stress")
+    lens = [[0, 1, 64, 3, 17, 64], [256, 0, 1, 2, 100, 129], [1, 512, 0, 65, 63, 5]]
+    b = synth.make_batch(spec, cand_counts=[2, 0, 3, 1, 1, 2], seq_lengths=lens, bag_min=0)
+    assert (np.diff(b["bag_offsets"]) == 0).any()
+    check_cvr(spec, m, b, "stress")
+
+
+def test_determinism_and_errors():
+    spec = synth.load_spec("c3")
+    m, _ = build_model(spec, "stress")
+    b = synth.make_batch(spec, requests=8)
+    _, o1, _ = run(m, b)
+    s1 = o1.cpu().numpy().copy()
+    _, o2, _ = run(m, b)
+    assert np.array_equal(s1, o2.cpu().numpy())
+    bad = dict(b, seq_ids=b["seq_ids"].copy())
+    bad["seq_ids"][5, 1] = 16                      # action table has 16 rows
+    _, _, st = run(m, bad)
+    assert st == cv.CVR_ERR_RANGE
+    bad = dict(b, seq_offsets=b["seq_offsets"].copy())
+    bad["seq_offsets"][1, 3] = bad["seq_offsets"][1, 4] + 1
+    _, _, st = run(m, bad)
+    assert st == cv.CVR_ERR_RANGE
+    _, _, st = run(m, b)
+    assert st == cv.CVR_OK
