@@ -30,46 +30,53 @@ WORKLOAD_TEXT = {
 }
 
 
-def dense_flops_per_candidate(spec):
-    """FLOPs of every Linear (2*K*N per candidate), as performed."""
-    from cvr_ranking_model_amd import synth
-    total = 0
-    for name, shape in synth.weight_shapes(spec).items():
-        if name.endswith(".weight"):
-            total += 2 * shape[0] * shape[1]
-    if spec["model"] == "hyformer":
-        # the sequence encoders run once per position, not once per candidate
-        L = sum(spec["seq"]["lengths"])
-        per_pos = sum(2 * shape[0] * shape[1] for n, shape in synth.weight_shapes(spec).items()
-                      if n.startswith("seq.") and n.endswith(".weight")) // len(spec["seq"]["lengths"])
-        seq_total = sum(2 * shape[0] * shape[1] for n, shape in synth.weight_shapes(spec).items()
-                        if n.startswith("seq.") and n.endswith(".weight"))
-        total = total - seq_total + per_pos * L
-    return total
+def stage_work(spec, batch):
+    """Algorithmic work per step, per stage: ("flop"|"byte", amount).
 
-
-def mlp_gemm_flops(spec, n):
-    from cvr_ranking_model_amd import synth
-    return sum(2 * n * s[0] * s[1] for k, s in synth.weight_shapes(spec).items()
-               if k.startswith("mlp.") and k.endswith(".weight") and s[0] > 1)
-
-
-def gather_bytes(spec, batch):
-    """Algorithmic bytes of one gather-pool launch: rows once per id, ids and offsets read, fp16/bf16 out."""
+    FLOPs count 2*M*N*K per Linear as performed.  Bytes count what the stage
+    must move: table rows once per id occurrence, the ids and offsets it reads,
+    and the low-precision outputs it writes (cache hits are not subtracted).
+    """
     import numpy as np
-    ex_lens = np.diff(batch["bag_offsets"].astype(np.int64))
+    from cvr_ranking_model_amd import synth
+    shapes = synth.weight_shapes(spec)
     R = len(batch["cand_offsets"]) - 1
     n = int(batch["cand_offsets"][-1])
-    rows = 0
-    o = 0
-    out = 0
+    lens = np.diff(batch["bag_offsets"].astype(np.int64))
+    rows, out, o = 0, 0, 0
     for f in spec["features"]:
         nb = n if f["side"] == "item" else R
         dim = spec["tables"][f["table"]]["dim"]
-        rows += int(ex_lens[o:o + nb].sum()) * dim * 4
+        rows += int(lens[o:o + nb].sum()) * dim * 4
         out += nb * dim * 2
         o += nb
-    return rows + 4 * len(batch["ids"]) + 4 * len(batch["bag_offsets"]) + out
+    work = {"gather_pool": ("byte", rows + 4 * len(batch["ids"]) + 4 * len(batch["bag_offsets"]) + out)}
+    lin = lambda name: 2 * shapes[name][0] * shapes[name][1]
+    if spec["model"] == "dlrm":
+        work["mlp_gemm"] = ("flop", n * sum(lin(k) for k in shapes if k.startswith("mlp.") and k.endswith(".weight")
+                                          and shapes[k][0] > 1))
+        work["dlrm_output"] = ("byte", n * spec["mlp_hidden"][-1] * 2 + n * 4)
+        return work
+    S = len(spec["seq"]["lengths"])
+    P = int(batch["seq_ids"].shape[0])
+    L = spec["n_layers"]
+    d = spec["d"]
+    per_pos = sum(lin(f"seq.0.{x}.weight") for x in ["gate", "up", "down"])
+    work["tokenize_gemm"] = ("flop", n * lin("tok.weight"))
+    work["swiglu"] = ("flop", P * per_pos)
+    work["swiglu_bytes"] = ("byte", P * (sum(spec["tables"][c["table"]]["dim"] for c in spec["seq"]["columns"]) * 4
+                                         + 4 * len(spec["seq"]["columns"]) + d * 2))
+    work["query_gemm"] = ("flop", L * n * sum(lin(f"layer.0.query.{q}.weight") for q in range(S)))
+    # each candidate reads its request's encoded positions once per layer (bf16 rows)
+    so = batch["seq_offsets"].astype(np.int64)
+    cand_req = np.repeat(np.arange(R), np.diff(batch["cand_offsets"]))
+    pos_per_cand = sum((so[q, cand_req + 1] - so[q, cand_req]).sum() for q in range(S))
+    work["attention"] = ("byte", L * int(pos_per_cand) * d * 2)
+    H = spec["mixer_heads"]
+    work["mixer_gemm"] = ("flop", L * n * H * (lin("layer.0.mix.0.fc1.weight") + lin("layer.0.mix.0.fc2.weight")))
+    work["ple_gemm"] = ("flop", n * spec["n_experts"] * lin("ple.expert.0.weight"))
+    work["head_gemm"] = ("flop", n * spec["n_tasks"] * lin("head.0.fc1.weight"))
+    return work
 
 
 def cpu_baseline(spec, variant, weights, budget_s=10.0):
@@ -105,7 +112,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--batch", type=int, default=None, help="requests per step (CVR batch sweep)")
     ap.add_argument("--variant", default="bench")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -125,7 +133,7 @@ def main():
     tables = cv.device_tables(spec, args.variant)
     weights = synth.make_weights(spec, args.variant)
     model = cv.Model(spec, tables, weights)
-    batch = synth.make_batch(spec, uniform_ids=args.uniform_ids)
+    batch = synth.make_batch(spec, requests=args.batch, uniform_ids=args.uniform_ids)
     db = cv.DeviceBatch(batch)
     n = db.n_candidates
     out = torch.empty(n * model.n_tasks, dtype=torch.float32, device="cuda")
@@ -146,25 +154,36 @@ def main():
     ms_step = dt * 1e3 / args.steps
     value = n * args.steps / dt
 
-    # dominant kernel and its roofline
+    # per-stage rooflines from the live event timings; the dominant stage gives "roofline"
+    work = stage_work(spec, batch)
+    peak_f = MFMA_PEAK_TFLOPS[spec["lowp"]]
+    table = {}
+    for st, (ms, launches) in stages.items():
+        entry = {"ms_per_step": round(ms / calls, 4), "launches_per_step": launches // max(calls, 1)}
+        kind = work.get(st)
+        if kind:
+            avg_s = ms / launches / 1e3
+            per_launch = kind[1] * calls / launches
+            if kind[0] == "flop":
+                ach = per_launch / avg_s / 1e12
+                entry.update(bound="mfma", achieved=round(ach, 1), peak=peak_f, unit="TFLOP/s", frac=round(ach / peak_f, 4))
+            else:
+                ach = per_launch / avg_s / 1e9
+                entry.update(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(ach / HBM_PEAK_GBS, 4))
+            entry["per_launch"] = per_launch
+            entry["avg_launch_us"] = round(avg_s * 1e6, 2)
+        if st == "swiglu" and "swiglu_bytes" in work:
+            b = work["swiglu_bytes"][1] * calls / launches
+            entry["hbm_GBs"] = round(b / (ms / launches / 1e3) / 1e9, 1)
+        table[st] = entry
     dom = max(stages, key=lambda k: stages[k][0])
-    gemm_ms, gemm_launches = stages.get("mlp_gemm", (0.0, 0))
-    flops_step = mlp_gemm_flops(spec, n)
+    d_entry = table[dom]
     roof = None
-    if dom == "mlp_gemm" and gemm_launches:
-        per_launch = flops_step * calls / gemm_launches
-        avg_s = gemm_ms / gemm_launches / 1e3
-        ach = per_launch / avg_s / 1e12
-        roof = {"bound": "mfma", "kernel": "gemm_kernel (hidden Linear+ReLU layers)", "achieved": round(ach, 1),
-                "peak": MFMA_PEAK_TFLOPS[spec["lowp"]], "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_PEAK_TFLOPS[spec["lowp"]], 4), "traffic": None,
-                "per_launch_flops": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
-    gb = gather_bytes(spec, batch)
-    g_ms, g_l = stages.get("gather_pool", (0.0, 1))
-    g_avg = g_ms / max(g_l, 1) / 1e3
-    gather = {"bound": "hbm", "achieved": round(gb / g_avg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-              "frac": round(gb / g_avg / 1e9 / HBM_PEAK_GBS, 4), "per_launch_bytes": gb,
-              "avg_launch_us": round(g_avg * 1e6, 2), "ids": "uniform" if args.uniform_ids else "zipf"}
+    if "bound" in d_entry:
+        roof = {"bound": d_entry["bound"], "kernel": dom, "achieved": d_entry["achieved"], "peak": d_entry["peak"],
+                "unit": d_entry["unit"], "frac": d_entry["frac"], "traffic": None,
+                "per_launch": d_entry["per_launch"], "avg_launch_us": d_entry["avg_launch_us"]}
     line = {
         "metric": "scored candidates/sec at 1 GPU",
         "value": round(value, 1),
@@ -181,9 +200,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "candidates_per_step": n,
                    "requests_per_step": db.n_requests},
         "roofline": roof,
-        "gather_roofline": gather,
-        "stage_ms_per_step": {k: round(v[0] / calls, 4) for k, v in stages.items()},
-        "dense_gflop_per_step": round(flops_step / 1e9, 2),
+        "stages": table,
+        "ids": "uniform" if args.uniform_ids else "zipf",
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
