@@ -177,7 +177,7 @@ static cvr_model* new_model(const cvr_spec* spec, const cvr_table* tables, int32
 static cvr_status check_segments(const cvr_model* m, std::string& why) {
   if (m->segs.size() > (size_t)kMaxASegments) { why = "model input alternates sides too often (max 4 runs)"; return CVR_ERR_UNSUPPORTED; }
   for (const auto& sg : m->segs)
-    if (sg.k_end % 8 || sg.col0 % 8) { why = "each run of same-side features must be a multiple of 8 columns"; return CVR_ERR_UNSUPPORTED; }
+    if (sg.k_end % 32 || sg.col0 % 8) { why = "each run of same-side features must end on a multiple of 32 columns"; return CVR_ERR_UNSUPPORTED; }
   if (m->e_dim % 32) { why = "model input width must be a multiple of 32"; return CVR_ERR_UNSUPPORTED; }
   return CVR_OK;
 }
