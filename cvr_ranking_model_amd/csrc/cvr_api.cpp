@@ -268,6 +268,7 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     w.hseq = take((size_t)P * d * lp);
     w.chunk_off = take((size_t)(S * R + 1) * 4);
     w.pool_part = take((size_t)(P / kSeqChunk + S * R + 1) * d * 4);
+    w.chunk_desc = take((size_t)(P / kSeqChunk + S * R + 1) * 8);
     w.seq_pool = take((size_t)S * R * d * 4);
     w.query = take((size_t)S * n * d * 4);
     w.mixhid = take((size_t)s.mixer_heads * n * s.mixer_hidden * lp);

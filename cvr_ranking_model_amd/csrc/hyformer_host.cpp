@@ -71,7 +71,8 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
 
   // ---- B3-B5: sequence encoding and mean pools (per request)
   int32_t* chunk_off = (int32_t*)(ws + w.chunk_off);
-  e = L(STAGE_SWIGLU, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, s); });
+  int2* chunk_desc = (int2*)(ws + w.chunk_desc);
+  e = L(STAGE_SWIGLU, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, chunk_desc, s); });
   if (e != hipSuccess) return e;
   {
     SwigluParams p{};
@@ -91,6 +92,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       col += t.dim;
     }
     p.chunk_off = chunk_off;
+    p.desc = chunk_desc;
     p.Wgu = (const __bf16*)m->wptr("seq.0.gate.weight");
     p.wgu_gstride = group_stride(m, [](int i) { return "seq." + S_(i) + ".gate.weight"; }, S, 2);
     p.bgu = (const float*)m->wptr("seq.0.gate.bias");

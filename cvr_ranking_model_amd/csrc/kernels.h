@@ -15,7 +15,7 @@ enum : int32_t {
 };
 
 constexpr int kMaxGatherFeatures = 32;
-constexpr int kSeqChunk = 64;  // positions per SwiGLU work item (never spanning two sequences)
+constexpr int kSeqChunk = 32;  // positions per SwiGLU work item (never spanning two sequences)
 constexpr int kMaxASegments = 4;
 
 // ---------------------------------------------------------------- expand (A0/B0)
@@ -112,8 +112,9 @@ constexpr int kMaxTasks = 8;
 constexpr int kMaxExperts = 8;
 
 // Chunk table: chunk_off[g] = number of kSeqChunk-position chunks before segment g = s*R + r.
+// and one descriptor per chunk (first position; segment << 8 | positions).
 hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
-                              hipStream_t st);
+                              int2* desc, hipStream_t st);
 
 struct SwigluParams {
   const int32_t* seq_offsets;   // [S][R+1]
@@ -126,6 +127,7 @@ struct SwigluParams {
   int64_t col_rows[kMaxSeqCols];
   const float* col_table[kMaxSeqCols];
   const int32_t* chunk_off;     // [S*R+1]
+  const int2* desc;             // [chunks]
   const __bf16* Wgu;            // per sequence [2*256][128]: gate rows then up rows
   int64_t wgu_gstride;
   const float* bgu;             // per sequence [2*256]

@@ -9,10 +9,10 @@
 // (sequence, request) segment into the next, so the per-chunk column sums of the encoded
 // states reduce to each segment's mean pool in a fixed order (bitwise reproducible).
 //
-// swiglu_kernel, per chunk (4 waves):
-//   1. gather: each position's 4 rows (fp32) -> clamp -> bf16 -> LDS tile E [64][128];
-//   2. gate|up = E W_gu^T (MFMA 32x32x16, fp32 accumulate); wave w owns gate columns
-//      64w..64w+63 and the matching up columns, so SiLU(gate+b) * (up+b) is formed in
+// swiglu_kernel, per chunk of 32 positions (4 waves):
+//   1. gather: each position's 4 rows (fp32) -> clamp -> bf16 -> LDS tile E [32][128];
+//   2. gate|up = W_gu E^T (MFMA 32x32x16, fp32 accumulate); wave w owns gate units
+//      64w..64w+63 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
 //      registers and written to LDS as bf16 (the input of the down projection);
 //   3. H = A W_down^T + b (MFMA), rounded to bf16 and stored; the rounded values are
 //      summed per column over the chunk's positions for the mean pool.
@@ -57,161 +57,234 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* __rest
   if (t == 1023) chunk_off[SR] = part[1023];
 }
 
-hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, chunk_off);
-  return hipGetLastError();
-}
-
-// Segment (s*R + r) and position range of chunk b, or false if b is past the last chunk.
-__device__ __forceinline__ bool locate_chunk(const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ seq_offsets,
-                                             int R, int S, int64_t n_positions, int b, int& seg, int64_t& p0, int& np) {
-  const int SR = S * R;
-  if (b >= chunk_off[SR]) return false;
-  int lo = 0, hi = SR - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_off[mid] <= b) lo = mid; else hi = mid - 1;
-  }
-  seg = lo;
-  const int s = lo / R, r = lo % R;
+// One descriptor per chunk: x = first position, y = (segment << 8) | positions in the chunk.
+__global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restrict__ seq_offsets, int R, int S,
+                                                         int64_t n_positions, const int32_t* __restrict__ chunk_off,
+                                                         int2* __restrict__ desc) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= S * R) return;
+  const int s = g / R, r = g % R;
   int64_t a = seq_offsets[(int64_t)s * (R + 1) + r], e = seq_offsets[(int64_t)s * (R + 1) + r + 1];
   a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
   e = e < a ? a : (e > n_positions ? n_positions : e);
-  p0 = a + (int64_t)(b - chunk_off[lo]) * kSeqChunk;
-  const int64_t left = e - p0;
-  np = left > kSeqChunk ? kSeqChunk : (int)left;
-  return np > 0;
+  const int c0 = chunk_off[g], c1 = chunk_off[g + 1];
+  for (int c = c0; c < c1; ++c) {
+    const int64_t p0 = a + (int64_t)(c - c0) * kSeqChunk;
+    const int64_t left = e - p0;
+    const int np = left > kSeqChunk ? kSeqChunk : (int)left;
+    desc[c] = make_int2((int)p0, (g << 8) | np);
+  }
+}
+
+hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
+                              int2* desc, hipStream_t st) {
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, chunk_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S * R == 0) return e;
+  hipLaunchKernelGGL(chunk_desc_kernel, dim3((S * R + 255) / 256), dim3(256), 0, st, seq_offsets, R, S, n_positions,
+                     chunk_off, desc);
+  return hipGetLastError();
 }
 
 constexpr int kD = 128;        // token width
 constexpr int kHid = 256;      // SwiGLU hidden width
 constexpr int kEPitch = kD + 8;
 constexpr int kAPitch = kHid + 8;
+constexpr int kM = kSeqChunk;  // positions per chunk = MFMA M tile
+static_assert(kM == 32, "one 32-row MFMA tile per chunk");
 
-__global__ __launch_bounds__(256) void swiglu_kernel(const SwigluParams p) {
+// Persistent: block b walks a contiguous range of chunks; each wave keeps its share of the
+// sequence's weights in registers (gate/up: 2+2 column tiles x 8 k-steps; down: 1 column
+// tile x 16 k-steps) and reloads them only when the range crosses into another sequence.
+// While one chunk's MFMAs run, the next chunk's table rows are already in flight.
+__global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
   typedef bf16x8 V8;
-  __shared__ __align__(16) bf16 Es[kSeqChunk * kEPitch];
-  __shared__ __align__(16) bf16 As[kSeqChunk * kAPitch];
+  __shared__ __align__(16) bf16 Es[kM * kEPitch];
+  __shared__ __align__(16) bf16 As[kM * kAPitch];
+  __shared__ __align__(16) float Bgu[2 * kHid];  // gate then up biases of the current sequence
 
-  int seg, np;
-  int64_t p0;
-  if (!locate_chunk(p.chunk_off, p.seq_offsets, p.R, p.S, p.n_positions, blockIdx.x, seg, p0, np)) return;
-  const int s = seg / p.R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int SR = p.S * p.R;
+  const int total = p.chunk_off[SR];
+  const int per = (total + gridDim.x - 1) / gridDim.x;
+  const int c_begin = blockIdx.x * per;
+  const int c_end = c_begin + per < total ? c_begin + per : total;
+  if (c_begin >= c_end) return;
 
-  // 1. gather + clamp + bf16 into Es (float4 granules: 64 positions x 32 granules)
-  bool bad = false;
+  // Each thread owns 4 float4 granules of the 32x128 chunk tile: granule i covers position
+  // (tid + 256 i) / 32 and columns 4 * ((tid + 256 i) % 32) .. +3, which sit in sequence
+  // column gcol[i] (fixed per thread).
+  int gcol[4], goff[4];
 #pragma unroll
-  for (int i = 0; i < (kSeqChunk * kD / 4) / 256; ++i) {
-    const int idx = tid + i * 256;
-    const int pos = idx >> 5;
-    const int col = (idx & 31) * 4;
+  for (int i = 0; i < 4; ++i) {
+    const int col = ((tid + i * 256) & 31) * 4;
     int ci = 0;
 #pragma unroll
-    for (int c = 1; c < kMaxSeqCols; ++c)
-      if (c < p.ncols && col >= p.col_off[c]) ci = c;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (pos < np) {
-      const int32_t id = p.seq_ids[(p0 + pos) * p.ncols + ci];
-      if (id >= 0 && (int64_t)id < p.col_rows[ci])
-        v = *reinterpret_cast<const float4*>(p.col_table[ci] + (int64_t)id * p.col_dim[ci] + (col - p.col_off[ci]));
-      else
-        bad = true;
-    }
-    bf16x4 o;
-    o[0] = (bf16)clamp_keep_nan(v.x, p.clamp);
-    o[1] = (bf16)clamp_keep_nan(v.y, p.clamp);
-    o[2] = (bf16)clamp_keep_nan(v.z, p.clamp);
-    o[3] = (bf16)clamp_keep_nan(v.w, p.clamp);
-    *reinterpret_cast<bf16x4*>(&Es[pos * kEPitch + col]) = o;
+    for (int cc = 1; cc < kMaxSeqCols; ++cc)
+      if (cc < p.ncols && col >= p.col_off[cc]) ci = cc;
+    gcol[i] = ci;
+    goff[i] = col - p.col_off[ci];
   }
-  if (bad) raise_flag(p.flag, ERRF_SEQ_ID_RANGE);
-  __syncthreads();
-
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  const bf16* Wgu = p.Wgu + (int64_t)s * p.wgu_gstride;   // [512][128]: gate rows 0..255, up rows 256..511
-  const float* bgu = p.bgu + (int64_t)s * p.bgu_gstride;  // [512]
-  // 2. gate|up for this wave's 64 hidden units
-  {
-    f32x16 acc[2][4];
+  const int gpos0 = tid >> 5;  // position of granule 0; granule i is at gpos0 + 8 i
+  bool bad = false;
+  auto desc_of = [&](int c) { return p.desc[c < c_end ? c : c_end - 1]; };
+  auto load_ids = [&](int2 d, int32_t (&id)[4]) {
+    const int np = d.y & 255;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int pos = gpos0 + 8 * i;
+      id[i] = p.seq_ids[((int64_t)d.x + (pos < np ? pos : 0)) * p.ncols + gcol[i]];
+    }
+  };
+  auto load_rows = [&](int2 d, const int32_t (&id)[4], float4 (&row)[4]) {
+    const int np = d.y & 255;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t r = id[i];
+      const bool ok = r >= 0 && (int64_t)r < p.col_rows[gcol[i]];
+      if (!ok && gpos0 + 8 * i < np) bad = true;
+      row[i] = *reinterpret_cast<const float4*>(p.col_table[gcol[i]] + (int64_t)(ok ? r : 0) * p.col_dim[gcol[i]] + goff[i]);
+      if (!ok || gpos0 + 8 * i >= np) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  V8 wg[4][kD / 16];   // gate tiles 0,1 and up tiles 2,3 of this wave
+  V8 wd[kHid / 16];    // down projection, output columns 32*wave..32*wave+31
+  float bd = 0.f;
+  int cur_s = -1;
+  auto load_weights = [&](int s) {
+    const bf16* Wgu = p.Wgu + (int64_t)s * p.wgu_gstride;
+    const float* bgu = p.bgu + (int64_t)s * p.bgu_gstride;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = (j < 2 ? 0 : kHid) + wave * 64 + (j & 1) * 32 + lr;
+#pragma unroll
+      for (int k = 0; k < kD / 16; ++k) wg[j][k] = *reinterpret_cast<const V8*>(Wgu + (int64_t)n * kD + k * 16 + lk);
+    }
+    __syncthreads();  // no wave still reads the previous sequence's biases
+    for (int h = tid; h < 2 * kHid; h += 256) Bgu[h] = bgu[h];
+    const bf16* Wd = p.Wd + (int64_t)s * p.wd_gstride;
+    const int n = wave * 32 + lr;
+#pragma unroll
+    for (int k = 0; k < kHid / 16; ++k) wd[k] = *reinterpret_cast<const V8*>(Wd + (int64_t)n * kHid + k * 16 + lk);
+    bd = (p.bd + (int64_t)s * p.bd_gstride)[n];
+    cur_s = s;
+  };
+
+  // Software pipeline over chunks: rows of c+1, ids of c+2 and the descriptor of c+3 are in
+  // flight while chunk c runs its MFMAs (indices past the range repeat the last chunk).
+  int2 dc = desc_of(c_begin), d1 = desc_of(c_begin + 1), d2 = desc_of(c_begin + 2);
+  int32_t id_c[4], id_1[4];
+  float4 row_c[4], row_1[4];
+  load_ids(dc, id_c);
+  load_ids(d1, id_1);
+  load_rows(dc, id_c, row_c);
+#pragma unroll 1
+  for (int c = c_begin; c < c_end; ++c) {
+    const int seg = dc.y >> 8, np = dc.y & 255;
+    const int64_t p0 = dc.x;
+    const int s = seg / p.R;
+    if (s != cur_s) load_weights(s);
+    // 1. clamp + bf16 of chunk c's rows into the E tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + i * 256;
+      bf16x4 o;
+      o[0] = (bf16)clamp_keep_nan(row_c[i].x, p.clamp);
+      o[1] = (bf16)clamp_keep_nan(row_c[i].y, p.clamp);
+      o[2] = (bf16)clamp_keep_nan(row_c[i].z, p.clamp);
+      o[3] = (bf16)clamp_keep_nan(row_c[i].w, p.clamp);
+      *reinterpret_cast<bf16x4*>(&Es[(idx >> 5) * kEPitch + (idx & 31) * 4]) = o;
+    }
+    __syncthreads();
+    // advance the pipeline
+    load_rows(d1, id_1, row_1);
+    int32_t id_2[4];
+    load_ids(d2, id_2);
+    const int2 d3 = desc_of(c + 3);
+
+    // 2. gate|up for this wave's 64 hidden units, computed transposed (hidden units x
+    //    positions) so each lane ends with four consecutive hidden units of one position:
+    //    SiLU(gate) * up for them leaves as one 8-byte LDS write.
+    {
+      f32x16 acc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kD; k += 16) {
-      V8 a[2], b[4];
+      for (int k = 0; k < kD / 16; ++k) {
+        const V8 e = *reinterpret_cast<const V8*>(&Es[lr * kEPitch + k * 16 + lk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const V8*>(&Es[(i * 32 + lr) * kEPitch + k + lk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = (j < 2 ? 0 : kHid) + wave * 64 + (j & 1) * 32 + lr;
-        b[j] = *reinterpret_cast<const V8*>(Wgu + (int64_t)n * kD + k + lk);
+        for (int j = 0; j < 4; ++j) acc[j] = Lowp<bf16>::mfma32(wg[j][k], e, acc[j]);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Lowp<bf16>::mfma32(a[i], b[j], acc[i][j]);
-    }
+        for (int v4 = 0; v4 < 4; ++v4) {
+          // rows 8*v4 + 4*(lane/32) .. +3 of tile j are hidden units; column lr is the position
+          const int h0 = wave * 64 + j * 32 + 8 * v4 + 4 * (lane >> 5);
+          const float4 bg4 = *reinterpret_cast<const float4*>(&Bgu[h0]);
+          const float4 bu4 = *reinterpret_cast<const float4*>(&Bgu[kHid + h0]);
+          const float bgv[4] = {bg4.x, bg4.y, bg4.z, bg4.w};
+          const float buv[4] = {bu4.x, bu4.y, bu4.z, bu4.w};
+          bf16x4 o;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = wave * 64 + j * 32 + lr;  // hidden unit
-      const float bg = bgu[n], bu = bgu[kHid + n];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const float g = acc[i][j][v] + bg;
-          const float u = acc[i][j + 2][v] + bu;
-          const float sg = g / (1.0f + expf(-g));
-          As[m * kAPitch + n] = (bf16)(sg * u);
+          for (int q = 0; q < 4; ++q) {
+            const float g = acc[j][4 * v4 + q] + bgv[q];
+            const float u = acc[j + 2][4 * v4 + q] + buv[q];
+            const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+            o[q] = (bf16)(sg * u);
+          }
+          *reinterpret_cast<bf16x4*>(&As[lr * kAPitch + h0]) = o;
         }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // 3. down projection: wave w owns output columns 32w..32w+31
-  const bf16* Wd = p.Wd + (int64_t)s * p.wd_gstride;  // [128][256]
-  const float* bd = p.bd + (int64_t)s * p.bd_gstride;
-  f32x16 acc2[2];
+    // 3. down projection -> H (bf16) and column sums for the mean pool; even and odd k steps
+    //    accumulate separately so consecutive MFMAs do not wait on each other
+    f32x16 acc2[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc2[i][v] = 0.f;
-  const int n = wave * 32 + lr;
-#pragma unroll 4
-  for (int k = 0; k < kHid; k += 16) {
-    const V8 b = *reinterpret_cast<const V8*>(Wd + (int64_t)n * kHid + k + lk);
+      for (int v = 0; v < 16; ++v) acc2[h][v] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const V8 a = *reinterpret_cast<const V8*>(&As[(i * 32 + lr) * kAPitch + k + lk]);
-      acc2[i] = Lowp<bf16>::mfma32(a, b, acc2[i]);
+    for (int k = 0; k < kHid / 16; ++k) {
+      const V8 a = *reinterpret_cast<const V8*>(&As[lr * kAPitch + k * 16 + lk]);
+      acc2[k & 1] = Lowp<bf16>::mfma32(a, wd[k], acc2[k & 1]);
     }
-  }
-  const float bn = bd[n];
-  float colsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+    const int n = wave * 32 + lr;
+    float colsum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (m < np) {
-        const bf16 h = (bf16)(acc2[i][v] + bn);
+        const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
         p.H[(p0 + m) * kD + n] = h;
         colsum += (float)h;
       }
     }
-  colsum += __shfl_xor(colsum, 32);
-  if (lane < 32) p.part[(int64_t)blockIdx.x * kD + n] = colsum;
+    colsum += __shfl_xor(colsum, 32);
+    if (lane < 32) p.part[(int64_t)c * kD + n] = colsum;
+    dc = d1;
+    d1 = d2;
+    d2 = d3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      row_c[i] = row_1[i];
+      id_1[i] = id_2[i];
+    }
+  }
+  if (bad) raise_flag(p.flag, ERRF_SEQ_ID_RANGE);
 }
 
 hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) {
   if (max_chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(max_chunks), dim3(256), 0, st, p);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int blocks = max_chunks < cus ? max_chunks : cus;
+  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
