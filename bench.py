@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--variant", default="bench")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one plain 256 MiB fp32 copy kernel (torch.neg) so a "
+                         "hardware-counter run can scale its byte counters against a known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with no "
@@ -151,6 +154,13 @@ def main():
     dt = time.perf_counter() - t0
     stages, calls = model.timing_end()
     assert model.sync_status() == cv.CVR_OK
+    if args.calibrate_copy:
+        # reads 256 MiB and writes 256 MiB once each: the reference for FETCH_SIZE / WRITE_SIZE
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step = dt * 1e3 / args.steps
     value = n * args.steps / dt
 

@@ -328,10 +328,309 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   }
 }
 
-// Tile choice (measured on the 1024x1024 hidden layers): 256x256 with 32-wide slices when
-// the grid holds at least four tiles per CU; otherwise 128x128 (64-wide slices when every
-// K-segment boundary allows, else 32-wide); 64x64 when even 128x128 cannot cover the chip
-// (the per-candidate GEMMs of the CVR model at small batch).
+// Hardware dispatch puts block b on XCD b % 8, in order b / 8 within it.  Renumber blocks so
+// each XCD receives one contiguous run of logical tiles (a bijection for any block count):
+// the tiles that share an A row-block (consecutive in N) then run together on one XCD and
+// reuse it from that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  const int q = total >> 3, rem = total & 7, x = b & 7;
+  return x * q + (x < rem ? x : rem) + (b >> 3);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte global -> LDS transfer per lane, written to lds_wave_base + 16 * lane (the LDS
+// base must be the same for every lane of the wave).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wide-layer GEMM, persistent: each block walks a list of BM x BN output tiles (256 x 256
+// or 256 x 128) with 4 waves of (BM/2) x (BN/2) built from MFMA 32x32x16 tiles.  K advances
+// in BK-wide slices that go from global memory straight into an NS-slot LDS ring (no register
+// staging), and the slice stream runs across tile boundaries: slice s+NS is requested as soon
+// as slot s%NS is released, mid-way through slice s, so the next tile's first slices are in
+// flight while this tile's epilogue runs.  Transfers and fragment reads are interleaved with
+// the matrix instructions so that their issue hides behind the MFMA pipe.
+// Stores and loads share one vector-memory counter, so a store holds up every later wait.
+// The epilogue therefore first lets the in-flight slices land and only then issues its stores;
+// the next tile's first NS-1 slices need no wait, and the first wait that does come (for slice
+// NS, requested after the stores) is two slices of matrix work later.
+// LDS banks: a 16-byte read is served 16 lanes (256 bytes) at a time, and the 16 lanes of a
+// fragment read cover 16 consecutive rows at one k chunk.  Rows are BK*2 bytes with the chunk
+// index XOR-ed with swz(row) = (row/4)%4 for 64-byte rows and (row/2)%8 for 128-byte rows,
+// which places those 16 reads on 16 distinct 16-byte bank groups.  The loaders choose which
+// chunk each lane fetches so that the fixed lane->LDS placement of a transfer (lane l at byte
+// 16 l) realises the layout.  Everything lives in one LDS allocation (ring, per-wave output
+// staging, bias): the waits on the ring are the explicit ones below.
+// The W fragment is the MFMA's first operand, so each lane's accumulators hold 4 consecutive
+// output columns of one row; the epilogue stages them through a per-wave LDS area and writes
+// whole row segments.
+// Tile order: each XCD gets one contiguous run of tiles and its blocks take them round-robin,
+// so tiles that share an A row-block run at the same time on the same L2.
+// Requirements (checked by the launcher): N % BN == 0, N <= kBigMaxN, K and every A-segment
+// boundary multiples of BK, 16-bit A sources and output, contiguous output rows with
+// ldc % 8 == 0, no residual, a grid that is a multiple of 8 blocks.
+constexpr int kBigMaxN = 1024;
+template <typename T, int BM, int BN, int BK, int NS, int MINB>
+__global__ __launch_bounds__(256, MINB) void gemm_big_kernel(const GemmParams p) {
+  typedef typename Lowp<T>::vec8 V8;
+  constexpr int KC = BK / 8;              // 16-byte chunks per slice row
+  constexpr int RPI = 64 / KC;            // rows filled by one wave transfer (1 KB)
+  constexpr int TPA = BM / RPI / 4;       // transfers per wave per slice: A rows
+  constexpr int TPB = BN / RPI / 4;       //                                W rows
+  constexpr int L = TPA + TPB;
+  constexpr int KS = BK / 16;             // MFMA k steps per slice
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int kSlot = (BM + BN) * BK;   // elements per ring slot: BM A rows, then BN W rows
+  constexpr int kStagePitch = WTN * 2 + 8;  // bytes per staged output row (odd multiple of 8)
+  constexpr int RPS = 512 / (WTN * 2);      // staged rows written back per wave instruction
+  constexpr int LPR = WTN / 4;              // lanes per staged row on the way out (8 bytes each)
+  static_assert(BK == 32 || BK == 64, "slice width");
+  static_assert(TPA >= 1 && TPB >= 1 && BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "loader shape");
+  static_assert(NS >= 2 && L * (NS - 2) < 64, "ring depth");
+  // One LDS allocation: the ring, the per-wave staging areas, the bias of all N columns.
+  constexpr int kRingBytes = NS * kSlot * (int)sizeof(T);
+  constexpr int kStageBytes = 4 * 32 * kStagePitch;
+  __shared__ __align__(1024) char lds[kRingBytes + kStageBytes + kBigMaxN * 4];
+  T* const smem = reinterpret_cast<T*>(lds);
+  char* const stage = lds + kRingBytes + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 32 * kStagePitch;
+  float* const bias_s = reinterpret_cast<float*>(lds + kRingBytes + kStageBytes);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = blockIdx.y;
+  const int ntn = p.N / BN;
+  const int total = ((p.M + BM - 1) / BM) * ntn;
+  const int x = blockIdx.x & 7, stride = gridDim.x >> 3;
+  const int tq = total >> 3, trem = total & 7;
+  const int first = x * tq + (x < trem ? x : trem) + (blockIdx.x >> 3);
+  const int last = (x + 1) * tq + (x + 1 < trem ? x + 1 : trem);
+  if (first >= last) return;
+  for (int c = tid; c < p.N; c += 256) bias_s[c] = p.bias ? p.bias[(int64_t)g * p.bias_gstride + c] : 0.f;
+
+  auto swz = [](int row) { return KC == 4 ? (row >> 2) & 3 : (row >> 1) & 7; };
+  // Loader: transfer (4i + wave) fills rows RPI*(4i+wave) .. +RPI-1; lane l lands in row
+  // l/KC of them at slot l%KC and must fetch k-chunk slot ^ swz(row).  swz(row) is the same
+  // for every i (RPI*4 is a multiple of the swizzle period), so each lane has one k-chunk.
+  const int lrow = lane / KC;
+  const int kch = (lane % KC) ^ swz(RPI * wave + lrow);
+  const int nk = p.K / BK;
+
+  // Issue cursor: tile it, slice ik (runs NS slices ahead of the compute cursor).
+  int it = first, ik = 0;
+  int am[TPA];
+  const T* wrow[TPB];
+  int seg = -1, seg_kb = 0, seg_end = 0;
+  int64_t seg_kstride = 8;
+  const T* aptr[TPA];
+  auto set_tile = [&](int t) {
+    const int tm0 = (t / ntn) * BM, tn0 = (t % ntn) * BN;
+#pragma unroll
+    for (int i = 0; i < TPA; ++i) {
+      const int r = tm0 + RPI * (4 * i + wave) + lrow;
+      am[i] = r < p.M ? r : p.M - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < TPB; ++i)
+      wrow[i] = reinterpret_cast<const T*>(p.W) + (int64_t)g * p.w_gstride +
+                (int64_t)(tn0 + RPI * (4 * i + wave) + lrow) * p.K + kch * 8;
+    seg = -1;
+    seg_kb = 0;
+    seg_end = 0;
+  };
+  auto enter_segment = [&](int k0) {
+    while (k0 >= seg_end) {
+      ++seg;
+      seg_kb = seg == 0 ? 0 : p.seg[seg - 1].k_end;
+      seg_end = p.seg[seg].k_end;
+    }
+    const ASeg& S = p.seg[seg];
+    seg_kstride = S.kstride8;
+#pragma unroll
+    for (int i = 0; i < TPA; ++i) {
+      const int64_t row = S.rowmap ? (int64_t)S.rowmap[am[i]] : (int64_t)am[i];
+      aptr[i] = reinterpret_cast<const T*>(S.ptr) + (int64_t)g * S.gstride + row * S.ld +
+                (int64_t)((S.col0 >> 3) + kch) * S.kstride8;
+    }
+  };
+  // Make the issue cursor's slice addressable (its A segment current).
+  auto prepare = [&]() {
+    if (ik * BK >= seg_end) enter_segment(ik * BK);
+  };
+  // Move the issue cursor on; past this block's last slice it stays there, so the remaining
+  // requests repeat that slice into slots that are not read any more.
+  auto advance = [&]() {
+    if (ik + 1 < nk) {
+      ++ik;
+    } else if (it + stride < last) {
+      it += stride;
+      ik = 0;
+      set_tile(it);
+    }
+  };
+  auto issue = [&](int slot) {
+    const int k0 = ik * BK;
+    const int64_t off = (int64_t)((k0 - seg_kb) >> 3) * seg_kstride;
+    T* sA = smem + slot * kSlot;
+    T* sB = sA + BM * BK;
+#pragma unroll
+    for (int i = 0; i < TPA; ++i) load_lds16(aptr[i] + off, sA + (4 * i + wave) * 512);
+#pragma unroll
+    for (int i = 0; i < TPB; ++i) load_lds16(wrow[i] + k0, sB + (4 * i + wave) * 512);
+  };
+
+  const int lr = lane & 31, lc = lane >> 5;
+  const int sw = swz(lr);
+  const int arow = (wm * WTM + lr) * BK;
+  const int brow = BM * BK + (wn * WTN + lr) * BK;
+  auto read_frags = [&](int slot, int ks, V8 (&fa)[FM], V8 (&fb)[FN]) {
+    const T* base = smem + slot * kSlot;
+    const int c = ((2 * ks + lc) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const V8*>(base + arow + i * 32 * BK + c);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const V8*>(base + brow + j * 32 * BK + c);
+  };
+  f32x16 acc[FM][FN];
+  auto mfmas = [&](const V8 (&fa)[FM], const V8 (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = Lowp<T>::mfma32(fb[j], fa[i], acc[i][j]);
+  };
+  constexpr int NMF = FM * FN;  // MFMAs per k step
+  constexpr int NRD = FM + FN;  // fragment reads per k step
+
+  // Every iteration requests exactly one slice, so exactly L * (NS - 2) transfers are younger
+  // than slice s+1 when the loop waits for it.
+  set_tile(it);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    prepare();
+    issue(s);
+    advance();
+  }
+  V8 fa[2][FM], fb[2][FN];
+  wait_vmcnt<L * (NS - 1)>();
+  __syncthreads();
+  read_frags(0, 0, fa[0], fb[0]);
+  int slot = 0;
+  bool landed = false;  // the first NS-1 slices of this tile are known to be in LDS
+
+#pragma unroll 1
+  for (int tc = first; tc < last; tc += stride) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+#pragma unroll 1
+    for (int kt = 0; kt < nk; ++kt) {
+      const int next = slot == NS - 1 ? 0 : slot + 1;
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        read_frags(slot, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        mfmas(fa[ks & 1], fb[ks & 1]);
+#pragma unroll
+        for (int q = 0; q < NRD; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);  // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              // 1 LDS read
+        }
+      }
+      prepare();
+      // Slice s+1 has landed for this wave (the barrier covers the other waves), and every
+      // wave is done reading slot s%NS before it is refilled.
+      if (!(landed && kt < NS - 1)) wait_vmcnt<L * (NS - 2)>();
+      __syncthreads();
+      issue(slot);
+      read_frags(next, 0, fa[KS & 1], fb[KS & 1]);
+      mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
+      // next slice's first fragments early (they gate the next iteration), transfers after
+#pragma unroll
+      for (int q = 0; q < NRD; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      }
+#pragma unroll
+      for (int q = 0; q < L; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 transfer
+      }
+      advance();
+      slot = next;
+    }
+
+    // Epilogue: lane holds, for m-tile i and n-tile j, row m = .. + lane%32 and the four
+    // consecutive columns n = .. + 8*q + 4*(lane/32) + 0..3 for q = 0..3.  Per m-tile the wave
+    // writes its 32 x WTN block into its own staging area (8-byte writes; a pitch that is an
+    // odd multiple of 8 bytes keeps 32 rows on distinct banks) and reads it back as rows.
+    const int m0 = (tc / ntn) * BM, ncol0 = (tc % ntn) * BN + wn * WTN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int mrow0 = m0 + wm * WTM + i * 32;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef T T4 __attribute__((ext_vector_type(4)));
+          const int col = j * 32 + 8 * q + 4 * lc;
+          const float4 b4 = *reinterpret_cast<const float4*>(&bias_s[ncol0 + col]);
+          const float bq[4] = {b4.x, b4.y, b4.z, b4.w};
+          T4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[i][j][4 * q + e] + bq[e];
+            if (p.relu) v = v > 0.f ? v : 0.f;
+            o[e] = Lowp<T>::from_f32(v);
+          }
+          *reinterpret_cast<T4*>(stage + lr * kStagePitch + col * 2) = o;
+        }
+      if (i == 0) wait_vmcnt<0>();  // the next tile's first slices land before any store
+#pragma unroll
+      for (int rr = 0; rr < 32 / RPS; ++rr) {
+        const int r = rr * RPS + lane / LPR;
+        const uint2 v = *reinterpret_cast<const uint2*>(stage + r * kStagePitch + (lane % LPR) * 8);
+        const int m = mrow0 + r;
+        if (m < p.M)
+          *reinterpret_cast<uint2*>(reinterpret_cast<T*>(p.C) + (int64_t)g * p.c_gstride + (int64_t)m * p.ldc + ncol0 +
+                                    4 * (lane % LPR)) = v;
+      }
+    }
+    landed = true;
+  }
+  // Requests past the last slice must land before the block's LDS is released.
+  wait_vmcnt<0>();
+}
+
+// Persistent grid for the wide-layer kernel: per_cu blocks per CU, a multiple of 8 (every XCD
+// gets the same number of blocks), never more than the tiles need.
+static int big_grid(int tiles, int per_cu) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    cus = n;
+  }
+  int b = cus * per_cu < tiles ? cus * per_cu : tiles;
+  b = (b + 7) & ~7;
+  return b < 8 ? 8 : b;
+}
+
+// Tile choice: the persistent wide-layer kernel (256 x 128 tiles, two blocks per CU) when its
+// layout requirements hold and there is at least a tile per CU; otherwise 128x128 (64-wide
+// slices when every K-segment boundary allows, else 32-wide); 64x64 when even 128x128 cannot
+// cover the chip (the per-candidate GEMMs of the CVR model at small batch).
 template <typename T, bool AF32>
 static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
@@ -339,14 +638,18 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   for (int s = 0; s < p.nseg; ++s) bk64 = bk64 && p.seg[s].k_end % 64 == 0;
   const char* env = getenv("CVR_GEMM_TILE");
   int tile = env ? atoi(env) : 0;
+  const bool big_ok = !AF32 && !p.out_f32 && p.N % 128 == 0 && p.N <= kBigMaxN && p.c_nstride8 == 8 && !p.R &&
+                      (p.ldc & 7) == 0 && (p.c_gstride & 7) == 0;
+  if (tile == 256 && !big_ok) tile = 0;
   if (!tile) {
-    if (p.N % 256 == 0 && (int64_t)tiles(256, 256) * p.groups >= 1024) tile = 256;
+    if (big_ok && (int64_t)tiles(256, 128) * p.groups >= 256) tile = 256;
     else if ((int64_t)tiles(128, 128) * p.groups >= 256) tile = 128;
     else tile = 64;
   }
   const dim3 blk(256);
   if (tile == 256) {
-    hipLaunchKernelGGL((gemm_kernel<T, 256, 256, 2, 2, AF32, 32>), dim3(tiles(256, 256), p.groups), blk, 0, st, p);
+    if constexpr (AF32) return hipErrorInvalidValue;  // excluded above
+    else hipLaunchKernelGGL((gemm_big_kernel<T, 256, 128, 32, 2, 2>), dim3(big_grid(tiles(256, 128), 2), p.groups), blk, 0, st, p);
   } else if (tile == 128) {
     if (bk64) hipLaunchKernelGGL((gemm_kernel<T, 128, 128, 2, 2, AF32, 64>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
     else hipLaunchKernelGGL((gemm_kernel<T, 128, 128, 2, 2, AF32, 32>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
