@@ -79,6 +79,29 @@ def stage_work(spec, batch):
     return work
 
 
+def measured_traffic(stage):
+    """HBM bytes per launch of a stage's kernel from the committed byte-counter summaries.
+
+    Each summary under profiles/ carries "traffic-json:" lines naming the kernel's source file
+    and its sha256 at the time the counters were taken; a figure whose source has changed
+    since is stale and is not reported.
+    """
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic-json:"):
+                continue
+            rec = json.loads(line[len("traffic-json:"):])
+            if rec.get("stage") != stage or rec.get("bytes_per_launch") is None:
+                continue
+            src = os.path.join(ROOT, rec["source"])
+            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+                return None, os.path.basename(path) + " (stale: kernel source changed)"
+            return int(rec["bytes_per_launch"]), os.path.basename(path)
+    return None, None
+
+
 def cpu_baseline(spec, variant, weights, budget_s=10.0):
     import numpy as np
     import oracle
@@ -191,9 +214,12 @@ def main():
     d_entry = table[dom]
     roof = None
     if "bound" in d_entry:
+        traffic, source = measured_traffic(dom) if args.workload == "c2" and not args.uniform_ids else (None, None)
         roof = {"bound": d_entry["bound"], "kernel": dom, "achieved": d_entry["achieved"], "peak": d_entry["peak"],
-                "unit": d_entry["unit"], "frac": d_entry["frac"], "traffic": None,
+                "unit": d_entry["unit"], "frac": d_entry["frac"], "traffic": traffic,
                 "per_launch": d_entry["per_launch"], "avg_launch_us": d_entry["avg_launch_us"]}
+        if source:
+            roof["traffic_source"] = source
     line = {
         "metric": "scored candidates/sec at 1 GPU",
         "value": round(value, 1),

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
   if (p.n <= 0 || p.S <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attention_kernel, dim3(p.n, p.S), dim3(256), 0, st, p);
+  launch_k(attention_kernel, dim3(p.n, p.S), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

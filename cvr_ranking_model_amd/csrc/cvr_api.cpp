@@ -290,6 +290,11 @@ extern "C" cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, in
 }
 
 // ------------------------------------------------------------------ timing
+LaunchTiming& cvr::launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+
 
 void Timing::reset() {
   for (hipEvent_t e : ev) (void)hipEventDestroy(e);

@@ -9,7 +9,7 @@ __global__ void clear_flag_kernel(int32_t* flag) {
 }
 
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t st) {
-  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(64), 0, st, flag);
+  launch_k(clear_flag_kernel, dim3(1), dim3(64), 0, st, flag);
   return hipGetLastError();
 }
 
@@ -56,7 +56,7 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st) {
   if (p.seq_offsets && (int64_t)p.S * (p.R + 1) > work) work = (int64_t)p.S * (p.R + 1);
   const int threads = 256;
   const int64_t blocks = (work + threads - 1) / threads;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, p);
+  launch_k(expand_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -72,9 +72,9 @@ hipError_t launch_convert(const float* src, void* dst, int64_t n, int lowp, hipS
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (lowp == 0)
-    hipLaunchKernelGGL(convert_kernel<f16>, dim3((unsigned)blocks), dim3(256), 0, st, src, (f16*)dst, n);
+    launch_k(convert_kernel<f16>, dim3((unsigned)blocks), dim3(256), 0, st, src, (f16*)dst, n);
   else
-    hipLaunchKernelGGL(convert_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st, src, (bf16*)dst, n);
+    launch_k(convert_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st, src, (bf16*)dst, n);
   return hipGetLastError();
 }
 
@@ -100,7 +100,7 @@ hipError_t launch_fill_table(float* t, int64_t total, uint64_t seed, double step
   const int64_t quads = total / 4;
   int64_t blocks = (quads + 255) / 256;
   if (blocks > 262144) blocks = 262144;
-  if (blocks > 0) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, t, quads, seed, step);
+  if (blocks > 0) launch_k(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, t, quads, seed, step);
   return hipGetLastError();
 }
 

@@ -98,9 +98,9 @@ hipError_t launch_gather_pool(GatherParams& p, hipStream_t st) {
   p.total_blocks = blocks;
   if (blocks == 0) return hipSuccess;
   if (p.lowp == 0)
-    hipLaunchKernelGGL(gather_pool_kernel<f16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+    launch_k(gather_pool_kernel<f16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
   else
-    hipLaunchKernelGGL(gather_pool_kernel<bf16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+    launch_k(gather_pool_kernel<bf16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -649,13 +649,13 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   const dim3 blk(256);
   if (tile == 256) {
     if constexpr (AF32) return hipErrorInvalidValue;  // excluded above
-    else hipLaunchKernelGGL((gemm_big_kernel<T, 256, 128, 32, 2, 2>), dim3(big_grid(tiles(256, 128), 2), p.groups), blk, 0, st, p);
+    else launch_k((gemm_big_kernel<T, 256, 128, 32, 2, 2>), dim3(big_grid(tiles(256, 128), 2), p.groups), blk, 0, st, p);
   } else if (tile == 128) {
-    if (bk64) hipLaunchKernelGGL((gemm_kernel<T, 128, 128, 2, 2, AF32, 64>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
-    else hipLaunchKernelGGL((gemm_kernel<T, 128, 128, 2, 2, AF32, 32>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
+    if (bk64) launch_k((gemm_kernel<T, 128, 128, 2, 2, AF32, 64>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
+    else launch_k((gemm_kernel<T, 128, 128, 2, 2, AF32, 32>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
   } else {
-    if (bk64) hipLaunchKernelGGL((gemm_kernel<T, 64, 64, 2, 2, AF32, 64>), dim3(tiles(64, 64), p.groups), blk, 0, st, p);
-    else hipLaunchKernelGGL((gemm_kernel<T, 64, 64, 2, 2, AF32, 32>), dim3(tiles(64, 64), p.groups), blk, 0, st, p);
+    if (bk64) launch_k((gemm_kernel<T, 64, 64, 2, 2, AF32, 64>), dim3(tiles(64, 64), p.groups), blk, 0, st, p);
+    else launch_k((gemm_kernel<T, 64, 64, 2, 2, AF32, 32>), dim3(tiles(64, 64), p.groups), blk, 0, st, p);
   }
   return hipGetLastError();
 }
@@ -709,10 +709,10 @@ hipError_t launch_dlrm_output(const void* H, int32_t M, int32_t K, const void* w
   if (M <= 0) return hipSuccess;
   const int blocks = (M + 3) / 4;
   if (lowp == 0)
-    hipLaunchKernelGGL(dlrm_output_kernel<f16>, dim3(blocks), dim3(256), 0, st, (const f16*)H, M, K,
+    launch_k(dlrm_output_kernel<f16>, dim3(blocks), dim3(256), 0, st, (const f16*)H, M, K,
                        (const f16*)w, b, logits, out);
   else
-    hipLaunchKernelGGL(dlrm_output_kernel<bf16>, dim3(blocks), dim3(256), 0, st, (const bf16*)H, M, K,
+    launch_k(dlrm_output_kernel<bf16>, dim3(blocks), dim3(256), 0, st, (const bf16*)H, M, K,
                        (const bf16*)w, b, logits, out);
   return hipGetLastError();
 }

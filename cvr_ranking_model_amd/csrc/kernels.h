@@ -1,9 +1,31 @@
 // Launch interfaces of the libcvr kernels (host side).  Internal to the library.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace cvr {
+
+// ---------------------------------------------------------------- kernel launches
+// Every kernel goes through launch_k.  When the calling thread has armed a pair of timing
+// events (launch_timing), the launch carries them in its dispatch: the begin event is
+// stamped when the first kernel of the bracket starts and the end event when the last one
+// ends, so the measured time is the kernels' own, without host-side event packets in between.
+// Arguments are converted to the kernel's parameter types before they are packed.
+struct LaunchTiming {
+  hipEvent_t begin = nullptr, end = nullptr;
+  int launched = 0;
+};
+LaunchTiming& launch_timing();
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                           Args&&... args) {
+  LaunchTiming& t = launch_timing();
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, t.launched == 0 ? t.begin : nullptr, t.end, 0,
+                        static_cast<KArgs>(args)...);
+  if (t.begin) t.launched++;
+  return hipGetLastError();
+}
 
 // Device error flag bits (OR-ed into the workspace's status word).
 enum : int32_t {

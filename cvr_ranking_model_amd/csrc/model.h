@@ -94,7 +94,9 @@ struct cvr_model {
 namespace cvr {
 WsPlan plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P);
 
-// Brackets each kernel launch of one scoring call with a pair of HIP events when timing is armed.
+// Times each launch function of one scoring call with a pair of HIP events when timing is armed:
+// the events ride on the dispatches themselves (see launch_k); a bracket that launched nothing
+// records both events back to back.
 struct Launcher {
   cvr_model* m;
   hipStream_t s;
@@ -111,10 +113,19 @@ struct Launcher {
   hipError_t operator()(int stage, F&& fn) {
     const bool rec = slot_base >= 0 && li < kMaxLaunchesPerCall;
     const size_t slot = (size_t)slot_base + li;
-    if (rec) (void)hipEventRecord(m->timing.ev[2 * slot], s);
+    LaunchTiming& lt = launch_timing();
+    if (rec) {
+      lt.begin = m->timing.ev[2 * slot];
+      lt.end = m->timing.ev[2 * slot + 1];
+      lt.launched = 0;
+    }
     hipError_t e = fn();
     if (rec) {
-      (void)hipEventRecord(m->timing.ev[2 * slot + 1], s);
+      if (lt.launched == 0) {
+        (void)hipEventRecord(lt.begin, s);
+        (void)hipEventRecord(lt.end, s);
+      }
+      lt = LaunchTiming{};
       m->timing.stage[slot] = stage;
     }
     li++;

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void ple_gate_kernel(const PleGateParams p) {
 
 hipError_t launch_ple_gate(const PleGateParams& p, hipStream_t st) {
   if (p.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ple_gate_kernel, dim3((p.n + 3) / 4), dim3(256), 0, st, p);
+  launch_k(ple_gate_kernel, dim3((p.n + 3) / 4), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void head_out_kernel(const HeadOutParams p) {
 hipError_t launch_head_out(const HeadOutParams& p, hipStream_t st) {
   const int total = p.n * p.K;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(head_out_kernel, dim3((total + 255) / 256), dim3(256), 0, st, p);
+  launch_k(head_out_kernel, dim3((total + 255) / 256), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

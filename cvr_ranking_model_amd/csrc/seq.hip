@@ -78,10 +78,10 @@ __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restri
 
 hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
                               int2* desc, hipStream_t st) {
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, chunk_off);
+  launch_k(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, chunk_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S * R == 0) return e;
-  hipLaunchKernelGGL(chunk_desc_kernel, dim3((S * R + 255) / 256), dim3(256), 0, st, seq_offsets, R, S, n_positions,
+  launch_k(chunk_desc_kernel, dim3((S * R + 255) / 256), dim3(256), 0, st, seq_offsets, R, S, n_positions,
                      chunk_off, desc);
   return hipGetLastError();
 }
@@ -284,7 +284,7 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) 
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int blocks = max_chunks < cus ? max_chunks : cus;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(256), 0, st, p);
+  launch_k(swiglu_kernel, dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(128) void seq_pool_kernel(const float* __restrict__
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
                            int64_t n_positions, float* pool, hipStream_t st) {
   if (R * S <= 0) return hipSuccess;
-  hipLaunchKernelGGL(seq_pool_kernel, dim3(R * S), dim3(kD), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, pool);
+  launch_k(seq_pool_kernel, dim3(R * S), dim3(kD), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, pool);
   return hipGetLastError();
 }
 
