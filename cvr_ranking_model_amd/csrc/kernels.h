@@ -11,20 +11,20 @@ namespace cvr {
 // events (launch_timing), the launch carries them in its dispatch: the begin event is
 // stamped when the first kernel of the bracket starts and the end event when the last one
 // ends, so the measured time is the kernels' own, without host-side event packets in between.
-// Arguments are converted to the kernel's parameter types before they are packed.
+// Arguments are converted to the kernel's parameter types before they are packed; callers
+// read the launch status with hipGetLastError().
 struct LaunchTiming {
   hipEvent_t begin = nullptr, end = nullptr;
   int launched = 0;
 };
 LaunchTiming& launch_timing();
 template <typename... KArgs, typename... Args>
-inline hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
-                           Args&&... args) {
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                     Args&&... args) {
   LaunchTiming& t = launch_timing();
   hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, t.launched == 0 ? t.begin : nullptr, t.end, 0,
                         static_cast<KArgs>(args)...);
   if (t.begin) t.launched++;
-  return hipGetLastError();
 }
 
 // Device error flag bits (OR-ed into the workspace's status word).

@@ -14,8 +14,9 @@
 //   2. gate|up = W_gu E^T (MFMA 32x32x16, fp32 accumulate); wave w owns gate units
 //      64w..64w+63 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
 //      registers and written to LDS as bf16 (the input of the down projection);
-//   3. H = A W_down^T + b (MFMA), rounded to bf16 and stored; the rounded values are
-//      summed per column over the chunk's positions for the mean pool.
+//   3. H = A W_down^T + b (MFMA), rounded to bf16, staged through LDS and stored as whole
+//      rows; the rounded values are summed per column over the chunk's positions for the
+//      mean pool.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -94,14 +95,17 @@ constexpr int kM = kSeqChunk;  // positions per chunk = MFMA M tile
 static_assert(kM == 32, "one 32-row MFMA tile per chunk");
 
 // Persistent: block b walks a contiguous range of chunks; each wave keeps its share of the
-// sequence's weights in registers (gate/up: 2+2 column tiles x 8 k-steps; down: 1 column
-// tile x 16 k-steps) and reloads them only when the range crosses into another sequence.
-// While one chunk's MFMAs run, the next chunk's table rows are already in flight.
+// sequence's weights in registers (gate/up: 2+2 unit tiles x 8 k-steps; down: 1 column tile x
+// 16 k-steps) and reloads them only when the range crosses into another sequence.
+// Order of one iteration (chunk c): MFMAs on E(c) -> H(c) in registers; convert the rows of
+// c+1 (requested one iteration earlier) into the other E buffer; request the rows of c+2, the
+// ids of c+3 and the descriptor of c+4; stage H(c) through LDS and store it.  Loads and stores share one vector-
+// memory counter, so every wait for loads comes a whole iteration after the last stores.
 __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
   typedef bf16x8 V8;
-  __shared__ __align__(16) bf16 Es[kM * kEPitch];
-  __shared__ __align__(16) bf16 As[kM * kAPitch];
-  __shared__ __align__(16) float Bgu[2 * kHid];  // gate then up biases of the current sequence
+  __shared__ __align__(16) bf16 Es[2][kM * kEPitch];
+  __shared__ __align__(16) bf16 As[kM * kAPitch];   // SiLU(gate) * up, then the staged H tile
+  __shared__ __align__(16) float Bgu[2 * kHid];     // gate then up biases of the current sequence
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
@@ -113,9 +117,11 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
   if (c_begin >= c_end) return;
 
   // Each thread owns 4 float4 granules of the 32x128 chunk tile: granule i covers position
-  // (tid + 256 i) / 32 and columns 4 * ((tid + 256 i) % 32) .. +3, which sit in sequence
-  // column gcol[i] (fixed per thread).
-  int gcol[4], goff[4];
+  // (tid + 256 i) / 32 and columns 4 * ((tid + 256 i) % 32) .. +3, which sit in one sequence
+  // column; its table, row count and row width are fixed for the kernel.
+  const float* gtab[4];
+  int64_t grows[4];
+  int gstride[4], gcol[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int col = ((tid + i * 256) & 31) * 4;
@@ -124,7 +130,9 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
     for (int cc = 1; cc < kMaxSeqCols; ++cc)
       if (cc < p.ncols && col >= p.col_off[cc]) ci = cc;
     gcol[i] = ci;
-    goff[i] = col - p.col_off[ci];
+    gtab[i] = p.col_table[ci] + (col - p.col_off[ci]);
+    grows[i] = p.col_rows[ci];
+    gstride[i] = p.col_dim[ci];
   }
   const int gpos0 = tid >> 5;  // position of granule 0; granule i is at gpos0 + 8 i
   bool bad = false;
@@ -142,10 +150,24 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t r = id[i];
-      const bool ok = r >= 0 && (int64_t)r < p.col_rows[gcol[i]];
-      if (!ok && gpos0 + 8 * i < np) bad = true;
-      row[i] = *reinterpret_cast<const float4*>(p.col_table[gcol[i]] + (int64_t)(ok ? r : 0) * p.col_dim[gcol[i]] + goff[i]);
-      if (!ok || gpos0 + 8 * i >= np) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool live = gpos0 + 8 * i < np;
+      const bool ok = r >= 0 && (int64_t)r < grows[i];
+      if (!ok && live) bad = true;
+      row[i] = *reinterpret_cast<const float4*>(gtab[i] + (int64_t)(ok ? r : 0) * gstride[i]);
+      if (!ok || !live) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  // clamp + bf16 of a chunk's rows into E buffer b
+  auto convert = [&](const float4 (&row)[4], int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + i * 256;
+      bf16x4 o;
+      o[0] = (bf16)clamp_keep_nan(row[i].x, p.clamp);
+      o[1] = (bf16)clamp_keep_nan(row[i].y, p.clamp);
+      o[2] = (bf16)clamp_keep_nan(row[i].z, p.clamp);
+      o[3] = (bf16)clamp_keep_nan(row[i].w, p.clamp);
+      *reinterpret_cast<bf16x4*>(&Es[b][(idx >> 5) * kEPitch + (idx & 31) * 4]) = o;
     }
   };
 
@@ -172,41 +194,28 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
     cur_s = s;
   };
 
-  // Software pipeline over chunks: rows of c+1, ids of c+2 and the descriptor of c+3 are in
-  // flight while chunk c runs its MFMAs (indices past the range repeat the last chunk).
-  int2 dc = desc_of(c_begin), d1 = desc_of(c_begin + 1), d2 = desc_of(c_begin + 2);
-  int32_t id_c[4], id_1[4];
-  float4 row_c[4], row_1[4];
-  load_ids(dc, id_c);
-  load_ids(d1, id_1);
-  load_rows(dc, id_c, row_c);
+  // Prologue: E(c_begin) in buffer 0, rows of c_begin+1 and ids of c_begin+2 in flight.
+  int2 dc = desc_of(c_begin), d1 = desc_of(c_begin + 1), d2 = desc_of(c_begin + 2), d3 = desc_of(c_begin + 3);
+  int32_t ids[4];
+  float4 row[4];
+  load_ids(dc, ids);
+  load_rows(dc, ids, row);
+  load_ids(d1, ids);
+  convert(row, 0);
+  load_rows(d1, ids, row);
+  load_ids(d2, ids);
+  int buf = 0;
 #pragma unroll 1
   for (int c = c_begin; c < c_end; ++c) {
     const int seg = dc.y >> 8, np = dc.y & 255;
     const int64_t p0 = dc.x;
     const int s = seg / p.R;
     if (s != cur_s) load_weights(s);
-    // 1. clamp + bf16 of chunk c's rows into the E tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + i * 256;
-      bf16x4 o;
-      o[0] = (bf16)clamp_keep_nan(row_c[i].x, p.clamp);
-      o[1] = (bf16)clamp_keep_nan(row_c[i].y, p.clamp);
-      o[2] = (bf16)clamp_keep_nan(row_c[i].z, p.clamp);
-      o[3] = (bf16)clamp_keep_nan(row_c[i].w, p.clamp);
-      *reinterpret_cast<bf16x4*>(&Es[(idx >> 5) * kEPitch + (idx & 31) * 4]) = o;
-    }
-    __syncthreads();
-    // advance the pipeline
-    load_rows(d1, id_1, row_1);
-    int32_t id_2[4];
-    load_ids(d2, id_2);
-    const int2 d3 = desc_of(c + 3);
+    __syncthreads();  // E(c) complete; As free
 
-    // 2. gate|up for this wave's 64 hidden units, computed transposed (hidden units x
-    //    positions) so each lane ends with four consecutive hidden units of one position:
-    //    SiLU(gate) * up for them leaves as one 8-byte LDS write.
+    // gate|up for this wave's 64 hidden units, computed transposed (hidden units x
+    // positions) so each lane ends with four consecutive hidden units of one position:
+    // SiLU(gate) * up for them leaves as one 8-byte LDS write.
     {
       f32x16 acc[4];
 #pragma unroll
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
         for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 #pragma unroll
       for (int k = 0; k < kD / 16; ++k) {
-        const V8 e = *reinterpret_cast<const V8*>(&Es[lr * kEPitch + k * 16 + lk]);
+        const V8 e = *reinterpret_cast<const V8*>(&Es[buf][lr * kEPitch + k * 16 + lk]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = Lowp<bf16>::mfma32(wg[j][k], e, acc[j]);
       }
@@ -242,8 +251,8 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
     }
     __syncthreads();
 
-    // 3. down projection -> H (bf16) and column sums for the mean pool; even and odd k steps
-    //    accumulate separately so consecutive MFMAs do not wait on each other
+    // down projection -> H (fp32 accumulators); even and odd k steps accumulate separately
+    // so consecutive MFMAs do not wait on each other
     f32x16 acc2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -254,27 +263,38 @@ __global__ __launch_bounds__(256, 1) void swiglu_kernel(const SwigluParams p) {
       const V8 a = *reinterpret_cast<const V8*>(&As[lr * kAPitch + k * 16 + lk]);
       acc2[k & 1] = Lowp<bf16>::mfma32(a, wd[k], acc2[k & 1]);
     }
+
+    // next chunk's E; then the gathers two and three chunks ahead go out before any store
+    convert(row, buf ^ 1);
+    load_rows(d2, ids, row);
+    load_ids(d3, ids);
+    const int2 d4 = desc_of(c + 4);  // used next iteration, so its load latency stays hidden
+
+    // H(c): round to bf16, column sums for the mean pool, stage rows in As, 16-byte stores
+    __syncthreads();  // every wave is done reading As
     const int n = wave * 32 + lr;
     float colsum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (m < np) {
-        const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
-        p.H[(p0 + m) * kD + n] = h;
-        colsum += (float)h;
-      }
+      const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
+      As[m * kAPitch + n] = h;
+      if (m < np) colsum += (float)h;
     }
     colsum += __shfl_xor(colsum, 32);
     if (lane < 32) p.part[(int64_t)c * kD + n] = colsum;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (tid >> 4) + 16 * i, ch = tid & 15;
+      if (r < np)
+        *reinterpret_cast<V8*>(p.H + (p0 + r) * kD + ch * 8) = *reinterpret_cast<const V8*>(&As[r * kAPitch + ch * 8]);
+    }
     dc = d1;
     d1 = d2;
     d2 = d3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      row_c[i] = row_1[i];
-      id_1[i] = id_2[i];
-    }
+    d3 = d4;
+    buf ^= 1;
   }
   if (bad) raise_flag(p.flag, ERRF_SEQ_ID_RANGE);
 }
