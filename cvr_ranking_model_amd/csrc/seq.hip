@@ -9,12 +9,12 @@
 // (sequence, request) segment into the next, so the per-chunk column sums of the encoded
 // states reduce to each segment's mean pool in a fixed order (bitwise reproducible).
 //
-// swiglu_kernel, per chunk of 32 positions (8 waves):
+// swiglu_kernel, per chunk of 32 positions (4 producer + 4 consumer waves):
 //   1. gather: each position's 4 rows (fp32) -> clamp -> bf16 -> LDS tile E [32][128];
-//   2. gate|up = W_gu E^T (MFMA 32x32x16, fp32 accumulate); wave w owns gate units
-//      32w..32w+31 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
+//   2. gate|up = W_gu E^T (MFMA 32x32x16, fp32 accumulate); producer w owns gate units
+//      64w..64w+63 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
 //      registers and written to LDS as bf16 (the input of the down projection);
-//   3. H = A W_down^T + b (MFMA 16x16x32), rounded to bf16, staged through LDS and stored as whole
+//   3. H = A W_down^T + b (MFMA 32x32x16), rounded to bf16, staged through LDS and stored as
 //      rows; the rounded values are summed per column over the chunk's positions for the
 //      mean pool.
 #include "device_common.h"
@@ -91,52 +91,139 @@ constexpr int kD = 128;        // token width
 constexpr int kHid = 256;      // SwiGLU hidden width
 constexpr int kEPitch = kD + 8;
 constexpr int kAPitch = kHid + 8;
+constexpr int kHPitch = 40;    // per-wave H staging: 32 columns + 8
 constexpr int kM = kSeqChunk;  // positions per chunk = MFMA M tile
-constexpr int kSwWaves = 8;    // two waves per SIMD
 static_assert(kM == 32, "one 32-row MFMA tile per chunk");
 
-// 16x16x32 bf16 MFMA: lane l holds A[l%16][8(l/16)..+7] and B[8(l/16)..+7][l%16] and gets
-// D[4(l/16)+v][l%16], v = 0..3.
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Persistent: block b walks a contiguous range of chunks with 8 waves (two per SIMD, so one
-// wave's VALU work and waits overlap the other's matrix instructions).  Each wave keeps its
-// share of the sequence's weights in registers and reloads them only when the range crosses
-// into another sequence: 32 gate + 32 up hidden units (gate|up as 2 MFMA 32x32x16 tiles x 8
-// k-steps) and 16 output columns of the down projection (MFMA 16x16x32 over 2 position tiles
-// x 8 k-steps).
-// Order of one iteration (chunk c): MFMAs on E(c) -> H(c) in registers; convert the rows of
-// c+1 (requested one iteration earlier) into the other E buffer; request the rows of c+2, the
-// ids of c+3 and the descriptor of c+4; stage H(c) through LDS and store it.  Loads and
-// stores share one vector-memory counter, so every wait for loads comes a whole iteration
-// after the last stores.
-__global__ __launch_bounds__(kSwWaves * 64, 1) void swiglu_kernel(const SwigluParams p) {
+// Persistent, producer/consumer: block b walks a contiguous range of n chunks with 8 waves.
+// Waves 0-3 (producers) hold the gate|up weights of 64 hidden units each and turn E(c) into
+// SiLU(gate) * up; they also write out the finished H rows and pool partials of chunk c-2.
+// Waves 4-7 (consumers) hold the down projection for 32 output columns each, turn chunk c-1
+// into bf16 H (staged in LDS) and pool partials, and gather and convert rows two chunks ahead.
+// Every SIMD runs one wave of each kind, so one's VALU work overlaps the other's matrix
+// instructions.  E, the SiLU tile, the H staging and the chunk descriptors are double-
+// buffered in LDS; one block barrier per iteration hands them over.
+// Loads and stores share one vector-memory counter: consumers only load (their waits count
+// loads alone, so rows two chunks ahead stay in flight) and producers only store (they take no
+// chunk data from global memory: descriptors come through LDS).
+// Both roles pass the same n + 3 block barriers: one after the consumers' prologue and one at
+// the end of each of the n + 2 pipeline iterations.
+__global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   typedef bf16x8 V8;
-  constexpr int NT = kSwWaves * 64;
-  constexpr int NG = kM * kD / 4 / NT;  // float4 granules per thread per chunk
   __shared__ __align__(16) bf16 Es[2][kM * kEPitch];
-  __shared__ __align__(16) bf16 As[kM * kAPitch];   // SiLU(gate) * up, then the staged H tile
-  __shared__ __align__(16) float Bgu[2 * kHid];     // gate then up biases of the current sequence
+  __shared__ __align__(16) bf16 As[2][kM * kAPitch];
+  __shared__ __align__(16) float Bs[4][3 * 64];          // producer w: gate bias, up bias, -log2(e) * gate bias
+  __shared__ __align__(16) bf16 Hs[2][kM * kEPitch];     // finished H tile of a chunk
+  __shared__ __align__(16) float Cs[2][kD];              // its pool partials
+  __shared__ int2 Ds[2];                                  // descriptor of the producers' next chunk
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool producer = wave < 4;
+  const int rw = wave & 3;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
-  const int l16 = lane & 15, lq = lane >> 4;
   const int SR = p.S * p.R;
   const int total = p.chunk_off[SR];
   const int per = (total + gridDim.x - 1) / gridDim.x;
   const int c_begin = blockIdx.x * per;
   const int c_end = c_begin + per < total ? c_begin + per : total;
-  if (c_begin >= c_end) return;
+  const int n = c_end - c_begin;
+  if (n <= 0) return;
+  auto desc_of = [&](int i) { return p.desc[c_begin + (i < n ? i : n - 1)]; };
 
-  // Granule i of a thread covers position (tid + NT i) / 32 and columns 4 * (tid % 32) .. +3,
-  // which sit in one sequence column; its table, row count and row width are fixed.
+  if (producer) {
+    V8 wg[4][kD / 16];  // gate tiles 0,1 and up tiles 2,3: units 64w + 32(j%2) + lane%32
+    float* bs = Bs[rw];
+    int cur_s = -1;
+    int2 dm1 = make_int2(0, 0), dm2 = make_int2(0, 0);  // descriptors of chunks i-1, i-2
+    __syncthreads();  // E(0) and Ds[0] are in place
+#pragma unroll 1
+    for (int i = 0; i <= n + 1; ++i) {
+      int2 d = make_int2(0, 0);
+      if (i < n) {
+        d = Ds[i & 1];
+        const int s = (d.y >> 8) / p.R;
+        if (s != cur_s) {
+          const bf16* Wgu = p.Wgu + (int64_t)s * p.wgu_gstride;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int u = (j < 2 ? 0 : kHid) + rw * 64 + (j & 1) * 32 + lr;
+#pragma unroll
+            for (int k = 0; k < kD / 16; ++k) wg[j][k] = *reinterpret_cast<const V8*>(Wgu + (int64_t)u * kD + k * 16 + lk);
+          }
+          const float* bgu = p.bgu + (int64_t)s * p.bgu_gstride + rw * 64 + lane;
+          const float bg = bgu[0], bu = bgu[kHid];
+          bs[lane] = bg;
+          bs[64 + lane] = bu;
+          bs[128 + lane] = -1.4426950408889634f * bg;
+          cur_s = s;
+        }
+        const int b = i & 1;
+        f32x16 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+        for (int k = 0; k < kD / 16; ++k) {
+          const V8 e = *reinterpret_cast<const V8*>(&Es[b][lr * kEPitch + k * 16 + lk]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = Lowp<bf16>::mfma32(wg[j][k], e, acc[j]);
+        }
+        // The tiles are hidden units x positions: lane holds units 8*v4 + 4*(lane/32) .. +3 of
+        // each tile for position lane%32, so SiLU(gate) * up of 4 units leaves as 8 bytes.
+        // exp(-g) = exp2(-log2(e) * acc - log2(e) * b_gate): the bias folds into one FMA.
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int h = j * 32 + 8 * v4 + 4 * (lane >> 5);
+            const float4 bg4 = *reinterpret_cast<const float4*>(&bs[h]);
+            const float4 bu4 = *reinterpret_cast<const float4*>(&bs[64 + h]);
+            const float4 cg4 = *reinterpret_cast<const float4*>(&bs[128 + h]);
+            const float bgv[4] = {bg4.x, bg4.y, bg4.z, bg4.w};
+            const float buv[4] = {bu4.x, bu4.y, bu4.z, bu4.w};
+            const float cgv[4] = {cg4.x, cg4.y, cg4.z, cg4.w};
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float ag = acc[j][4 * v4 + q], au = acc[j + 2][4 * v4 + q];
+              const float e2 = __builtin_amdgcn_exp2f(fmaf(ag, -1.4426950408889634f, cgv[q]));
+              const float r = __builtin_amdgcn_rcpf(1.0f + e2);
+              o[q] = (bf16)(((ag + bgv[q]) * (au + buv[q])) * r);
+            }
+            *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + h]) = o;
+          }
+      }
+      if (i >= 2) {
+        // chunk i-2 out: 32 rows x 128 columns of H (16 bytes per thread, twice) and partials
+        const int c = c_begin + i - 2;
+        const int np = dm2.y & 255;
+        const bf16* hsrc = Hs[i & 1];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r = (tid >> 4) + 16 * q, ch = tid & 15;
+          if (r < np)
+            *reinterpret_cast<V8*>(p.H + ((int64_t)dm2.x + r) * kD + ch * 8) =
+                *reinterpret_cast<const V8*>(&hsrc[r * kEPitch + ch * 8]);
+        }
+        if (tid < kD) p.part[(int64_t)c * kD + tid] = Cs[i & 1][tid];
+      }
+      dm2 = dm1;
+      dm1 = d;
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- consumers
+  const int bt = tid - 256;  // 0..255
+  // Granule i of a consumer thread covers position (bt + 256 i) / 32 and columns
+  // 4 * (bt % 32) .. +3, which sit in one sequence column (table, rows and width fixed).
   const float* gtab;
   int64_t grows;
   int gstride, gcol;
   {
-    const int col = (tid & 31) * 4;
+    const int col = (bt & 31) * 4;
     int ci = 0;
 #pragma unroll
     for (int cc = 1; cc < kMaxSeqCols; ++cc)
@@ -146,34 +233,32 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void swiglu_kernel(const SwigluPa
     grows = p.col_rows[ci];
     gstride = p.col_dim[ci];
   }
-  const int gpos0 = tid >> 5;  // position of granule 0; granule i is at gpos0 + (NT/32) i
+  const int gpos0 = bt >> 5;  // granule i is at position gpos0 + 8 i
   bool bad = false;
-  auto desc_of = [&](int c) { return p.desc[c < c_end ? c : c_end - 1]; };
-  auto load_ids = [&](int2 d, int32_t (&id)[NG]) {
+  auto load_ids = [&](int2 d, int32_t (&id)[4]) {
     const int np = d.y & 255;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int pos = gpos0 + (NT / 32) * i;
+    for (int i = 0; i < 4; ++i) {
+      const int pos = gpos0 + 8 * i;
       id[i] = p.seq_ids[((int64_t)d.x + (pos < np ? pos : 0)) * p.ncols + gcol];
     }
   };
-  auto load_rows = [&](int2 d, const int32_t (&id)[NG], float4 (&row)[NG]) {
+  auto load_rows = [&](int2 d, const int32_t (&id)[4], float4 (&row)[4]) {
     const int np = d.y & 255;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int32_t r = id[i];
-      const bool live = gpos0 + (NT / 32) * i < np;
+      const bool live = gpos0 + 8 * i < np;
       const bool ok = r >= 0 && (int64_t)r < grows;
       if (!ok && live) bad = true;
       row[i] = *reinterpret_cast<const float4*>(gtab + (int64_t)(ok ? r : 0) * gstride);
       if (!ok || !live) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  // clamp + bf16 of a chunk's rows into E buffer b
-  auto convert = [&](const float4 (&row)[NG], int b) {
+  auto convert = [&](const float4 (&row)[4], int b) {
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int idx = tid + i * NT;
+    for (int i = 0; i < 4; ++i) {
+      const int idx = bt + i * 256;
       bf16x4 o;
       o[0] = (bf16)clamp_keep_nan(row[i].x, p.clamp);
       o[1] = (bf16)clamp_keep_nan(row[i].y, p.clamp);
@@ -183,133 +268,84 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void swiglu_kernel(const SwigluPa
     }
   };
 
-  V8 wg[2][kD / 16];   // gate tile (units 32w..32w+31) and the matching up tile
-  V8 wd[kHid / 32];    // down projection: output column 16w + lane%16, k = 32 ks + 8 (lane/16)
+  V8 wd[kHid / 16];  // down projection: output column 32w + lane%32
   float bd = 0.f;
   int cur_s = -1;
-  auto load_weights = [&](int s) {
-    const bf16* Wgu = p.Wgu + (int64_t)s * p.wgu_gstride;
-    const float* bgu = p.bgu + (int64_t)s * p.bgu_gstride;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = j * kHid + wave * 32 + lr;
-#pragma unroll
-      for (int k = 0; k < kD / 16; ++k) wg[j][k] = *reinterpret_cast<const V8*>(Wgu + (int64_t)n * kD + k * 16 + lk);
-    }
-    __syncthreads();  // no wave still reads the previous sequence's biases
-    for (int h = tid; h < 2 * kHid; h += NT) Bgu[h] = bgu[h];
-    const bf16* Wd = p.Wd + (int64_t)s * p.wd_gstride;
-    const int n = wave * 16 + l16;
-#pragma unroll
-    for (int ks = 0; ks < kHid / 32; ++ks) wd[ks] = *reinterpret_cast<const V8*>(Wd + (int64_t)n * kHid + ks * 32 + lq * 8);
-    bd = (p.bd + (int64_t)s * p.bd_gstride)[n];
-    cur_s = s;
-  };
+  const int ncol = rw * 32 + lr;
 
-  // Prologue: E(c_begin) in buffer 0, rows of c_begin+1 and ids of c_begin+2 in flight.
-  int2 dc = desc_of(c_begin), d1 = desc_of(c_begin + 1), d2 = desc_of(c_begin + 2), d3 = desc_of(c_begin + 3);
-  int32_t ids[NG];
-  float4 row[NG];
-  load_ids(dc, ids);
-  load_rows(dc, ids, row);
+  // Descriptors of chunks i-1 .. i+4 (relative to the iteration), loaded ahead; rows of i+1 and
+  // i+2 and ids of i+3 in flight at the start of iteration i.
+  int2 dprev = desc_of(0), d0 = desc_of(0), d1 = desc_of(1), d2 = desc_of(2), d3 = desc_of(3), d4 = desc_of(4);
+  int32_t ids[4];
+  float4 rowA[4], rowB[4];
+  load_ids(d0, ids);
+  load_rows(d0, ids, rowA);
   load_ids(d1, ids);
-  convert(row, 0);
-  load_rows(d1, ids, row);
+  convert(rowA, 0);
+  load_rows(d1, ids, rowA);
   load_ids(d2, ids);
-  int buf = 0;
-#pragma unroll 1
-  for (int c = c_begin; c < c_end; ++c) {
-    const int seg = dc.y >> 8, np = dc.y & 255;
-    const int64_t p0 = dc.x;
-    const int s = seg / p.R;
-    if (s != cur_s) load_weights(s);
-    __syncthreads();  // E(c) complete; As free
+  load_rows(d2, ids, rowB);
+  load_ids(d3, ids);
+  if (bt == 0) Ds[0] = d0;
+  __syncthreads();  // E(0) and Ds[0] complete (pairs with the producers' first wait)
 
-    // gate|up for this wave's 32 hidden units, computed transposed (hidden units x
-    // positions) so each lane ends with four consecutive hidden units of one position:
-    // SiLU(gate) * up for them leaves as one 8-byte LDS write.
-    {
-      f32x16 acc[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-#pragma unroll
-      for (int k = 0; k < kD / 16; ++k) {
-        const V8 e = *reinterpret_cast<const V8*>(&Es[buf][lr * kEPitch + k * 16 + lk]);
-        acc[0] = Lowp<bf16>::mfma32(wg[0][k], e, acc[0]);
-        acc[1] = Lowp<bf16>::mfma32(wg[1][k], e, acc[1]);
-      }
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        // rows 8*v4 + 4*(lane/32) .. +3 of the tile are hidden units; column lr is the position
-        const int h0 = wave * 32 + 8 * v4 + 4 * (lane >> 5);
-        const float4 bg4 = *reinterpret_cast<const float4*>(&Bgu[h0]);
-        const float4 bu4 = *reinterpret_cast<const float4*>(&Bgu[kHid + h0]);
-        const float bgv[4] = {bg4.x, bg4.y, bg4.z, bg4.w};
-        const float buv[4] = {bu4.x, bu4.y, bu4.z, bu4.w};
-        bf16x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float g = acc[0][4 * v4 + q] + bgv[q];
-          const float u = acc[1][4 * v4 + q] + buv[q];
-          const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-          o[q] = (bf16)(sg * u);
-        }
-        *reinterpret_cast<bf16x4*>(&As[lr * kAPitch + h0]) = o;
-      }
+  // One pipeline iteration; `cur` holds the rows of chunk i+1 and is refilled with i+3.
+  auto step = [&](int i, float4 (&cur)[4]) {
+    int2 d5 = d4;
+    if (i + 1 < n) {
+      convert(cur, (i + 1) & 1);
+      load_rows(d3, ids, cur);
+      load_ids(d4, ids);
+      d5 = desc_of(i + 5);
+      if (bt == 0) Ds[(i + 1) & 1] = d1;
     }
-    __syncthreads();
-
-    // down projection for output columns 16w .. 16w+15: two 16-position tiles
-    f32x4 acc2[2];
+    if (i >= 1 && i <= n) {
+      // chunk i-1: down projection on the SiLU tile, bf16 H staged for the producers
+      const int np = dprev.y & 255;
+      const int s = (dprev.y >> 8) / p.R;
+      if (s != cur_s) {
+        const bf16* Wd = p.Wd + (int64_t)s * p.wd_gstride;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc2[t][v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < kHid / 32; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const V8 a = *reinterpret_cast<const V8*>(&As[(16 * t + l16) * kAPitch + ks * 32 + lq * 8]);
-        acc2[t] = mfma16(a, wd[ks], acc2[t]);
+        for (int k = 0; k < kHid / 16; ++k) wd[k] = *reinterpret_cast<const V8*>(Wd + (int64_t)ncol * kHid + k * 16 + lk);
+        bd = (p.bd + (int64_t)s * p.bd_gstride)[ncol];
+        cur_s = s;
       }
-    }
-
-    // next chunk's E; then the gathers two and three chunks ahead go out before any store
-    convert(row, buf ^ 1);
-    load_rows(d2, ids, row);
-    load_ids(d3, ids);
-    const int2 d4 = desc_of(c + 4);  // used next iteration, so its load latency stays hidden
-
-    // H(c): round to bf16, column sums for the mean pool, stage rows in As, 16-byte stores.
-    // Lane holds rows 16t + 4(lane/16) + v of column 16w + lane%16.
-    __syncthreads();  // every wave is done reading As
-    const int n = wave * 16 + l16;
-    float colsum = 0.f;
+      const bf16* A = As[(i - 1) & 1];
+      f32x16 acc2[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 16 * t + 4 * lq + v;
-        const bf16 h = (bf16)(acc2[t][v] + bd);
-        As[m * kAPitch + n] = h;
+        for (int v = 0; v < 16; ++v) acc2[h][v] = 0.f;
+#pragma unroll
+      for (int k = 0; k < kHid / 16; ++k) {
+        const V8 a = *reinterpret_cast<const V8*>(&A[lr * kAPitch + k * 16 + lk]);
+        acc2[k & 1] = Lowp<bf16>::mfma32(a, wd[k], acc2[k & 1]);
+      }
+      // lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column ncol
+      bf16* hdst = Hs[(i - 1) & 1];
+      float colsum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
+        hdst[m * kEPitch + ncol] = h;
         if (m < np) colsum += (float)h;
       }
-    colsum += __shfl_xor(colsum, 16);
-    colsum += __shfl_xor(colsum, 32);
-    if (lane < 16) p.part[(int64_t)c * kD + n] = colsum;
-    __syncthreads();
-    {
-      const int r = tid >> 4, ch = tid & 15;
-      if (r < np)
-        *reinterpret_cast<V8*>(p.H + (p0 + r) * kD + ch * 8) = *reinterpret_cast<const V8*>(&As[r * kAPitch + ch * 8]);
+      colsum += __shfl_xor(colsum, 32);
+      if (lane < 32) Cs[(i - 1) & 1][ncol] = colsum;
     }
-    dc = d1;
+    dprev = d0;
+    d0 = d1;
     d1 = d2;
     d2 = d3;
     d3 = d4;
-    buf ^= 1;
+    d4 = d5;
+    __syncthreads();
+  };
+#pragma unroll 1
+  for (int i = 0; i <= n + 1; i += 2) {
+    step(i, rowA);
+    if (i + 1 <= n + 1) step(i + 1, rowB);
   }
   if (bad) raise_flag(p.flag, ERRF_SEQ_ID_RANGE);
 }
@@ -319,7 +355,7 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) 
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int blocks = max_chunks < cus ? max_chunks : cus;
-  launch_k(swiglu_kernel, dim3(blocks), dim3(kSwWaves * 64), 0, st, p);
+  launch_k(swiglu_kernel, dim3(blocks), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
