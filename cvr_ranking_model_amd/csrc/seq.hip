@@ -91,7 +91,6 @@ constexpr int kD = 128;        // token width
 constexpr int kHid = 256;      // SwiGLU hidden width
 constexpr int kEPitch = kD + 8;
 constexpr int kAPitch = kHid + 8;
-constexpr int kHPitch = 40;    // per-wave H staging: 32 columns + 8
 constexpr int kM = kSeqChunk;  // positions per chunk = MFMA M tile
 static_assert(kM == 32, "one 32-row MFMA tile per chunk");
 
@@ -135,6 +134,20 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
     float* bs = Bs[rw];
     int cur_s = -1;
     int2 dm1 = make_int2(0, 0), dm2 = make_int2(0, 0);  // descriptors of chunks i-1, i-2
+    // chunk i-2 out: 32 rows x 128 columns of H (16 bytes per thread, twice) and partials
+    auto store_out = [&](int i) {
+      const int c = c_begin + i - 2;
+      const int np = dm2.y & 255;
+      const bf16* hsrc = Hs[i & 1];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = (tid >> 4) + 16 * q, ch = tid & 15;
+        if (r < np)
+          *reinterpret_cast<V8*>(p.H + ((int64_t)dm2.x + r) * kD + ch * 8) =
+              *reinterpret_cast<const V8*>(&hsrc[r * kEPitch + ch * 8]);
+      }
+      if (tid < kD) p.part[(int64_t)c * kD + tid] = Cs[i & 1][tid];
+    };
     __syncthreads();  // E(0) and Ds[0] are in place
 #pragma unroll 1
     for (int i = 0; i <= n + 1; ++i) {
@@ -194,20 +207,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
             *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + h]) = o;
           }
       }
-      if (i >= 2) {
-        // chunk i-2 out: 32 rows x 128 columns of H (16 bytes per thread, twice) and partials
-        const int c = c_begin + i - 2;
-        const int np = dm2.y & 255;
-        const bf16* hsrc = Hs[i & 1];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int r = (tid >> 4) + 16 * q, ch = tid & 15;
-          if (r < np)
-            *reinterpret_cast<V8*>(p.H + ((int64_t)dm2.x + r) * kD + ch * 8) =
-                *reinterpret_cast<const V8*>(&hsrc[r * kEPitch + ch * 8]);
-        }
-        if (tid < kD) p.part[(int64_t)c * kD + tid] = Cs[i & 1][tid];
-      }
+      if (i >= 2) store_out(i);
       dm2 = dm1;
       dm1 = d;
       __syncthreads();
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   // Granule i of a consumer thread covers position (bt + 256 i) / 32 and columns
   // 4 * (bt % 32) .. +3, which sit in one sequence column (table, rows and width fixed).
   const float* gtab;
-  int64_t grows;
+  uint32_t grows;
   int gstride, gcol;
   {
     const int col = (bt & 31) * 4;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       if (cc < p.ncols && col >= p.col_off[cc]) ci = cc;
     gcol = ci;
     gtab = p.col_table[ci] + (col - p.col_off[ci]);
-    grows = p.col_rows[ci];
+    grows = p.col_rows[ci] > 0x7fffffff ? 0x7fffffffu : (uint32_t)p.col_rows[ci];  // ids are int32
     gstride = p.col_dim[ci];
   }
   const int gpos0 = bt >> 5;  // granule i is at position gpos0 + 8 i
@@ -243,27 +243,33 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       id[i] = p.seq_ids[((int64_t)d.x + (pos < np ? pos : 0)) * p.ncols + gcol];
     }
   };
+  // Rows of positions past the chunk's length are loaded but never used: row m of H depends on
+  // row m of E alone and such rows are neither stored nor summed.  An out-of-range id raises
+  // the error flag and reads row 0 instead.
   auto load_rows = [&](int2 d, const int32_t (&id)[4], float4 (&row)[4]) {
     const int np = d.y & 255;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int32_t r = id[i];
-      const bool live = gpos0 + 8 * i < np;
-      const bool ok = r >= 0 && (int64_t)r < grows;
-      if (!ok && live) bad = true;
-      row[i] = *reinterpret_cast<const float4*>(gtab + (int64_t)(ok ? r : 0) * gstride);
-      if (!ok || !live) row[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t r = (uint32_t)id[i];
+      const bool ok = r < grows;
+      if (!ok && gpos0 + 8 * i < np) bad = true;
+      row[i] = *reinterpret_cast<const float4*>(gtab + (ok ? r : 0u) * (uint64_t)gstride);
     }
+  };
+  // clamp to [-c, c] keeping NaN, as one median-of-three and a NaN select
+  auto clampv = [&](float x) {
+    const float m = __builtin_amdgcn_fmed3f(x, -p.clamp, p.clamp);
+    return x != x ? x : m;
   };
   auto convert = [&](const float4 (&row)[4], int b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = bt + i * 256;
       bf16x4 o;
-      o[0] = (bf16)clamp_keep_nan(row[i].x, p.clamp);
-      o[1] = (bf16)clamp_keep_nan(row[i].y, p.clamp);
-      o[2] = (bf16)clamp_keep_nan(row[i].z, p.clamp);
-      o[3] = (bf16)clamp_keep_nan(row[i].w, p.clamp);
+      o[0] = (bf16)clampv(row[i].x);
+      o[1] = (bf16)clampv(row[i].y);
+      o[2] = (bf16)clampv(row[i].z);
+      o[3] = (bf16)clampv(row[i].w);
       *reinterpret_cast<bf16x4*>(&Es[b][(idx >> 5) * kEPitch + (idx & 31) * 4]) = o;
     }
   };
@@ -291,6 +297,8 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
 
   // One pipeline iteration; `cur` holds the rows of chunk i+1 and is refilled with i+3.
   auto step = [&](int i, float4 (&cur)[4]) {
+    // E(i+1) and the gathers further ahead first: VALU work while the producer on this SIMD
+    // runs its gate|up matrix instructions
     int2 d5 = d4;
     if (i + 1 < n) {
       convert(cur, (i + 1) & 1);
@@ -299,9 +307,10 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       d5 = desc_of(i + 5);
       if (bt == 0) Ds[(i + 1) & 1] = d1;
     }
-    if (i >= 1 && i <= n) {
-      // chunk i-1: down projection on the SiLU tile, bf16 H staged for the producers
-      const int np = dprev.y & 255;
+    const bool down = i >= 1 && i <= n;
+    f32x16 acc2[2];
+    if (down) {
+      // chunk i-1: down projection on the SiLU tile, while the producer runs its SiLU
       const int s = (dprev.y >> 8) / p.R;
       if (s != cur_s) {
         const bf16* Wd = p.Wd + (int64_t)s * p.wd_gstride;
@@ -311,7 +320,6 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         cur_s = s;
       }
       const bf16* A = As[(i - 1) & 1];
-      f32x16 acc2[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -321,15 +329,28 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         const V8 a = *reinterpret_cast<const V8*>(&A[lr * kAPitch + k * 16 + lk]);
         acc2[k & 1] = Lowp<bf16>::mfma32(a, wd[k], acc2[k & 1]);
       }
-      // lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of column ncol
+    }
+    if (down) {
+      // bf16 H staged for the producers; lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of ncol
+      const int np = dprev.y & 255;
       bf16* hdst = Hs[(i - 1) & 1];
       float colsum = 0.f;
+      if (np == kM) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
-        hdst[m * kEPitch + ncol] = h;
-        if (m < np) colsum += (float)h;
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
+          hdst[m * kEPitch + ncol] = h;
+          colsum += (float)h;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
+          hdst[m * kEPitch + ncol] = h;
+          if (m < np) colsum += (float)h;
+        }
       }
       colsum += __shfl_xor(colsum, 32);
       if (lane < 32) Cs[(i - 1) & 1][ncol] = colsum;
