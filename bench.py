@@ -140,6 +140,9 @@ def main():
     ap.add_argument("--variant", default="bench")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time graph replays (cvr_score_graph); per-stage rooflines then come from an eager pass "
+                         "of the same steps that follows")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 256 MiB fp32 copy kernel (torch.neg) so a "
                          "hardware-counter run can scale its byte counters against a known size")
@@ -168,6 +171,17 @@ def main():
     for _ in range(args.warmup):
         model.score(db, out)
     assert model.sync_status() == cv.CVR_OK
+    graph_dt = None
+    if args.graph:
+        for _ in range(max(1, args.warmup)):
+            model.score_graph(db, out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            model.score_graph(db, out)
+        torch.cuda.synchronize()
+        graph_dt = time.perf_counter() - t0
+        assert model.sync_status() == cv.CVR_OK
     model.timing_begin(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -177,6 +191,9 @@ def main():
     dt = time.perf_counter() - t0
     stages, calls = model.timing_end()
     assert model.sync_status() == cv.CVR_OK
+    eager_dt = dt
+    if graph_dt is not None:
+        dt = graph_dt
     if args.calibrate_copy:
         # reads 256 MiB and writes 256 MiB once each: the reference for FETCH_SIZE / WRITE_SIZE
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
@@ -238,7 +255,11 @@ def main():
         "roofline": roof,
         "stages": table,
         "ids": "uniform" if args.uniform_ids else "zipf",
+        "launch": "graph replay" if args.graph else "eager",
     }
+    if args.graph:
+        line["eager_ms_per_step"] = round(eager_dt * 1e3 / args.steps, 4)
+        line["roofline_pass"] = "eager steps timed right after the graph replays (per-kernel events)"
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.variant, weights)

@@ -504,6 +504,73 @@ extern "C" cvr_status cvr_score(cvr_handle h, const cvr_batch* b, void* workspac
   return CVR_OK;
 }
 
+// ------------------------------------------------------------------ graph replay
+void GraphCache::reset() {
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  exec = nullptr;
+  graph = nullptr;
+  valid = false;
+}
+
+static bool same_key(const GraphCache& g, const cvr_batch* b, void* ws, size_t ws_bytes, float* out, hipStream_t s,
+                     int debug) {
+  return g.valid && g.ws == ws && g.ws_bytes == ws_bytes && g.out == out && g.stream == s && g.debug == debug &&
+         g.batch.n_requests == b->n_requests && g.batch.n_candidates == b->n_candidates && g.batch.n_ids == b->n_ids &&
+         g.batch.n_positions == b->n_positions && g.batch.cand_offsets == b->cand_offsets &&
+         g.batch.bag_offsets == b->bag_offsets && g.batch.ids == b->ids && g.batch.seq_offsets == b->seq_offsets &&
+         g.batch.seq_ids == b->seq_ids;
+}
+
+extern "C" cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes,
+                                      float* out_scores, void* hip_stream) {
+  if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
+  if (!hip_stream) return fail(h, CVR_ERR_ARG, "graph replay needs a created stream (the null stream cannot be captured)");
+  WsPlan plan;
+  cvr_status st = check_batch(h, b, workspace, ws_bytes, out_scores, plan);
+  if (st != CVR_OK) return st;
+  if (h->spec.model == CVR_MODEL_DLRM && h->spec.n_hidden == 0) return fail(h, CVR_ERR_UNSUPPORTED, "DLRM without hidden layers");
+  hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  GraphCache& g = h->graph;
+  if (!same_key(g, b, workspace, ws_bytes, out_scores, s, h->debug)) {
+    g.reset();
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("begin capture: ") + hipGetErrorString(e));
+    Launcher L(h, s, false);
+    e = run_front(h, b, ws, plan, L, s);
+    if (e == hipSuccess && b->n_candidates > 0) {
+      if (h->spec.model == CVR_MODEL_DLRM) e = run_dlrm(h, b, ws, plan, out_scores, L, s);
+      else e = run_hyformer(h, b, ws, plan, out_scores, L, s);
+    }
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(s, &graph);
+    if (e == hipSuccess) e = ec;
+    if (e == hipSuccess) e = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+    g.graph = graph;
+    if (e != hipSuccess) {
+      g.reset();
+      return fail(h, CVR_ERR_HIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    }
+    g.valid = true;
+    g.batch = *b;
+    g.ws = workspace;
+    g.ws_bytes = ws_bytes;
+    g.out = out_scores;
+    g.stream = s;
+    g.debug = h->debug;
+  }
+  const hipError_t e = hipGraphLaunch(g.exec, s);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
+  h->last_ws = ws;
+  h->last_plan = plan;
+  h->last_R = b->n_requests;
+  h->last_n = b->n_candidates;
+  h->last_P = b->n_positions;
+  h->last_debug = h->debug;
+  return CVR_OK;
+}
+
 extern "C" cvr_status cvr_sync_status(cvr_handle h, void* hip_stream) {
   if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
   hipStream_t s = (hipStream_t)hip_stream;
@@ -601,5 +668,6 @@ extern "C" const char* cvr_status_string(cvr_status s) {
 extern "C" void cvr_destroy(cvr_handle h) {
   if (!h) return;
   h->timing.reset();
+  h->graph.reset();
   delete h;
 }

@@ -54,6 +54,20 @@ struct WsPlan {
   size_t total = 0;
 };
 
+// One captured scoring call: replayed while every launch parameter it baked in is unchanged.
+struct GraphCache {
+  bool valid = false;
+  cvr_batch batch{};
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* out = nullptr;
+  hipStream_t stream = nullptr;
+  int debug = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  void reset();
+};
+
 struct Timing {
   bool armed = false;
   int max_calls = 0;
@@ -89,6 +103,7 @@ struct cvr_model {
   int64_t last_R = 0, last_n = 0, last_P = 0;
   int last_debug = 0, last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0;
   cvr::Timing timing;
+  cvr::GraphCache graph;
 };
 
 namespace cvr {
@@ -102,9 +117,9 @@ struct Launcher {
   hipStream_t s;
   int slot_base = -1;
   int li = 0;
-  Launcher(cvr_model* mm, hipStream_t ss) : m(mm), s(ss) {
+  Launcher(cvr_model* mm, hipStream_t ss, bool timed = true) : m(mm), s(ss) {
     Timing& t = m->timing;
-    if (t.armed && t.calls < t.max_calls) {
+    if (timed && t.armed && t.calls < t.max_calls) {
       slot_base = t.calls * kMaxLaunchesPerCall;
       t.calls++;
     }

@@ -62,6 +62,7 @@ _PROTOS = {
                              C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]),
     "cvr_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int64, C.c_int64, C.POINTER(C.c_size_t)]),
     "cvr_score": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
+    "cvr_score_graph": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "cvr_sync_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "cvr_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
     "cvr_debug_export": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t), C.c_void_p]),
@@ -126,6 +127,10 @@ def cvr_workspace_bytes(h, max_requests, max_candidates, max_ids, max_positions)
 
 def cvr_score(h, batch_c, ws_ptr, ws_bytes, out_ptr, stream):
     _check(lib().cvr_score(h, C.byref(batch_c), ws_ptr, ws_bytes, out_ptr, stream), h)
+
+
+def cvr_score_graph(h, batch_c, ws_ptr, ws_bytes, out_ptr, stream):
+    _check(lib().cvr_score_graph(h, C.byref(batch_c), ws_ptr, ws_bytes, out_ptr, stream), h)
 
 
 def cvr_sync_status(h, stream):
@@ -231,14 +236,19 @@ def device_tables(spec, variant="bench", device="cuda"):
 class DeviceBatch:
     """A batch packed on the host into one pinned int32 buffer and copied to the GPU once."""
 
-    def __init__(self, batch, device="cuda", stream=None):
-        torch = _torch()
+    @staticmethod
+    def _parts(batch):
         parts = [np.ascontiguousarray(batch["cand_offsets"], np.int32), np.ascontiguousarray(batch["bag_offsets"], np.int32),
                  np.ascontiguousarray(batch["ids"], np.int32)]
         has_seq = batch.get("seq_offsets") is not None
         if has_seq:
             parts += [np.ascontiguousarray(batch["seq_offsets"], np.int32).reshape(-1),
                       np.ascontiguousarray(batch["seq_ids"], np.int32).reshape(-1)]
+        return parts, has_seq
+
+    def __init__(self, batch, device="cuda", stream=None):
+        torch = _torch()
+        parts, has_seq = self._parts(batch)
         sizes = [p.size for p in parts]
         # 64-element (256-byte) aligned sections
         offs, total = [], 0
@@ -250,6 +260,7 @@ class DeviceBatch:
         for p, o in zip(parts, offs):
             hn[o:o + p.size] = p.reshape(-1)
         self.host = host
+        self._offs, self._sizes = offs, sizes
         self.dev = host.to(device, non_blocking=True)
         base = self.dev.data_ptr()
         self.c = cvr_batch()
@@ -267,6 +278,18 @@ class DeviceBatch:
         self.n_candidates = self.c.n_candidates
         self.n_ids = self.c.n_ids
         self.n_positions = self.c.n_positions
+
+    def refill(self, batch):
+        """Copy another batch of exactly the same section sizes into the same device buffer
+        (its pointers, and so a captured scoring graph, stay valid)."""
+        parts, _ = self._parts(batch)
+        if [p.size for p in parts] != self._sizes:
+            raise ValueError("refill needs a batch with the same sizes")
+        self.host.numpy()[:] = 0
+        hn = self.host.numpy()
+        for p, o in zip(parts, self._offs):
+            hn[o:o + p.size] = p.reshape(-1)
+        self.dev.copy_(self.host, non_blocking=True)
 
 
 class Model:
@@ -304,6 +327,25 @@ class Model:
             out = torch.empty(max(1, dbatch.n_candidates * self.n_tasks), dtype=torch.float32, device=self.device)
         cvr_score(self.h, dbatch.c, C.c_void_p(ws.data_ptr()), ws.numel(), C.c_void_p(out.data_ptr()),
                   _stream_ptr(self.stream))
+        return out
+
+    def score_graph(self, dbatch: DeviceBatch, out=None):
+        """cvr_score_graph on the model's stream (or a private one ordered after the current
+        stream: graph capture needs a created stream)."""
+        torch = _torch()
+        ws = self.workspace(dbatch.n_requests, dbatch.n_candidates, dbatch.n_ids, dbatch.n_positions)
+        if out is None:
+            out = torch.empty(max(1, dbatch.n_candidates * self.n_tasks), dtype=torch.float32, device=self.device)
+        s = self.stream
+        if s is None:
+            if getattr(self, "_gstream", None) is None:
+                self._gstream = torch.cuda.Stream()
+            s = self._gstream
+            s.wait_stream(torch.cuda.current_stream())
+        cvr_score_graph(self.h, dbatch.c, C.c_void_p(ws.data_ptr()), ws.numel(), C.c_void_p(out.data_ptr()),
+                        C.c_void_p(s.cuda_stream))
+        if self.stream is None:
+            torch.cuda.current_stream().wait_stream(s)
         return out
 
     def sync_status(self):

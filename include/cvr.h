@@ -182,6 +182,21 @@ cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_c
 cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
                      float* out_scores, void* hip_stream);
 
+/* cvr_score through graph replay (CVR article section 3.4.4: the serving
+ * path captures the scoring launches once per batch shape and replays them).
+ * Same arguments and result as cvr_score.  The first call for a given key --
+ * the batch's four sizes and five array pointers, workspace, ws_bytes,
+ * out_scores, hip_stream and the debug setting -- captures the call's kernel
+ * launches on hip_stream into a HIP graph and launches it; later calls with
+ * the same key replay that graph, which reads the batch arrays' contents at
+ * replay time.  A call with a different key replaces the graph.  hip_stream
+ * must be a created stream (CVR_ERR_ARG for the null stream); cvr_timing does
+ * not record graph launches.  Host-side checks run on every call; device-side
+ * checks are reported by cvr_sync_status as for cvr_score.  The graph is
+ * released by cvr_destroy. */
+cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
+                           float* out_scores, void* hip_stream);
+
 /* Wait for the stream and report the device error flag of the last
  * cvr_score on that workspace: CVR_ERR_RANGE if an id was outside its table
  * or offsets were malformed (the batch's scores must then be discarded). */
