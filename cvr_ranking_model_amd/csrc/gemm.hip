@@ -352,8 +352,9 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-// Wide-layer GEMM, persistent: each block walks a list of BM x BN output tiles (256 x 256
-// or 256 x 128) with 4 waves of (BM/2) x (BN/2) built from MFMA 32x32x16 tiles.  K advances
+// Wide-layer GEMM, persistent: each block walks a list of BM x BN output tiles (256 x 256 with
+// 8 waves, one block per CU; or 256 x 128 with 4 waves, two blocks per CU), every wave a
+// 128 x 64 tile of MFMA 32x32x16 (two waves per SIMD either way).  K advances
 // in BK-wide slices that go from global memory straight into an NS-slot LDS ring (no register
 // staging), and the slice stream runs across tile boundaries: slice s+NS is requested as soon
 // as slot s%NS is released, mid-way through slice s, so the next tile's first slices are in
@@ -380,26 +381,29 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 // ldc % 8 == 0, no residual, a grid that is a multiple of 8 blocks.
 constexpr int kBigMaxN = 1024;
 template <typename T, int BM, int BN, int BK, int NS, int MINB>
-__global__ __launch_bounds__(256, MINB) void gemm_big_kernel(const GemmParams p) {
+__global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const GemmParams p) {
   typedef typename Lowp<T>::vec8 V8;
   constexpr int KC = BK / 8;              // 16-byte chunks per slice row
   constexpr int RPI = 64 / KC;            // rows filled by one wave transfer (1 KB)
-  constexpr int TPA = BM / RPI / 4;       // transfers per wave per slice: A rows
-  constexpr int TPB = BN / RPI / 4;       //                                W rows
+  constexpr int NW = BN / 64 * 2;         // waves: 2 along M x BN/64 along N, each 128 x 64
+  constexpr int NT = NW * 64;
+  constexpr int TPA = BM / RPI / NW;      // transfers per wave per slice: A rows
+  constexpr int TPB = BN / RPI / NW;      //                                W rows
   constexpr int L = TPA + TPB;
   constexpr int KS = BK / 16;             // MFMA k steps per slice
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = 128, WTN = 64;       // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int kSlot = (BM + BN) * BK;   // elements per ring slot: BM A rows, then BN W rows
   constexpr int kStagePitch = WTN * 2 + 8;  // bytes per staged output row (odd multiple of 8)
   constexpr int RPS = 512 / (WTN * 2);      // staged rows written back per wave instruction
   constexpr int LPR = WTN / 4;              // lanes per staged row on the way out (8 bytes each)
   static_assert(BK == 32 || BK == 64, "slice width");
-  static_assert(TPA >= 1 && TPB >= 1 && BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "loader shape");
+  static_assert(BM == 256, "two 128-row wave tiles along M");
+  static_assert(TPA >= 1 && TPB >= 1 && BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "loader shape");
   static_assert(NS >= 2 && L * (NS - 2) < 64, "ring depth");
   // One LDS allocation: the ring, the per-wave staging areas, the bias of all N columns.
   constexpr int kRingBytes = NS * kSlot * (int)sizeof(T);
-  constexpr int kStageBytes = 4 * 32 * kStagePitch;
+  constexpr int kStageBytes = NW * 32 * kStagePitch;
   __shared__ __align__(1024) char lds[kRingBytes + kStageBytes + kBigMaxN * 4];
   T* const smem = reinterpret_cast<T*>(lds);
   char* const stage = lds + kRingBytes + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 32 * kStagePitch;
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_big_kernel(const GemmParams p)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int g = blockIdx.y;
   const int ntn = p.N / BN;
   const int total = ((p.M + BM - 1) / BM) * ntn;
@@ -416,12 +420,12 @@ __global__ __launch_bounds__(256, MINB) void gemm_big_kernel(const GemmParams p)
   const int first = x * tq + (x < trem ? x : trem) + (blockIdx.x >> 3);
   const int last = (x + 1) * tq + (x + 1 < trem ? x + 1 : trem);
   if (first >= last) return;
-  for (int c = tid; c < p.N; c += 256) bias_s[c] = p.bias ? p.bias[(int64_t)g * p.bias_gstride + c] : 0.f;
+  for (int c = tid; c < p.N; c += NT) bias_s[c] = p.bias ? p.bias[(int64_t)g * p.bias_gstride + c] : 0.f;
 
   auto swz = [](int row) { return KC == 4 ? (row >> 2) & 3 : (row >> 1) & 7; };
-  // Loader: transfer (4i + wave) fills rows RPI*(4i+wave) .. +RPI-1; lane l lands in row
+  // Loader: transfer (NW i + wave) fills rows RPI*(NW i+wave) .. +RPI-1; lane l lands in row
   // l/KC of them at slot l%KC and must fetch k-chunk slot ^ swz(row).  swz(row) is the same
-  // for every i (RPI*4 is a multiple of the swizzle period), so each lane has one k-chunk.
+  // for every i (RPI*NW is a multiple of the swizzle period), so each lane has one k-chunk.
   const int lrow = lane / KC;
   const int kch = (lane % KC) ^ swz(RPI * wave + lrow);
   const int nk = p.K / BK;
@@ -437,13 +441,13 @@ __global__ __launch_bounds__(256, MINB) void gemm_big_kernel(const GemmParams p)
     const int tm0 = (t / ntn) * BM, tn0 = (t % ntn) * BN;
 #pragma unroll
     for (int i = 0; i < TPA; ++i) {
-      const int r = tm0 + RPI * (4 * i + wave) + lrow;
+      const int r = tm0 + RPI * (NW * i + wave) + lrow;
       am[i] = r < p.M ? r : p.M - 1;
     }
 #pragma unroll
     for (int i = 0; i < TPB; ++i)
       wrow[i] = reinterpret_cast<const T*>(p.W) + (int64_t)g * p.w_gstride +
-                (int64_t)(tn0 + RPI * (4 * i + wave) + lrow) * p.K + kch * 8;
+                (int64_t)(tn0 + RPI * (NW * i + wave) + lrow) * p.K + kch * 8;
     seg = -1;
     seg_kb = 0;
     seg_end = 0;
@@ -484,9 +488,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_big_kernel(const GemmParams p)
     T* sA = smem + slot * kSlot;
     T* sB = sA + BM * BK;
 #pragma unroll
-    for (int i = 0; i < TPA; ++i) load_lds16(aptr[i] + off, sA + (4 * i + wave) * 512);
+    for (int i = 0; i < TPA; ++i) load_lds16(aptr[i] + off, sA + (NW * i + wave) * 512);
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) load_lds16(wrow[i] + k0, sB + (4 * i + wave) * 512);
+    for (int i = 0; i < TPB; ++i) load_lds16(wrow[i] + k0, sB + (NW * i + wave) * 512);
   };
 
   const int lr = lane & 31, lc = lane >> 5;
@@ -627,10 +631,10 @@ static int big_grid(int tiles, int per_cu) {
   return b < 8 ? 8 : b;
 }
 
-// Tile choice: the persistent wide-layer kernel (256 x 128 tiles, two blocks per CU) when its
-// layout requirements hold and there is at least a tile per CU; otherwise 128x128 (64-wide
-// slices when every K-segment boundary allows, else 32-wide); 64x64 when even 128x128 cannot
-// cover the chip (the per-candidate GEMMs of the CVR model at small batch).
+// Tile choice: the persistent wide-layer kernel when its layout requirements hold and there is
+// at least a tile per CU (256 x 256 tiles when N allows, else 256 x 128); otherwise 128x128
+// (64-wide slices when every K-segment boundary allows, else 32-wide); 64x64 when even 128x128
+// cannot cover the chip (the per-candidate GEMMs of the CVR model at small batch).
 template <typename T, bool AF32>
 static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
@@ -649,6 +653,9 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   const dim3 blk(256);
   if (tile == 256) {
     if constexpr (AF32) return hipErrorInvalidValue;  // excluded above
+    else if (p.N % 256 == 0 && (int64_t)tiles(256, 256) * p.groups >= 256)
+      launch_k((gemm_big_kernel<T, 256, 256, 32, 3, 1>), dim3(big_grid(tiles(256, 256), 1), p.groups), dim3(512), 0,
+               st, p);
     else launch_k((gemm_big_kernel<T, 256, 128, 32, 2, 2>), dim3(big_grid(tiles(256, 128), 2), p.groups), blk, 0, st, p);
   } else if (tile == 128) {
     if (bk64) launch_k((gemm_kernel<T, 128, 128, 2, 2, AF32, 64>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
