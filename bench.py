@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--batch", type=int, default=None, help="requests per step (CVR batch sweep)")
+    ap.add_argument("--candidates", type=int, default=None,
+                    help="candidates per request (CVR: 1 user + C candidates sharing its sequences)")
     ap.add_argument("--variant", default="bench")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,7 +164,7 @@ def main():
     tables = cv.device_tables(spec, args.variant)
     weights = synth.make_weights(spec, args.variant)
     model = cv.Model(spec, tables, weights)
-    batch = synth.make_batch(spec, requests=args.batch, uniform_ids=args.uniform_ids)
+    batch = synth.make_batch(spec, requests=args.batch, candidates=args.candidates, uniform_ids=args.uniform_ids)
     db = cv.DeviceBatch(batch)
     n = db.n_candidates
     out = torch.empty(n * model.n_tasks, dtype=torch.float32, device="cuda")

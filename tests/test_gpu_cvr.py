@@ -138,6 +138,13 @@ def test_c4_two_layers_small():
     check_cvr(spec, m, synth.make_batch(spec, requests=6), "stress")
 
 
+def test_one_user_many_candidates():
+    spec = synth.load_spec("c3")
+    banner("c3 1 user + 500 candidates: 2 requests x 500, sequences once per request, oracle on request 1")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec, requests=2, candidates=500), "stress", requests=[1])
+
+
 def test_ragged_multi_candidate():
     spec = synth.load_spec("c3")
     banner("c3 ragged: several candidates per request, empty and length-1 sequences, empty bags")
