@@ -354,8 +354,8 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 
 // Wide-layer GEMM, persistent: each block walks a list of BM x BN output tiles (256 x 256 with
 // 8 waves, one block per CU; or 256 x 128 with 4 waves, two blocks per CU), every wave a
-// 128 x 64 tile of MFMA 32x32x16 (two waves per SIMD either way).  K advances
-// in BK-wide slices that go from global memory straight into an NS-slot LDS ring (no register
+// 128 x 64 tile of MFMA 32x32x16 (two waves per SIMD either way).  K advances in BK-wide
+// slices (32 or 64) that go from global memory straight into an NS-slot LDS ring (no register
 // staging), and the slice stream runs across tile boundaries: slice s+NS is requested as soon
 // as slot s%NS is released, mid-way through slice s, so the next tile's first slices are in
 // flight while this tile's epilogue runs.  Transfers and fragment reads are interleaved with
@@ -403,10 +403,13 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
   static_assert(NS >= 2 && L * (NS - 2) < 64, "ring depth");
   // One LDS allocation: the ring, the per-wave staging areas, the bias of all N columns.
   constexpr int kRingBytes = NS * kSlot * (int)sizeof(T);
-  constexpr int kStageBytes = NW * 32 * kStagePitch;
+  // Staged output rows per pass: a whole 32-row m-tile, or half of it when the ring leaves too
+  // little LDS.
+  constexpr int SR = kRingBytes + NW * 32 * kStagePitch + kBigMaxN * 4 <= 160 * 1024 ? 32 : 16;
+  constexpr int kStageBytes = NW * SR * kStagePitch;
   __shared__ __align__(1024) char lds[kRingBytes + kStageBytes + kBigMaxN * 4];
   T* const smem = reinterpret_cast<T*>(lds);
-  char* const stage = lds + kRingBytes + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 32 * kStagePitch;
+  char* const stage = lds + kRingBytes + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * SR * kStagePitch;
   float* const bias_s = reinterpret_cast<float*>(lds + kRingBytes + kStageBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -583,32 +586,41 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int mrow0 = m0 + wm * WTM + i * 32;
+      typedef T T4 __attribute__((ext_vector_type(4)));
+      T4 o[FN][4];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          typedef T T4 __attribute__((ext_vector_type(4)));
           const int col = j * 32 + 8 * q + 4 * lc;
           const float4 b4 = *reinterpret_cast<const float4*>(&bias_s[ncol0 + col]);
           const float bq[4] = {b4.x, b4.y, b4.z, b4.w};
-          T4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float v = acc[i][j][4 * q + e] + bq[e];
             if (p.relu) v = v > 0.f ? v : 0.f;
-            o[e] = Lowp<T>::from_f32(v);
+            o[j][q][e] = Lowp<T>::from_f32(v);
           }
-          *reinterpret_cast<T4*>(stage + lr * kStagePitch + col * 2) = o;
         }
-      if (i == 0) wait_vmcnt<0>();  // the next tile's first slices land before any store
 #pragma unroll
-      for (int rr = 0; rr < 32 / RPS; ++rr) {
-        const int r = rr * RPS + lane / LPR;
-        const uint2 v = *reinterpret_cast<const uint2*>(stage + r * kStagePitch + (lane % LPR) * 8);
-        const int m = mrow0 + r;
-        if (m < p.M)
-          *reinterpret_cast<uint2*>(reinterpret_cast<T*>(p.C) + (int64_t)g * p.c_gstride + (int64_t)m * p.ldc + ncol0 +
-                                    4 * (lane % LPR)) = v;
+      for (int h = 0; h < 32 / SR; ++h) {
+        if (SR == 32 || (lr >> 4) == h) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<T4*>(stage + (lr - h * SR) * kStagePitch + (j * 32 + 8 * q + 4 * lc) * 2) = o[j][q];
+        }
+        if (i == 0 && h == 0) wait_vmcnt<0>();  // the next tile's first slices land before any store
+#pragma unroll
+        for (int rr = 0; rr < SR / RPS; ++rr) {
+          const int r = rr * RPS + lane / LPR;
+          const uint2 v = *reinterpret_cast<const uint2*>(stage + r * kStagePitch + (lane % LPR) * 8);
+          const int m = mrow0 + h * SR + r;
+          if (m < p.M)
+            *reinterpret_cast<uint2*>(reinterpret_cast<T*>(p.C) + (int64_t)g * p.c_gstride + (int64_t)m * p.ldc +
+                                      ncol0 + 4 * (lane % LPR)) = v;
+        }
       }
     }
     landed = true;
@@ -653,9 +665,15 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   const dim3 blk(256);
   if (tile == 256) {
     if constexpr (AF32) return hipErrorInvalidValue;  // excluded above
-    else if (p.N % 256 == 0 && (int64_t)tiles(256, 256) * p.groups >= 256)
-      launch_k((gemm_big_kernel<T, 256, 256, 32, 3, 1>), dim3(big_grid(tiles(256, 256), 1), p.groups), dim3(512), 0,
-               st, p);
+    else if (p.N % 256 == 0 && (int64_t)tiles(256, 256) * p.groups >= 256) {
+      // 64-wide slices (half the block barriers) when every A segment allows them
+      if (bk64)
+        launch_k((gemm_big_kernel<T, 256, 256, 64, 2, 1>), dim3(big_grid(tiles(256, 256), 1), p.groups), dim3(512), 0,
+                 st, p);
+      else
+        launch_k((gemm_big_kernel<T, 256, 256, 32, 3, 1>), dim3(big_grid(tiles(256, 256), 1), p.groups), dim3(512), 0,
+                 st, p);
+    }
     else launch_k((gemm_big_kernel<T, 256, 128, 32, 2, 2>), dim3(big_grid(tiles(256, 128), 2), p.groups), blk, 0, st, p);
   } else if (tile == 128) {
     if (bk64) launch_k((gemm_kernel<T, 128, 128, 2, 2, AF32, 64>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
