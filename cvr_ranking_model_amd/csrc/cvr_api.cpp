@@ -3,8 +3,10 @@
 // allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <string>
@@ -233,11 +235,31 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
     if (!seen[i]) { std::string n = m->w[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "missing weight " + n); }
   hipError_t he = hipStreamSynchronize(s);
   if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("create sync: ") + hipGetErrorString(he)); }
+  if (const char* pr = getenv("CVR_DLRM_PASS_ROWS")) m->pass_rows = std::max(0ll, atoll(pr));  // tuning override
   *out = m;
   return CVR_OK;
 }
 
 // ------------------------------------------------------------------ workspace
+
+// The DLRM MLP runs all its layers over one slice of candidates before the next slice, so
+// its two activation buffers hold one slice rather than the whole batch.  A slice is sized so
+// that one buffer takes at most 128 MB (65536 candidates at width 1024, fp16): at 128k
+// candidates the whole-batch buffers (2 x 256 MB) would stream through the 256 MB
+// last-level cache on every layer, while two slices keep their buffers there.  Each slice
+// costs one more launch per layer, so slices are no smaller than that.  The result does not
+// depend on the split: each candidate's row is computed by the same arithmetic in any slice.
+// The slice never grows with n, so a workspace sized for a batch serves every smaller one.
+int64_t cvr::dlrm_pass_rows(const cvr_model* m, int64_t n) {
+  if (m->debug || m->pass_rows == 0) return n;
+  int64_t rows = m->pass_rows;
+  if (rows < 0) {
+    int maxw = 1;
+    for (int i = 0; i < m->spec.n_hidden; ++i) maxw = std::max(maxw, m->hidden[i]);
+    rows = std::max<int64_t>(256, ((int64_t)128 << 20) / ((int64_t)maxw * 2) / 256 * 256);
+  }
+  return std::min(n, rows);
+}
 
 WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) {
   const cvr_spec& s = m->spec;
@@ -259,8 +281,9 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
   if (s.model == CVR_MODEL_DLRM) {
     int maxw = 1;
     for (int i = 0; i < s.n_hidden; ++i) maxw = std::max(maxw, m->hidden[i]);
-    w.h[0] = take((size_t)n * maxw * lp);
-    w.h[1] = take((size_t)n * maxw * lp);
+    const int64_t hr = dlrm_pass_rows(m, n);
+    w.h[0] = take((size_t)hr * maxw * lp);
+    w.h[1] = take((size_t)hr * maxw * lp);
   } else {
     const int64_t d = s.d, S = s.n_seq, T = s.n_tokens + s.n_seq;
     w.tok[0] = take((size_t)n * T * d * 4);
@@ -422,13 +445,15 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
 }
 
 // The model input as GEMM K-segments (request-side runs read through cand_req).
-static void input_segments(const cvr_model* m, char* ws, const WsPlan& w, GemmParams& g) {
+// Candidate rows r0.. of the model input: item columns are read in place, request columns
+// through the candidate -> request map.
+static void input_segments(const cvr_model* m, char* ws, const WsPlan& w, GemmParams& g, int64_t r0 = 0) {
   g.nseg = (int)m->segs.size();
   for (size_t i = 0; i < m->segs.size(); ++i) {
     const InputSeg& sg = m->segs[i];
     ASeg& a = g.seg[i];
-    a.ptr = ws + (sg.item ? w.x_item : w.x_req);
-    a.rowmap = sg.item ? nullptr : (const int32_t*)(ws + w.cand_req);
+    a.ptr = sg.item ? ws + w.x_item + (size_t)r0 * m->ld_item * 2 : ws + w.x_req;
+    a.rowmap = sg.item ? nullptr : (const int32_t*)(ws + w.cand_req) + r0;
     a.ld = sg.item ? m->ld_item : m->ld_req;
     a.gstride = 0;
     a.k_end = sg.k_end;
@@ -440,43 +465,49 @@ static void input_segments(const cvr_model* m, char* ws, const WsPlan& w, GemmPa
 static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan& w, float* out, Launcher& L,
                            hipStream_t s) {
   const cvr_spec& sp = m->spec;
-  const int n = b->n_candidates;
+  const int64_t n = b->n_candidates;
+  const int64_t pr = dlrm_pass_rows(m, n);
+  if (sp.n_hidden < 1) return hipErrorInvalidValue;  // zero hidden layers: not supported by the output kernel
   hipError_t e = hipSuccess;
-  int in = m->e_dim;
-  int cur = -1;
-  for (int i = 0; i < sp.n_hidden; ++i) {
-    const int width = m->hidden[i];
-    GemmParams g{};
-    g.M = n;
-    g.N = width;
-    g.K = in;
-    g.groups = 1;
-    if (i == 0) input_segments(m, ws, w, g);
-    else {
-      g.nseg = 1;
-      g.seg[0] = ASeg{ws + w.h[cur], nullptr, (int64_t)in, 0, in, 8, 0, 0};
+  for (int64_t r0 = 0; r0 < n; r0 += pr) {
+    const int mc = (int)std::min(pr, n - r0);
+    int in = m->e_dim;
+    int cur = -1;
+    for (int i = 0; i < sp.n_hidden; ++i) {
+      const int width = m->hidden[i];
+      GemmParams g{};
+      g.M = mc;
+      g.N = width;
+      g.K = in;
+      g.groups = 1;
+      if (i == 0) input_segments(m, ws, w, g, r0);
+      else {
+        g.nseg = 1;
+        g.seg[0] = ASeg{ws + w.h[cur], nullptr, (int64_t)in, 0, in, 8, 0, 0};
+      }
+      g.W = m->wptr("mlp." + std::to_string(i) + ".weight");
+      g.bias = (const float*)m->wptr("mlp." + std::to_string(i) + ".bias");
+      const int nxt = cur == 0 ? 1 : 0;
+      g.C = ws + w.h[nxt];
+      g.ldc = width;
+      g.c_nstride8 = 8;
+      g.relu = 1;
+      e = L(STAGE_MLP_GEMM, [&] { return launch_gemm(g, sp.lowp, s); });
+      if (e != hipSuccess) return e;
+      cur = nxt;
+      in = width;
     }
-    g.W = m->wptr("mlp." + std::to_string(i) + ".weight");
-    g.bias = (const float*)m->wptr("mlp." + std::to_string(i) + ".bias");
-    const int nxt = cur == 0 ? 1 : 0;
-    g.C = ws + w.h[nxt];
-    g.ldc = width;
-    g.c_nstride8 = 8;
-    g.relu = 1;
-    e = L(STAGE_MLP_GEMM, [&] { return launch_gemm(g, sp.lowp, s); });
+    m->last_hidden_buf = cur;
+    const void* H = ws + w.h[cur];
+    const int L_ = sp.n_hidden;
+    e = L(STAGE_DLRM_OUTPUT, [&] {
+      return launch_dlrm_output(H, mc, in, m->wptr("mlp." + std::to_string(L_) + ".weight"),
+                                (const float*)m->wptr("mlp." + std::to_string(L_) + ".bias"),
+                                (float*)(ws + w.logits) + r0, out + r0, sp.lowp, s);
+    });
     if (e != hipSuccess) return e;
-    cur = nxt;
-    in = width;
   }
-  m->last_hidden_buf = cur < 0 ? 0 : cur;
-  const void* H = cur < 0 ? nullptr : ws + w.h[cur];
-  if (cur < 0) return hipErrorInvalidValue;  // zero hidden layers: not supported by the output kernel
-  const int L_ = sp.n_hidden;
-  return L(STAGE_DLRM_OUTPUT, [&] {
-    return launch_dlrm_output(H, n, in, m->wptr("mlp." + std::to_string(L_) + ".weight"),
-                              (const float*)m->wptr("mlp." + std::to_string(L_) + ".bias"),
-                              (float*)(ws + w.logits), out, sp.lowp, s);
-  });
+  return e;
 }
 
 extern "C" cvr_status cvr_score(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes, float* out_scores,

@@ -97,6 +97,7 @@ struct cvr_model {
   const void* wptr(const std::string& name) const { return arena + w[widx.at(name)].off; }
   // state
   int debug = 0;
+  int64_t pass_rows = -1;  // DLRM candidates per MLP pass: -1 derived from the layer width, 0 one pass
   std::string err;
   char* last_ws = nullptr;
   cvr::WsPlan last_plan;
@@ -108,6 +109,8 @@ struct cvr_model {
 
 namespace cvr {
 WsPlan plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P);
+// Candidates per DLRM MLP pass for a batch of n (all of them in debug mode).
+int64_t dlrm_pass_rows(const cvr_model* m, int64_t n);
 
 // Times each launch function of one scoring call with a pair of HIP events when timing is armed:
 // the events ride on the dispatches themselves (see launch_k); a bracket that launched nothing

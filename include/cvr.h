@@ -178,7 +178,13 @@ cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_c
  * DLRM) for every candidate c and task k.  workspace: device, 256-byte
  * aligned, at least cvr_workspace_bytes for this batch's sizes.  Host-side
  * checks return at once; device-side checks are reported by cvr_sync_status.
- * Enqueued on hip_stream; returns without synchronising. */
+ * Enqueued on hip_stream; returns without synchronising.
+ * DLRM specs run the hidden layers over slices of the candidates, each slice
+ * through every layer before the next (at most 128 MB per activation buffer:
+ * 65536 candidates at width 1024; the environment variable
+ * CVR_DLRM_PASS_ROWS, read by cvr_create, sets another slice size, 0 meaning
+ * one slice).  Scores do not depend on the slicing.  With debug on, one slice
+ * covers the batch so that the last hidden layer can be exported whole. */
 cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
                      float* out_scores, void* hip_stream);
 
