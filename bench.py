@@ -140,6 +140,9 @@ def main():
     ap.add_argument("--candidates", type=int, default=None,
                     help="candidates per request (CVR: 1 user + C candidates sharing its sequences)")
     ap.add_argument("--variant", default="bench")
+    ap.add_argument("--ple-task-experts", default=None,
+                    help="CVR: experts each task's gate mixes, tasks separated by '/', e.g. 0,2/1,2 "
+                         "(PLE with one task-specific expert per task and a shared one)")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -160,6 +163,8 @@ def main():
     from cvr_ranking_model_amd import cvr as cv
 
     spec = synth.load_spec(args.workload)
+    if args.ple_task_experts:
+        spec["ple_task_experts"] = [[int(e) for e in t.split(",")] for t in args.ple_task_experts.split("/")]
     print(f"[bench] workload {args.workload}: filling tables", file=sys.stderr, flush=True)
     tables = cv.device_tables(spec, args.variant)
     weights = synth.make_weights(spec, args.variant)
@@ -252,8 +257,9 @@ def main():
         "vs_baseline": None,
         "dtype": spec["lowp"],
         "data": f"synthetic ({args.variant} variant: seeded hash tables, Zipf ids, Glorot weights)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "candidates_per_step": n,
-                   "requests_per_step": db.n_requests},
+        "config": dict({"workload": WORKLOAD_TEXT[args.workload], "candidates_per_step": n,
+                        "requests_per_step": db.n_requests},
+                       **({"ple_task_experts": spec["ple_task_experts"]} if args.ple_task_experts else {})),
         "roofline": roof,
         "stages": table,
         "ids": "uniform" if args.uniform_ids else "zipf",

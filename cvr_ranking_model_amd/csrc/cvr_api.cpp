@@ -72,6 +72,17 @@ static cvr_status check_spec(const cvr_spec* s, const cvr_table* tables, int32_t
         s->head_hidden <= 0 || s->head_hidden % 32) { why = "mixer/expert/head widths must be multiples of 32"; return CVR_ERR_UNSUPPORTED; }
     if (s->n_experts <= 0 || s->n_experts > 8 || s->n_tasks <= 0 || s->n_tasks > 8) { why = "bad expert/task counts"; return CVR_ERR_SPEC; }
     if (s->expert_dim % 64) { why = "expert width must be a multiple of 64"; return CVR_ERR_UNSUPPORTED; }
+    if (s->task_experts) {
+      for (int k = 0; k < s->n_tasks; ++k) {
+        int cnt = 0;
+        for (int e = 0; e < s->n_experts; ++e) {
+          const int32_t v = s->task_experts[k * s->n_experts + e];
+          if (v != 0 && v != 1) { why = "task_experts entries must be 0 or 1"; return CVR_ERR_SPEC; }
+          cnt += v;
+        }
+        if (cnt == 0) { why = "every task must mix at least one expert"; return CVR_ERR_SPEC; }
+      }
+    }
     if (!(s->tau > 0.f) || !std::isfinite(s->tau)) { why = "tau must be positive"; return CVR_ERR_SPEC; }
   }
   return CVR_OK;
@@ -151,8 +162,8 @@ static void plan_weights(cvr_model* m) {
     const int zd = T * d;
     for (int e = 0; e < s.n_experts; ++e) add("ple.expert." + std::to_string(e) + ".weight", s.expert_dim, zd, true);
     for (int e = 0; e < s.n_experts; ++e) add("ple.expert." + std::to_string(e) + ".bias", s.expert_dim, 1, false);
-    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".weight", s.n_experts, zd, true);
-    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".bias", s.n_experts, 1, false);
+    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".weight", __builtin_popcount(m->task_mask[k]), zd, true);
+    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".bias", __builtin_popcount(m->task_mask[k]), 1, false);
     for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc1.weight", s.head_hidden, s.expert_dim, true);
     for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc1.bias", s.head_hidden, 1, false);
     for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc2.weight", 1, s.head_hidden, true);
@@ -170,6 +181,13 @@ static cvr_model* new_model(const cvr_spec* spec, const cvr_table* tables, int32
   m->spec.hidden = m->hidden.data();
   if (spec->model == CVR_MODEL_HYFORMER) m->seq_tables.assign(spec->seq_tables, spec->seq_tables + spec->n_seq_cols);
   m->spec.seq_tables = m->seq_tables.data();
+  if (spec->model == CVR_MODEL_HYFORMER) {
+    m->task_mask.assign(spec->n_tasks, 0);
+    for (int k = 0; k < spec->n_tasks; ++k)
+      for (int e = 0; e < spec->n_experts; ++e)
+        if (!spec->task_experts || spec->task_experts[k * spec->n_experts + e]) m->task_mask[k] |= 1 << e;
+  }
+  m->spec.task_experts = nullptr;  // the caller's array is not kept; task_mask holds it
   m->tables.assign(tables, tables + n_tables);
   derive(m);
   plan_weights(m);

@@ -238,10 +238,11 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     p.Z = (const float*)tok[cur];
     p.n = n;
     p.zdim = T * d;
-    p.Wg = (const __bf16*)m->wptr("ple.gate.0.weight");
-    p.wg_task_stride = group_stride(m, [](int i) { return "ple.gate." + S_(i) + ".weight"; }, K, 2);
-    if (K > 1 && p.wg_task_stride < 0) return hipErrorInvalidValue;
-    for (int k = 0; k < K; ++k) p.bg[k] = (const float*)m->wptr("ple.gate." + S_(k) + ".bias");
+    for (int k = 0; k < K; ++k) {
+      p.wg[k] = (const __bf16*)m->wptr("ple.gate." + S_(k) + ".weight");
+      p.bg[k] = (const float*)m->wptr("ple.gate." + S_(k) + ".bias");
+      p.emask[k] = m->task_mask[k];
+    }
     p.E = E;
     p.K = K;
     p.experts = (const float*)(ws + w.experts);

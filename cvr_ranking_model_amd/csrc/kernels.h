@@ -186,9 +186,9 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st);
 struct PleGateParams {
   const float* Z;               // [n][zdim] (rounded to bf16 as the gates' Linear input)
   int32_t n, zdim;
-  const __bf16* Wg;             // task k, expert e: Wg + k*wg_task_stride + e*zdim
-  int64_t wg_task_stride;
-  const float* bg[kMaxTasks];   // [E] per task
+  const __bf16* wg[kMaxTasks];  // task k: one row of zdim per expert it mixes, in expert order
+  const float* bg[kMaxTasks];   // task k: one bias per expert it mixes
+  int32_t emask[kMaxTasks];     // task k mixes expert e iff bit e is set
   int32_t E, K;
   const float* experts;         // [n][E*edim]
   int32_t edim;

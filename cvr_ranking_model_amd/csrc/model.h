@@ -84,6 +84,7 @@ struct cvr_model {
   cvr_spec spec{};
   std::vector<cvr_feature> feats;
   std::vector<int32_t> hidden, seq_tables;
+  std::vector<int32_t> task_mask;  // CVR: bit e of task_mask[k] set if task k's gate mixes expert e
   std::vector<cvr_table> tables;
   // derived layout
   std::vector<int> fcol;

@@ -43,7 +43,7 @@ class cvr_spec(C.Structure):
                 ("n_seq_cols", C.c_int32), ("seq_tables", C.POINTER(C.c_int32)),
                 ("swiglu_hidden", C.c_int32), ("tau", C.c_float), ("mixer_heads", C.c_int32),
                 ("mixer_hidden", C.c_int32), ("n_experts", C.c_int32), ("expert_dim", C.c_int32),
-                ("n_tasks", C.c_int32), ("head_hidden", C.c_int32)]
+                ("n_tasks", C.c_int32), ("head_hidden", C.c_int32), ("task_experts", C.POINTER(C.c_int32))]
 
 
 class cvr_weight(C.Structure):
@@ -215,6 +215,15 @@ def spec_to_c(spec, tables):
         s.mixer_heads, s.mixer_hidden = spec["mixer_heads"], spec["mixer_hidden"]
         s.n_experts, s.expert_dim = spec["n_experts"], spec["expert_dim"]
         s.n_tasks, s.head_hidden = spec["n_tasks"], spec["head_hidden"]
+        if spec.get("ple_task_experts") is not None:
+            E = spec["n_experts"]
+            mask = [0] * (spec["n_tasks"] * E)
+            for k, experts in enumerate(spec["ple_task_experts"]):
+                for e in experts:
+                    mask[k * E + e] = 1
+            te = (C.c_int32 * len(mask))(*mask)
+            keep.append(te)
+            s.task_experts = te
     tabs = (cvr_table * len(tables))(*[cvr_table(t.data_ptr(), t.shape[0], t.shape[1]) for t in tables])
     keep.append(tabs)
     return s, tabs, keep

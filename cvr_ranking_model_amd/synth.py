@@ -332,9 +332,11 @@ def weight_shapes(spec: dict) -> dict:
     for e in range(spec["n_experts"]):
         shapes[f"ple.expert.{e}.weight"] = (spec["expert_dim"], z_dim)
         shapes[f"ple.expert.{e}.bias"] = (spec["expert_dim"],)
+    te = spec.get("ple_task_experts")
     for k in range(spec["n_tasks"]):
-        shapes[f"ple.gate.{k}.weight"] = (spec["n_experts"], z_dim)
-        shapes[f"ple.gate.{k}.bias"] = (spec["n_experts"],)
+        g = spec["n_experts"] if te is None else len(te[k])
+        shapes[f"ple.gate.{k}.weight"] = (g, z_dim)
+        shapes[f"ple.gate.{k}.bias"] = (g,)
     for k in range(spec["n_tasks"]):
         shapes[f"head.{k}.fc1.weight"] = (spec["head_hidden"], spec["expert_dim"])
         shapes[f"head.{k}.fc1.bias"] = (spec["head_hidden"],)

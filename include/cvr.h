@@ -112,6 +112,13 @@ typedef struct {
   int32_t expert_dim;       /* expert width (256) */
   int32_t n_tasks;          /* scenarios / heads (2) */
   int32_t head_hidden;      /* head hidden width (128) */
+  /* (CVR) Which experts each task's gate mixes: task_experts[k * n_experts + e]
+   * is 1 if task k mixes expert e, else 0; every task needs at least one.
+   * NULL: every task mixes every expert (shared experts only, MMoE-style).
+   * With 3 experts and 2 tasks, {1,0,1, 0,1,1} is PLE with one task-specific
+   * expert per task plus one shared expert (CVR article section 3.2.4).  Gate
+   * k's Linear has one output per expert it mixes, in expert order. */
+  const int32_t* task_experts;
 } cvr_spec;
 
 /* One dense parameter, fp32, device memory, read only during cvr_create.

@@ -172,6 +172,15 @@ def mixer(spec, weights, l, Y, rnd):
     return Y + token_revert(F, Y.shape[1])
 
 
+def task_experts(spec):
+    """Experts mixed by each task's gate: every expert (shared experts only) unless the spec
+    lists them per task (PLE with task-specific experts)."""
+    lists = spec.get("ple_task_experts")
+    if lists is None:
+        return [list(range(spec["n_experts"])) for _ in range(spec["n_tasks"])]
+    return [sorted(int(e) for e in lst) for lst in lists]
+
+
 def ple_heads(spec, weights, z, rnd):
     """Steps B10-B11: PLE experts, per-task gates and two-layer heads.
 
@@ -179,10 +188,13 @@ def ple_heads(spec, weights, z, rnd):
     PLE + MLP heads: three experts that are single fully-connected layers and
     heads of two fully-connected layers with a nonlinearity; section 3.2 also
     calls the prediction level an MMoE-style expert structure.  Reading: the
-    three experts are shared ReLU(Linear) layers, each task mixes them with
-    its own softmax gate (a Linear to 3 logits) — single-level PLE with shared
-    experts only, which is exactly MMoE — and each head is
-    Linear -> ReLU -> Linear -> sigmoid, the sigmoid in fp32.
+    experts are ReLU(Linear) layers; each task mixes a set of them with its
+    own softmax gate (a Linear with one output per expert in its set), and
+    each head is Linear -> ReLU -> Linear -> sigmoid, the sigmoid in fp32.
+    By default every task mixes all experts — single-level PLE with shared
+    experts only, which is exactly MMoE.  With ``ple_task_experts`` a task
+    mixes only the listed experts, e.g. its own task-specific expert plus a
+    shared one (PLE proper).
     ``z`` is the flattened last-layer token matrix [c, T*d].
     Returns (logits [c, tasks], gated task inputs list).
     """
@@ -191,9 +203,9 @@ def ple_heads(spec, weights, z, rnd):
     experts = [np.maximum(z @ _w(weights, f"ple.expert.{e}.weight", rnd).T + _b(weights, f"ple.expert.{e}.bias"), 0.0)
                for e in range(E)]
     logits, tin = [], []
-    for k in range(spec["n_tasks"]):
+    for k, mixed in enumerate(task_experts(spec)):
         g = softmax(z @ _w(weights, f"ple.gate.{k}.weight", rnd).T + _b(weights, f"ple.gate.{k}.bias"))
-        t = rnd(sum(g[:, e:e + 1] * experts[e] for e in range(E)))
+        t = rnd(sum(g[:, i:i + 1] * experts[e] for i, e in enumerate(mixed)))
         u = rnd(np.maximum(t @ _w(weights, f"head.{k}.fc1.weight", rnd).T + _b(weights, f"head.{k}.fc1.bias"), 0.0))
         y = u @ _w(weights, f"head.{k}.fc2.weight", rnd).T + _b(weights, f"head.{k}.fc2.bias")
         logits.append(y[:, 0])

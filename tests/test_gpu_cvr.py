@@ -117,6 +117,15 @@ def test_c3_parity(variant):
     check_cvr(spec, m, synth.make_batch(spec, requests=16), variant)
 
 
+@pytest.mark.parametrize("task_experts", [[[0, 2], [1, 2]], [[2], [0, 1]]])
+def test_c3_task_specific_experts(task_experts):
+    """PLE with task-specific experts: each task's gate mixes only its listed experts."""
+    spec = dict(synth.load_spec("c3"), ple_task_experts=task_experts)
+    banner(f"c3 stress, PLE task experts {task_experts}: 16 samples")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec, requests=16), "stress")
+
+
 def test_c3_full_sampled():
     spec = synth.load_spec("c3")
     banner("c3 full: 512 samples, oracle on samples 0, 200, 511")

@@ -162,6 +162,42 @@ def test_ple_gates(rng):
     assert np.array_equal(tin[1], ex[1])                                          # dominant gate -> that expert
 
 
+def test_task_specific_experts_reduce_to_masked_shared_gate(rng):
+    """PLE with task-specific experts equals the shared-expert (MMoE) gate whose excluded
+    experts get a zero weight row and a bias of -1e30: their softmax weight is exactly 0."""
+    te = [[0, 2], [1, 2]]
+    spec_t = dict(tiny_cvr_spec(), ple_task_experts=te)
+    spec_s = tiny_cvr_spec()
+    w_t = _cvr_weights(spec_t)
+    assert w_t["ple.gate.0.weight"].shape == (2, 16 * spec_t["d"])
+    w_s = dict(w_t)
+    for k, mixed in enumerate(te):
+        gw = np.zeros((3, 16 * spec_s["d"]), np.float32)
+        gb = np.full(3, -1e30, np.float32)
+        for i, e in enumerate(mixed):
+            gw[e], gb[e] = w_t[f"ple.gate.{k}.weight"][i], w_t[f"ple.gate.{k}.bias"][i]
+        w_s[f"ple.gate.{k}.weight"], w_s[f"ple.gate.{k}.bias"] = gw, gb
+    z = rng.standard_normal((5, 16 * spec_s["d"]))
+    lt, tt = hf.ple_heads(spec_t, w_t, z, IDENT)
+    ls, ts = hf.ple_heads(spec_s, w_s, z, IDENT)
+    for k in range(2):
+        assert np.allclose(tt[k], ts[k], rtol=1e-14, atol=1e-15)
+    assert np.allclose(lt, ls, rtol=1e-13, atol=1e-14)
+    # the two tasks mix different experts, so their inputs differ
+    assert not np.allclose(tt[0], tt[1])
+
+
+def test_single_expert_task_takes_that_expert(rng):
+    """A task that mixes one expert has a gate of exactly 1: its input is that expert's output."""
+    spec = dict(tiny_cvr_spec(), ple_task_experts=[[2], [0, 1]])
+    w = _cvr_weights(spec)
+    assert w["ple.gate.0.weight"].shape[0] == 1 and w["ple.gate.1.weight"].shape[0] == 2
+    z = rng.standard_normal((3, 16 * spec["d"]))
+    ex2 = np.maximum(z @ w["ple.expert.2.weight"].T.astype(np.float64) + w["ple.expert.2.bias"], 0)
+    _, tin = hf.ple_heads(spec, w, z, IDENT)
+    assert np.array_equal(tin[0], ex2)
+
+
 def test_head_closed_form():
     spec = tiny_cvr_spec(expert_dim=2, head_hidden=2, experts=1, tasks=1, d=16)
     z = np.zeros((1, 16 * 16))
@@ -178,8 +214,10 @@ def test_head_closed_form():
     assert logits[0, 0] == 2 * 1.5 - 4.0 + 0.125
 
 
-def _tiny_model(layers=1, C=2, seed=0, lens=None, **kw):
+def _tiny_model(layers=1, C=2, seed=0, lens=None, ple_task_experts=None, **kw):
     spec = tiny_cvr_spec(layers=layers, **kw)
+    if ple_task_experts is not None:
+        spec["ple_task_experts"] = ple_task_experts
     tables = array_tables(spec, seed=seed)
     w = _cvr_weights(spec)
     b = synth.make_batch(spec, requests=3, candidates=C, seq_lengths=lens)
@@ -302,21 +340,24 @@ def _brute_force(spec, tables, w, b):
         z = [v for tok in Zt for v in tok]
         experts = [relu(lin(w[f"ple.expert.{e_}.weight"], z, w[f"ple.expert.{e_}.bias"])) for e_ in range(spec["n_experts"])]
         logits = []
+        lists = spec.get("ple_task_experts") or [list(range(spec["n_experts"]))] * spec["n_tasks"]
         for k in range(spec["n_tasks"]):
             gl = lin(w[f"ple.gate.{k}.weight"], z, w[f"ple.gate.{k}.bias"])
             m = max(gl)
             ge = [math.exp(v - m) for v in gl]
             ge = [v / sum(ge) for v in ge]
-            t_in = [sum(ge[e_] * experts[e_][j] for e_ in range(len(experts))) for j in range(spec["expert_dim"])]
+            mixed = sorted(lists[k])
+            t_in = [sum(ge[i] * experts[e_][j] for i, e_ in enumerate(mixed)) for j in range(spec["expert_dim"])]
             u = relu(lin(w[f"head.{k}.fc1.weight"], t_in, w[f"head.{k}.fc1.bias"]))
             logits.append(lin(w[f"head.{k}.fc2.weight"], u, w[f"head.{k}.fc2.bias"])[0])
         out.append(logits)
     return np.array(out)
 
 
-@pytest.mark.parametrize("layers", [1, 2])
-def test_whole_model_brute_force_exact(layers):
-    spec, tables, w, b = _tiny_model(layers=layers, C=2, lens=[[3, 0, 2], [1, 4, 2], [2, 2, 1]])
+@pytest.mark.parametrize("layers,task_experts", [(1, None), (2, None), (1, [[0, 2], [1, 2]])])
+def test_whole_model_brute_force_exact(layers, task_experts):
+    spec, tables, w, b = _tiny_model(layers=layers, C=2, lens=[[3, 0, 2], [1, 4, 2], [2, 2, 1]],
+                                     ple_task_experts=task_experts)
     got = oracle.score(spec, tables, w, b, exact=True)["logits"]
     want = _brute_force(spec, tables, w, b)
     assert np.allclose(got, want, rtol=1e-11, atol=1e-11)
