@@ -225,6 +225,26 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
   for (int i = 0; i < n_tables; ++i)
     if (!tables[i].data || ((uintptr_t)tables[i].data & 15)) return fail(nullptr, CVR_ERR_ARG, "table data must be non-null and 16-byte aligned");
   cvr_model* m = new_model(spec, tables, n_tables);
+  // Kernels read tables at device addresses: device memory is used as is, pinned host memory
+  // (a table kept in host DRAM) through its device-side address; memory HIP does not know
+  // (pageable host memory) cannot be read by a kernel and is refused.
+  for (int i = 0; i < n_tables; ++i) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, tables[i].data) != hipSuccess) {
+      (void)hipGetLastError();
+      delete m;
+      return fail(nullptr, CVR_ERR_ARG, "table " + std::to_string(i) + " is neither device memory nor pinned host memory");
+    }
+    if (attr.type == hipMemoryTypeHost) {
+      void* p = nullptr;
+      if (hipHostGetDevicePointer(&p, (void*)tables[i].data, 0) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        delete m;
+        return fail(nullptr, CVR_ERR_ARG, "table " + std::to_string(i) + ": host memory without a device address");
+      }
+      m->tables[i].data = (const float*)p;
+    }
+  }
   st = check_segments(m, why);
   if (st != CVR_OK) { delete m; return fail(nullptr, st, why); }
   if (!weight_arena || ((uintptr_t)weight_arena & 255)) { delete m; return fail(nullptr, CVR_ERR_ARG, "weight arena must be non-null and 256-byte aligned"); }
@@ -389,7 +409,7 @@ extern "C" cvr_status cvr_timing_end(cvr_handle h, double* stage_ms, int32_t* st
 extern "C" const char* cvr_stage_name(cvr_handle, int32_t stage) {
   static const char* names[kNumStages] = {"expand", "gather_pool", "mlp_gemm", "dlrm_output", "tokenize_gemm",
                                           "swiglu", "seq_pool", "query_gemm", "attention", "mixer_gemm",
-                                          "ple_gemm", "ple_gate", "head_gemm", "head_out"};
+                                          "ple_gemm", "ple_gate", "head_gemm", "head_out", "cache"};
   return (stage >= 0 && stage < kNumStages) ? names[stage] : "";
 }
 
@@ -408,6 +428,19 @@ static cvr_status check_batch(cvr_model* m, const cvr_batch* b, void* ws, size_t
   plan = plan_workspace(m, b->n_requests, b->n_candidates, m->spec.model == CVR_MODEL_DLRM ? 0 : b->n_positions);
   if (ws_bytes < plan.total) return fail(m, CVR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.total) + " bytes");
   return CVR_OK;
+}
+
+static GatherCache gather_cache(const cvr_model::Cache& c, int32_t dim) {
+  const CacheLayout l = cache_layout(c.sets, c.ways, dim);
+  GatherCache g{};
+  g.hdr = (CacheHeader*)c.state;
+  g.tags = (int32_t*)(c.state + l.tags);
+  g.stamps = (int32_t*)(c.state + l.stamps);
+  g.first = (int32_t*)(c.state + l.first);
+  g.rows = (float*)(c.state + l.rows);
+  g.sets = (int32_t)c.sets;
+  g.ways = c.ways;
+  return g;
 }
 
 // Shared front of both models: flag clear, expand, gather-pool into the two input matrices.
@@ -441,13 +474,28 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
   gp.clamp = sp.clamp;
   gp.lowp = sp.lowp;
   gp.flag = flag;
+  CacheHeader* hdrs[kMaxCaches];
+  for (size_t c = 0; c < m->caches.size(); ++c) {
+    gp.cache[c] = gather_cache(m->caches[c], m->tables[m->caches[c].table].dim);
+    hdrs[c] = gp.cache[c].hdr;
+  }
+  if (!m->caches.empty()) {
+    e = L(STAGE_CACHE, [&] { return launch_cache_begin(hdrs, (int)m->caches.size(), s); });
+    if (e != hipSuccess) return e;
+  }
   int64_t base = 0;
   size_t dbg = w.pooled;
   for (int f = 0; f < sp.n_features; ++f) {
     const cvr_table& t = m->tables[sp.features[f].table];
     const bool item = sp.features[f].side == CVR_SIDE_ITEM;
     GatherFeature& F = gp.f[f];
+    F.cache = -1;
     F.table = t.data;
+    for (size_t c = 0; c < m->caches.size(); ++c)
+      if (m->caches[c].table == sp.features[f].table) {
+        F.cache = (int32_t)c;
+        F.table = m->caches[c].host_dev;
+      }
     F.rows = t.rows;
     F.dim = t.dim;
     F.nbags = item ? b->n_candidates : b->n_requests;
@@ -459,7 +507,17 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
     dbg += (size_t)F.nbags * t.dim * 4;
     base += F.nbags;
   }
-  return L(STAGE_GATHER, [&] { return launch_gather_pool(gp, s); });
+  e = L(STAGE_GATHER, [&] { return launch_gather_pool(gp, s); });
+  if (e != hipSuccess) return e;
+  for (size_t c = 0; c < m->caches.size(); ++c) {
+    const cvr_model::Cache& mc = m->caches[c];
+    e = L(STAGE_CACHE, [&] {
+      return launch_cache_admit(gp.cache[c], b->ids, b->n_ids, mc.host_dev, m->tables[mc.table].rows,
+                                m->tables[mc.table].dim, s);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // The model input as GEMM K-segments (request-side runs read through cand_req).
@@ -687,6 +745,75 @@ extern "C" cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, si
 }
 
 // ------------------------------------------------------------------ misc
+
+// ------------------------------------------------------------------ HBM hot-row cache
+
+extern "C" cvr_status cvr_cache_state_bytes(int64_t sets, int32_t ways, int32_t dim, size_t* bytes) {
+  if (!bytes) return fail(nullptr, CVR_ERR_ARG, "bytes is null");
+  if (sets < 1 || ways < 1 || ways > kCacheMaxWays || sets * ways >= INT32_MAX || dim < 4 || dim % 4)
+    return fail(nullptr, CVR_ERR_ARG, "bad cache shape");
+  *bytes = cache_layout(sets, ways, dim).total;
+  return CVR_OK;
+}
+
+static const cvr_model::Cache* find_cache(const cvr_model* m, int32_t table) {
+  for (const auto& c : m->caches)
+    if (c.table == table) return &c;
+  return nullptr;
+}
+
+extern "C" cvr_status cvr_cache_attach(cvr_handle h, int32_t table, int64_t sets, int32_t ways, void* state,
+                                       size_t state_bytes, void* hip_stream) {
+  if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
+  if (table < 0 || table >= (int32_t)h->tables.size()) return fail(h, CVR_ERR_ARG, "table index out of range");
+  const int32_t dim = h->tables[table].dim;
+  if (sets < 1 || ways < 1 || ways > std::min(kCacheMaxWays, dim / 4) || sets * ways >= INT32_MAX)
+    return fail(h, CVR_ERR_ARG, "cache shape: need 1 <= ways <= min(16, dim/4), sets >= 1, sets*ways < 2^31");
+  bool used = false;
+  for (int f = 0; f < h->spec.n_features; ++f) used |= h->spec.features[f].table == table;
+  if (!used) return fail(h, CVR_ERR_ARG, "no feature reads this table");
+  for (int32_t t : h->seq_tables)
+    if (t == table) return fail(h, CVR_ERR_UNSUPPORTED, "sequence-column tables cannot be cached");
+  if (find_cache(h, table)) return fail(h, CVR_ERR_ARG, "table already has a cache");
+  if ((int)h->caches.size() >= kMaxCaches) return fail(h, CVR_ERR_UNSUPPORTED, "at most 4 caches per model");
+  if (!state || ((uintptr_t)state & 255)) return fail(h, CVR_ERR_ARG, "state must be non-null and 256-byte aligned");
+  const CacheLayout l = cache_layout(sets, ways, dim);
+  if (state_bytes < l.total) return fail(h, CVR_ERR_WORKSPACE, "cache state too small");
+  // tables[].data already holds the device-side address (cvr_create translates host memory).
+  cvr_model::Cache c{table, sets, ways, (char*)state, h->tables[table].data};
+  hipError_t e = launch_cache_init(gather_cache(c, dim), (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("cache init: ") + hipGetErrorString(e));
+  h->caches.push_back(c);
+  h->graph.reset();
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_cache_stats(cvr_handle h, int32_t table, int64_t* counters, void* hip_stream) {
+  if (!h || !counters) return fail(h, CVR_ERR_ARG, "null argument");
+  const cvr_model::Cache* c = find_cache(h, table);
+  if (!c) return fail(h, CVR_ERR_ARG, "table has no cache");
+  unsigned long long v[CACHE_NCOUNTERS];
+  hipStream_t s = (hipStream_t)hip_stream;
+  hipError_t e = hipMemcpyAsync(v, ((CacheHeader*)c->state)->counters, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("cache stats: ") + hipGetErrorString(e));
+  for (int i = 0; i < CACHE_NCOUNTERS; ++i) counters[i] = (int64_t)v[i];
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_cache_export(cvr_handle h, int32_t table, int32_t* tags, int32_t* stamps, void* hip_stream) {
+  if (!h || !tags || !stamps) return fail(h, CVR_ERR_ARG, "null argument");
+  const cvr_model::Cache* c = find_cache(h, table);
+  if (!c) return fail(h, CVR_ERR_ARG, "table has no cache");
+  const CacheLayout l = cache_layout(c->sets, c->ways, h->tables[table].dim);
+  const size_t bytes = (size_t)c->sets * c->ways * 4;
+  hipStream_t s = (hipStream_t)hip_stream;
+  hipError_t e = hipMemcpyAsync(tags, c->state + l.tags, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(stamps, c->state + l.stamps, bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("cache export: ") + hipGetErrorString(e));
+  return CVR_OK;
+}
 
 extern "C" cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed, double halfwidth,
                                      void* hip_stream) {

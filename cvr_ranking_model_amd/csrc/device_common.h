@@ -45,6 +45,16 @@ template <> struct Lowp<bf16> {
   static __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 };
 
+// The 32-bit finaliser of MurmurHash3 (Appleby): maps a row id to its cache set.
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
 // Clamp to [-c, c]; NaN passes through (comparisons with NaN are false).
 __device__ __forceinline__ float clamp_keep_nan(float v, float c) {
   return v < -c ? -c : (v > c ? c : v);

@@ -11,7 +11,8 @@
 // (section 3.1, item 2) on fp32 embeddings (CTR article, section 三) bit for bit.
 // The pooled value is clamped to +-clamp (NaN passes) and rounded to nearest-even
 // into fp16/bf16 (CTR article, section 三), then written at the feature's column
-// of the request-side or item-side input matrix.
+// of the request-side or item-side input matrix.  A table kept in host memory behind an
+// HBM hot-row cache is read through the cache (see CACHED below).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -20,7 +21,15 @@ namespace cvr {
 constexpr int kGatherThreads = 256;
 constexpr int kUnroll = 8;
 
-template <typename T>
+// CACHED: some feature of the launch reads a table that sits behind an HBM hot-row cache
+// (CTR article, section 二).  For such a feature each id is looked up in its set: the group's
+// first `ways` lanes read the set's tags and a ballot finds the way.  A hit reads the row from
+// the cache and stamps the way with the batch number; a miss reads it from the host table and
+// offers the lookup's position to the set's admission slot (atomicMin: the earliest miss of
+// the batch is admitted after the gather).  Either way the same fp32 row is added, so the
+// pooled value does not depend on the cache.  Hits and misses are summed per block and added
+// to the cache's counters.
+template <typename T, bool CACHED>
 __global__ __launch_bounds__(kGatherThreads) void gather_pool_kernel(const GatherParams p) {
   const int b = blockIdx.x;
   int fi = 0;
@@ -32,75 +41,139 @@ __global__ __launch_bounds__(kGatherThreads) void gather_pool_kernel(const Gathe
   const int bags_per_block = kGatherThreads / lpb;
   const int local = (b - F.block_begin) * bags_per_block + (int)threadIdx.x / lpb;
   const int lane = (int)threadIdx.x % lpb;
-  if (local >= F.nbags) return;
+  const bool cached = CACHED && F.cache >= 0;
+  if (!cached && local >= F.nbags) return;          // block-uniform when cached: no barrier follows
 
-  const int64_t g = F.bag_base + local;
-  int64_t lo = p.bag_offsets[g];
-  int64_t hi = p.bag_offsets[g + 1];
-  // Malformed offsets are reported by the expand step; here they only must not lead outside ids.
-  lo = lo < 0 ? 0 : (lo > p.n_ids ? p.n_ids : lo);
-  hi = hi < lo ? lo : (hi > p.n_ids ? p.n_ids : hi);
+  GatherCache C{};
+  int epoch = 0;
+  int gl = 0;
+  if (cached) {
+    C = p.cache[F.cache];
+    epoch = C.hdr->epoch;
+    gl = ((int)threadIdx.x & 63) - lane;              // the group's first lane in its wave
+  }
+  uint32_t hits = 0, misses = 0;
+  if (local < F.nbags) {
+    const int64_t g = F.bag_base + local;
+    int64_t lo = p.bag_offsets[g];
+    int64_t hi = p.bag_offsets[g + 1];
+    // Malformed offsets are reported by the expand step; here they only must not lead outside ids.
+    lo = lo < 0 ? 0 : (lo > p.n_ids ? p.n_ids : lo);
+    hi = hi < lo ? lo : (hi > p.n_ids ? p.n_ids : hi);
 
-  const float* __restrict__ tab = F.table + lane * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  bool bad = false;
+    const float* __restrict__ tab = F.table + lane * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool bad = false;
 #pragma unroll 1
-  for (int64_t j = lo; j < hi; j += kUnroll) {
-    float4 r[kUnroll];
+    for (int64_t j = lo; j < hi; j += kUnroll) {
+      float4 r[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j + u < hi) {
-        const int32_t id = p.ids[j + u];
-        if (id >= 0 && (int64_t)id < F.rows)
-          r[u] = *reinterpret_cast<const float4*>(tab + (int64_t)id * F.dim);
-        else
-          bad = true;
+      for (int u = 0; u < kUnroll; ++u) {
+        r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j + u < hi) {
+          const int32_t id = p.ids[j + u];
+          if (id >= 0 && (int64_t)id < F.rows) {
+            const float* src = tab + (int64_t)id * F.dim;
+            if (cached) {
+              const uint32_t set = fmix32((uint32_t)id) % (uint32_t)C.sets;
+              const int64_t base = (int64_t)set * C.ways;
+              const int32_t tag = lane < C.ways ? C.tags[base + lane] : -1;
+              const uint64_t found = (__ballot(tag == id) >> gl) & ((1ull << C.ways) - 1);
+              if (found) {
+                const int way = __builtin_ctzll(found);
+                src = C.rows + (base + way) * F.dim + lane * 4;
+                if (lane == 0) {
+                  C.stamps[base + way] = epoch;
+                  ++hits;
+                }
+              } else if (lane == 0) {
+                atomicMin(&C.first[set], (int32_t)(j + u));
+                ++misses;
+              }
+            }
+            r[u] = *reinterpret_cast<const float4*>(src);
+          } else {
+            bad = true;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j + u < hi) {
+          acc.x += r[u].x;
+          acc.y += r[u].y;
+          acc.z += r[u].z;
+          acc.w += r[u].w;
+        }
       }
     }
+    if (bad) raise_flag(p.flag, ERRF_ID_RANGE);
+    const int64_t len = hi - lo;
+    if (len > 0) {
+      const float fl = (float)len;
+      acc.x = acc.x / fl;
+      acc.y = acc.y / fl;
+      acc.z = acc.z / fl;
+      acc.w = acc.w / fl;
+    }
+    if (F.dbg) *reinterpret_cast<float4*>(F.dbg + (int64_t)local * F.dim + lane * 4) = acc;
+    typedef typename Lowp<T>::vec4 V4;
+    V4 o;
+    o[0] = Lowp<T>::from_f32(clamp_keep_nan(acc.x, p.clamp));
+    o[1] = Lowp<T>::from_f32(clamp_keep_nan(acc.y, p.clamp));
+    o[2] = Lowp<T>::from_f32(clamp_keep_nan(acc.z, p.clamp));
+    o[3] = Lowp<T>::from_f32(clamp_keep_nan(acc.w, p.clamp));
+    T* out = reinterpret_cast<T*>(F.out) + (int64_t)local * F.ldo + F.col + lane * 4;
+    *reinterpret_cast<V4*>(out) = o;
+  }
+  if (cached) {
+    // Block totals of the lookups' outcomes (only each group's lane 0 counted).
+    __shared__ uint32_t red[2][kGatherThreads / 64];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (j + u < hi) {
-        acc.x += r[u].x;
-        acc.y += r[u].y;
-        acc.z += r[u].z;
-        acc.w += r[u].w;
+    for (int off = 32; off >= 1; off >>= 1) {
+      hits += __shfl_xor(hits, off);
+      misses += __shfl_xor(misses, off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      red[0][threadIdx.x >> 6] = hits;
+      red[1][threadIdx.x >> 6] = misses;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t h = 0, m = 0;
+      for (int w = 0; w < kGatherThreads / 64; ++w) {
+        h += red[0][w];
+        m += red[1][w];
       }
+      if (h + m) atomicAdd(&C.hdr->counters[CACHE_LOOKUPS], (unsigned long long)(h + m));
+      if (h) atomicAdd(&C.hdr->counters[CACHE_HITS], (unsigned long long)h);
+      if (m) atomicAdd(&C.hdr->counters[CACHE_MISSES], (unsigned long long)m);
     }
   }
-  if (bad) raise_flag(p.flag, ERRF_ID_RANGE);
-  const int64_t len = hi - lo;
-  if (len > 0) {
-    const float fl = (float)len;
-    acc.x = acc.x / fl;
-    acc.y = acc.y / fl;
-    acc.z = acc.z / fl;
-    acc.w = acc.w / fl;
-  }
-  if (F.dbg) *reinterpret_cast<float4*>(F.dbg + (int64_t)local * F.dim + lane * 4) = acc;
-  typedef typename Lowp<T>::vec4 V4;
-  V4 o;
-  o[0] = Lowp<T>::from_f32(clamp_keep_nan(acc.x, p.clamp));
-  o[1] = Lowp<T>::from_f32(clamp_keep_nan(acc.y, p.clamp));
-  o[2] = Lowp<T>::from_f32(clamp_keep_nan(acc.z, p.clamp));
-  o[3] = Lowp<T>::from_f32(clamp_keep_nan(acc.w, p.clamp));
-  T* out = reinterpret_cast<T*>(F.out) + (int64_t)local * F.ldo + F.col + lane * 4;
-  *reinterpret_cast<V4*>(out) = o;
 }
 
 hipError_t launch_gather_pool(GatherParams& p, hipStream_t st) {
   int blocks = 0;
+  bool any_cached = false;
   for (int k = 0; k < p.nf; ++k) {
     p.f[k].block_begin = blocks;
     const int bags_per_block = kGatherThreads / (p.f[k].dim / 4);
     blocks += (p.f[k].nbags + bags_per_block - 1) / bags_per_block;
+    any_cached |= p.f[k].cache >= 0;
   }
   p.total_blocks = blocks;
   if (blocks == 0) return hipSuccess;
-  if (p.lowp == 0)
-    launch_k(gather_pool_kernel<f16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
-  else
-    launch_k(gather_pool_kernel<bf16>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+  if (any_cached) {
+    if (p.lowp == 0)
+      launch_k(gather_pool_kernel<f16, true>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+    else
+      launch_k(gather_pool_kernel<bf16, true>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+  } else {
+    if (p.lowp == 0)
+      launch_k(gather_pool_kernel<f16, false>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+    else
+      launch_k(gather_pool_kernel<bf16, false>, dim3(blocks), dim3(kGatherThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 

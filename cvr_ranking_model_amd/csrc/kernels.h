@@ -57,6 +57,39 @@ struct ExpandParams {
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t st);
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
 
+// ---------------------------------------------------------------- HBM hot-row cache
+// Directory of one table's cache, in caller-owned device memory (see cache_layout):
+// header (epoch, counters), tags [sets][ways] (row held or -1), stamps [sets][ways] (batch of
+// last use), first [sets] (earliest missed lookup of the current batch, INT32_MAX if none),
+// rows [sets * ways][dim] fp32.
+constexpr int kMaxCaches = 4;
+constexpr int kCacheMaxWays = 16;
+enum { CACHE_LOOKUPS = 0, CACHE_HITS, CACHE_MISSES, CACHE_ADMISSIONS, CACHE_EVICTIONS, CACHE_NCOUNTERS };
+struct CacheLayout {
+  size_t tags, stamps, first, rows, total;  // byte offsets into the state; total bytes
+};
+CacheLayout cache_layout(int64_t sets, int32_t ways, int32_t dim);
+struct CacheHeader {
+  int32_t epoch;
+  int32_t pad_[15];
+  unsigned long long counters[CACHE_NCOUNTERS];
+};
+struct GatherCache {
+  int32_t* tags;
+  int32_t* stamps;
+  int32_t* first;
+  float* rows;
+  CacheHeader* hdr;
+  int32_t sets, ways;
+};
+hipError_t launch_cache_init(const GatherCache& c, hipStream_t st);
+// Starts a batch: every attached cache's epoch advances by one.
+hipError_t launch_cache_begin(CacheHeader* const* hdrs, int n, hipStream_t st);
+// After the gather: each set that missed admits the row of its earliest missed lookup into
+// its least recently used way, copying the row from the host table.
+hipError_t launch_cache_admit(const GatherCache& c, const int32_t* ids, int64_t n_ids, const float* host_table,
+                              int64_t rows, int32_t dim, hipStream_t st);
+
 // ---------------------------------------------------------------- gather + mean-pool (A1-A2/B1)
 struct GatherFeature {
   const float* table;
@@ -69,10 +102,11 @@ struct GatherFeature {
   int32_t col;          // first output column
   float* dbg;           // fp32 pooled [nbags][dim] or null
   int32_t block_begin;  // first block of this feature in the launch
-  int32_t pad_;
+  int32_t cache;        // index into GatherParams::cache when the table sits behind an HBM cache, else -1
 };
 struct GatherParams {
   GatherFeature f[kMaxGatherFeatures];
+  GatherCache cache[kMaxCaches];
   int32_t nf;
   int32_t total_blocks;
   const int32_t* bag_offsets;

@@ -25,6 +25,7 @@ enum Stage {
   STAGE_PLE_GATE,
   STAGE_HEAD_GEMM,
   STAGE_HEAD_OUT,
+  STAGE_CACHE,
   kNumStages
 };
 constexpr int kMaxLaunchesPerCall = 64;
@@ -106,6 +107,15 @@ struct cvr_model {
   int last_debug = 0, last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0;
   cvr::Timing timing;
   cvr::GraphCache graph;
+  // HBM hot-row caches attached to host-resident tables (cvr_cache_attach)
+  struct Cache {
+    int32_t table;
+    int64_t sets;
+    int32_t ways;
+    char* state;             // caller-owned device memory, laid out by cache_layout
+    const float* host_dev;   // device-side address of the host table
+  };
+  std::vector<Cache> caches;
 };
 
 namespace cvr {

@@ -71,6 +71,10 @@ _PROTOS = {
                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "cvr_stage_name": (C.c_char_p, [C.c_void_p, C.c_int32]),
     "cvr_fill_table": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_uint64, C.c_double, C.c_void_p]),
+    "cvr_cache_state_bytes": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]),
+    "cvr_cache_attach": (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "cvr_cache_stats": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int64), C.c_void_p]),
+    "cvr_cache_export": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_void_p]),
     "cvr_last_error": (C.c_char_p, [C.c_void_p]),
     "cvr_status_string": (C.c_char_p, [C.c_int]),
     "cvr_destroy": (None, [C.c_void_p]),
@@ -149,6 +153,30 @@ def cvr_debug_export(h, what, dst_ptr, dst_bytes, stream):
     written = C.c_size_t(0)
     _check(lib().cvr_debug_export(h, what, dst_ptr, dst_bytes, C.byref(written), stream), h)
     return written.value
+
+
+def cvr_cache_state_bytes(sets, ways, dim):
+    out = C.c_size_t(0)
+    _check(lib().cvr_cache_state_bytes(sets, ways, dim, C.byref(out)))
+    return out.value
+
+
+def cvr_cache_attach(h, table, sets, ways, state_ptr, state_bytes, stream):
+    _check(lib().cvr_cache_attach(h, table, sets, ways, state_ptr, state_bytes, stream), h)
+
+
+def cvr_cache_stats(h, table, stream):
+    out = (C.c_int64 * 5)()
+    _check(lib().cvr_cache_stats(h, table, out, stream), h)
+    return list(out)
+
+
+def cvr_cache_export(h, table, entries, stream):
+    tags = np.empty(entries, np.int32)
+    stamps = np.empty(entries, np.int32)
+    _check(lib().cvr_cache_export(h, table, tags.ctypes.data_as(C.POINTER(C.c_int32)),
+                                  stamps.ctypes.data_as(C.POINTER(C.c_int32)), stream), h)
+    return tags, stamps
 
 
 def cvr_timing_begin(h, max_calls):
@@ -328,6 +356,29 @@ class Model:
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.ws
+
+    def attach_cache(self, table, sets, ways):
+        """Serve ``table`` through an HBM hot-row cache of sets x ways rows (state held here)."""
+        torch = _torch()
+        # an out-of-range table index is reported by the library's own check
+        dim = int(self.tables[table].shape[1]) if 0 <= table < len(self.tables) else 4
+        nbytes = cvr_cache_state_bytes(sets, ways, dim) if ways >= 1 and sets >= 1 else 256
+        state = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        cvr_cache_attach(self.h, table, sets, ways, C.c_void_p(state.data_ptr()), nbytes, _stream_ptr(self.stream))
+        if not hasattr(self, "caches"):
+            self.caches = {}
+        self.caches[table] = (state, sets, ways)
+
+    def cache_stats(self, table):
+        """Counters since attach: lookups, hits, misses, admissions, evictions."""
+        v = cvr_cache_stats(self.h, table, _stream_ptr(self.stream))
+        return dict(zip(["lookups", "hits", "misses", "admissions", "evictions"], v))
+
+    def cache_export(self, table):
+        """The cache directory as (tags, stamps), each [sets, ways] int32."""
+        _, sets, ways = self.caches[table]
+        tags, stamps = cvr_cache_export(self.h, table, sets * ways, _stream_ptr(self.stream))
+        return tags.reshape(sets, ways), stamps.reshape(sets, ways)
 
     def score(self, dbatch: DeviceBatch, out=None):
         torch = _torch()

@@ -236,6 +236,48 @@ cvr_status cvr_set_debug(cvr_handle h, int32_t debug);
 cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, size_t dst_bytes, size_t* written,
                             void* hip_stream);
 
+/* HBM hot-row cache over a host-resident table (CTR article section 二: hot
+ * embeddings in GPU HBM in front of host DRAM, least-recently-used
+ * replacement, hit and miss rates monitored).
+ *
+ * The table's data pointer given to cvr_create points to pinned host memory
+ * (hipHostMalloc) or to device memory.  Once a cache is attached, every
+ * scoring call looks each id of the features that read the table up in the
+ * cache: a hit reads the row from HBM, a miss reads it from the table itself
+ * (over the bus for host memory).  Pooled values are the same either way.
+ * The cache has `sets` x `ways` entries; row r belongs to set fmix32(r) mod
+ * sets (fmix32 = MurmurHash3's 32-bit finaliser).  Time is counted in scoring
+ * calls: call t stamps every way it hits with t, and all its lookups see the
+ * cache as it was when the call began.  After its lookups, each set that
+ * missed admits one row, that of its earliest missed lookup (smallest
+ * position in batch.ids), into its least recently used way: an empty way
+ * first, then the smallest stamp, ties to the lowest way.  Counters since
+ * attach: lookups, hits, misses (lookups = hits + misses; ids outside the
+ * table are not counted), admissions, evictions (admissions that replaced a
+ * row).
+ *
+ * cvr_cache_state_bytes: device bytes of one cache's state (directory and
+ * rows) for the given shape and the table's dim.
+ * cvr_cache_attach: serve `table` (index into cvr_create's tables; it must
+ * feed at least one feature and no sequence column) through a cache whose
+ * state lives in `state` (device memory of at least cvr_cache_state_bytes,
+ * 256-byte aligned, caller-owned, kept alive until cvr_destroy).  1 <= ways <=
+ * min(16, dim/4), 1 <= sets, sets * ways < 2^31; at most 4 caches per model;
+ * a table takes one cache.  Initialises the state (empty, counters zero) on
+ * hip_stream.  Scoring calls enqueued afterwards use it; a graph captured by
+ * cvr_score_graph before the attach is discarded.
+ * cvr_cache_stats: waits for hip_stream and writes the five counters
+ * (lookups, hits, misses, admissions, evictions) to counters[0..4] (host).
+ * cvr_cache_export: waits for hip_stream and copies the directory to host
+ * arrays of sets * ways int32: tags (row held, -1 if empty) and stamps (call
+ * of last use; 0 for a way never filled).
+ * Calls that overlap on one model race on its caches. */
+cvr_status cvr_cache_state_bytes(int64_t sets, int32_t ways, int32_t dim, size_t* bytes);
+cvr_status cvr_cache_attach(cvr_handle h, int32_t table, int64_t sets, int32_t ways, void* state,
+                            size_t state_bytes, void* hip_stream);
+cvr_status cvr_cache_stats(cvr_handle h, int32_t table, int64_t* counters, void* hip_stream);
+cvr_status cvr_cache_export(cvr_handle h, int32_t table, int32_t* tags, int32_t* stamps, void* hip_stream);
+
 /* Per-stage kernel timing with HIP events recorded on the scoring stream.
  * cvr_timing_begin arms up to max_calls subsequent cvr_score calls;
  * cvr_timing_end waits for them and writes, per stage, the summed

@@ -93,3 +93,12 @@ def test_fill_and_create_argument_checks():
         cv.cvr_create(s, tabs, len(spec["tables"]), None, 0, None, 0, None)
     assert e.value.status == cv.CVR_ERR_ARG
     assert cv.lib().cvr_status_string(cv.CVR_ERR_RANGE).decode().startswith("id or offset")
+
+
+def test_cache_state_bytes_host_checks():
+    small = cv.cvr_cache_state_bytes(16, 4, 32)
+    assert small >= 16 * 4 * 32 * 4 and small % 256 == 0          # at least the cached rows
+    assert cv.cvr_cache_state_bytes(32, 4, 32) > small
+    for sets, ways, dim in [(0, 4, 32), (16, 0, 32), (16, 17, 64), (16, 4, 30), (1 << 30, 4, 32)]:
+        with pytest.raises(cv.CvrError):
+            cv.cvr_cache_state_bytes(sets, ways, dim)
