@@ -140,6 +140,12 @@ def main():
     ap.add_argument("--candidates", type=int, default=None,
                     help="candidates per request (CVR: 1 user + C candidates sharing its sequences)")
     ap.add_argument("--variant", default="bench")
+    ap.add_argument("--cache", action="store_true",
+                    help="DLRM: keep the ID tables in pinned host memory behind HBM hot-row caches "
+                         "(CTR article section 二) and cycle through --cache-batches distinct batches")
+    ap.add_argument("--cache-gb", type=float, default=5.0, help="HBM given to the caches (the article's L0: ~5 GB)")
+    ap.add_argument("--cache-ways", type=int, default=8)
+    ap.add_argument("--cache-batches", type=int, default=16)
     ap.add_argument("--ple-task-experts", default=None,
                     help="CVR: experts each task's gate mixes, tasks separated by '/', e.g. 0,2/1,2 "
                          "(PLE with one task-specific expert per task and a shared one)")
@@ -167,17 +173,46 @@ def main():
         spec["ple_task_experts"] = [[int(e) for e in t.split(",")] for t in args.ple_task_experts.split("/")]
     print(f"[bench] workload {args.workload}: filling tables", file=sys.stderr, flush=True)
     tables = cv.device_tables(spec, args.variant)
+    cached = []
+    if args.cache:
+        if spec["model"] != "dlrm":
+            sys.exit("--cache applies to the DLRM workloads")
+        # the single-id ID tables go to host memory; the HBM budget is split by table size
+        cached = sorted({f["table"] for f in spec["features"] if f["name"] in ("user_id", "item_id")})
+        for t in cached:
+            h = torch.empty(tables[t].shape, dtype=torch.float32, pin_memory=True)
+            h.copy_(tables[t])
+            tables[t] = h
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     weights = synth.make_weights(spec, args.variant)
     model = cv.Model(spec, tables, weights)
-    batch = synth.make_batch(spec, requests=args.batch, candidates=args.candidates, uniform_ids=args.uniform_ids)
-    db = cv.DeviceBatch(batch)
+    cache_cfg = {}
+    if cached:
+        total = sum(spec["tables"][t]["rows"] * spec["tables"][t]["dim"] * 4 for t in cached)
+        budget = args.cache_gb * 1e9
+        for t in cached:
+            rows, dim = spec["tables"][t]["rows"], spec["tables"][t]["dim"]
+            share = budget * rows * dim * 4 / total
+            sets = max(1, int(min(rows, share / (dim * 4)) // args.cache_ways))
+            model.attach_cache(t, sets, args.cache_ways)
+            cache_cfg[spec["tables"][t]["name"]] = {"sets": sets, "ways": args.cache_ways,
+                                                    "hbm_GB": round(sets * args.cache_ways * dim * 4 / 1e9, 3),
+                                                    "table_GB": round(rows * dim * 4 / 1e9, 3)}
+    nb = args.cache_batches if cached else 1
+    batches = [synth.make_batch(spec, requests=args.batch, candidates=args.candidates, uniform_ids=args.uniform_ids,
+                                seed_offset=i) for i in range(nb)]
+    batch = batches[0]
+    dbs = [cv.DeviceBatch(b) for b in batches]
+    db = dbs[0]
     n = db.n_candidates
     out = torch.empty(n * model.n_tasks, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     print(f"[bench] {n} candidates per step; warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        model.score(db, out)
+    for i in range(max(args.warmup, nb if cached else 0)):
+        model.score(dbs[i % nb], out)
     assert model.sync_status() == cv.CVR_OK
+    stats0 = {t: model.cache_stats(t) for t in cached}
     graph_dt = None
     if args.graph:
         for _ in range(max(1, args.warmup)):
@@ -192,11 +227,15 @@ def main():
     model.timing_begin(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        model.score(db, out)
+    for i in range(args.steps):
+        model.score(dbs[i % nb], out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     stages, calls = model.timing_end()
+    for t in cached:
+        st1, st0 = model.cache_stats(t), stats0[t]
+        d = {k: st1[k] - st0[k] for k in st1}
+        cache_cfg[spec["tables"][t]["name"]].update(d, hit_rate=round(d["hits"] / max(d["lookups"], 1), 4))
     assert model.sync_status() == cv.CVR_OK
     eager_dt = dt
     if graph_dt is not None:
@@ -212,7 +251,8 @@ def main():
     value = n * args.steps / dt
 
     # per-stage rooflines from the live event timings; the dominant stage gives "roofline"
-    work = stage_work(spec, batch)
+    works = [stage_work(spec, b) for b in batches]
+    work = {k: (v[0], sum(w[k][1] for w in works) / len(works)) for k, v in works[0].items()}
     peak_f = MFMA_PEAK_TFLOPS[spec["lowp"]]
     table = {}
     for st, (ms, launches) in stages.items():
@@ -259,7 +299,8 @@ def main():
         "data": f"synthetic ({args.variant} variant: seeded hash tables, Zipf ids, Glorot weights)",
         "config": dict({"workload": WORKLOAD_TEXT[args.workload], "candidates_per_step": n,
                         "requests_per_step": db.n_requests},
-                       **({"ple_task_experts": spec["ple_task_experts"]} if args.ple_task_experts else {})),
+                       **({"ple_task_experts": spec["ple_task_experts"]} if args.ple_task_experts else {}),
+                       **({"hot_row_cache": cache_cfg, "distinct_batches": nb} if cached else {})),
         "roofline": roof,
         "stages": table,
         "ids": "uniform" if args.uniform_ids else "zipf",

@@ -437,6 +437,7 @@ static GatherCache gather_cache(const cvr_model::Cache& c, int32_t dim) {
   g.tags = (int32_t*)(c.state + l.tags);
   g.stamps = (int32_t*)(c.state + l.stamps);
   g.first = (int32_t*)(c.state + l.first);
+  g.queue = (int32_t*)(c.state + l.queue);
   g.rows = (float*)(c.state + l.rows);
   g.sets = (int32_t)c.sets;
   g.ways = c.ways;
@@ -513,7 +514,7 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
     const cvr_model::Cache& mc = m->caches[c];
     e = L(STAGE_CACHE, [&] {
       return launch_cache_admit(gp.cache[c], b->ids, b->n_ids, mc.host_dev, m->tables[mc.table].rows,
-                                m->tables[mc.table].dim, s);
+                                m->tables[mc.table].dim, b->n_ids, s);
     });
     if (e != hipSuccess) return e;
   }
@@ -792,12 +793,16 @@ extern "C" cvr_status cvr_cache_stats(cvr_handle h, int32_t table, int64_t* coun
   if (!h || !counters) return fail(h, CVR_ERR_ARG, "null argument");
   const cvr_model::Cache* c = find_cache(h, table);
   if (!c) return fail(h, CVR_ERR_ARG, "table has no cache");
-  unsigned long long v[CACHE_NCOUNTERS];
+  unsigned long long v[CACHE_NCOUNTERS][kCacheCounterSlots];
   hipStream_t s = (hipStream_t)hip_stream;
   hipError_t e = hipMemcpyAsync(v, ((CacheHeader*)c->state)->counters, sizeof(v), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("cache stats: ") + hipGetErrorString(e));
-  for (int i = 0; i < CACHE_NCOUNTERS; ++i) counters[i] = (int64_t)v[i];
+  for (int i = 0; i < CACHE_NCOUNTERS; ++i) {
+    unsigned long long sum = 0;
+    for (int k = 0; k < kCacheCounterSlots; ++k) sum += v[i][k];
+    counters[i] = (int64_t)sum;
+  }
   return CVR_OK;
 }
 

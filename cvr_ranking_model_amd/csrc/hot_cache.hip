@@ -25,7 +25,8 @@ CacheLayout cache_layout(int64_t sets, int32_t ways, int32_t dim) {
   l.tags = align256(sizeof(CacheHeader));
   l.stamps = align256(l.tags + entries * 4);
   l.first = align256(l.stamps + entries * 4);
-  l.rows = align256(l.first + (size_t)sets * 4);
+  l.queue = align256(l.first + (size_t)sets * 4);
+  l.rows = align256(l.queue + (size_t)sets * 4);
   l.total = align256(l.rows + entries * dim * 4);
   return l;
 }
@@ -38,8 +39,13 @@ __global__ __launch_bounds__(256) void cache_init_kernel(const GatherCache c) {
     c.stamps[i] = 0;
   }
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < c.sets; i += stride) c.first[i] = INT32_MAX;
-  if (blockIdx.x == 0 && threadIdx.x < CACHE_NCOUNTERS) c.hdr->counters[threadIdx.x] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) c.hdr->epoch = 0;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < CACHE_NCOUNTERS * kCacheCounterSlots; i += blockDim.x)
+      (&c.hdr->counters[0][0])[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    c.hdr->epoch = 0;
+    c.hdr->queued = 0;
+  }
 }
 
 hipError_t launch_cache_init(const GatherCache& c, hipStream_t st) {
@@ -55,7 +61,10 @@ struct CacheBeginArgs {
 };
 
 __global__ void cache_begin_kernel(const CacheBeginArgs a) {
-  if ((int)threadIdx.x < a.n) a.hdr[threadIdx.x]->epoch += 1;
+  if ((int)threadIdx.x < a.n) {
+    a.hdr[threadIdx.x]->epoch += 1;
+    a.hdr[threadIdx.x]->queued = 0;
+  }
 }
 
 hipError_t launch_cache_begin(CacheHeader* const* hdrs, int n, hipStream_t st) {
@@ -68,16 +77,21 @@ hipError_t launch_cache_begin(CacheHeader* const* hdrs, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
-// One group of dim/4 lanes per set: every lane reads the set's directory and picks the same
-// victim way; each lane copies four floats of the admitted row; lane 0 updates the directory.
+// One group of dim/4 lanes per queued set (the gather queued each set that missed once):
+// every lane reads the set's directory and picks the same victim way; each lane copies four
+// floats of the admitted row; lane 0 updates the directory.  Groups stride over the queue.
 __global__ __launch_bounds__(256) void cache_admit_kernel(const GatherCache c, const int32_t* __restrict__ ids,
                                                           int64_t n_ids, const float* __restrict__ host,
                                                           int64_t rows, int32_t dim) {
   const int lpb = dim >> 2;
-  const int64_t s = (int64_t)blockIdx.x * (256 / lpb) + (int)threadIdx.x / lpb;
+  const int gpb = 256 / lpb;
   const int lane = (int)threadIdx.x % lpb;
+  const int queued = min(c.hdr->queued, c.sets);
   uint32_t adm = 0, ev = 0;
-  if (s < c.sets) {
+#pragma unroll 1
+  for (int q = blockIdx.x * gpb + (int)threadIdx.x / lpb; q < queued; q += gridDim.x * gpb) {
+    const int64_t s = c.queue[q];
+    if (s < 0 || s >= c.sets) continue;
     const int32_t j = c.first[s];
     // A position is only ever offered for an id inside the table; the checks keep a slot left
     // over from an interrupted call from reading outside the arrays.
@@ -106,8 +120,8 @@ __global__ __launch_bounds__(256) void cache_admit_kernel(const GatherCache c, c
       if (lane == 0) {
         c.tags[base + victim] = row;
         c.stamps[base + victim] = c.hdr->epoch;
-        adm = 1;
-        ev = evict ? 1 : 0;
+        adm += 1;
+        ev += evict ? 1 : 0;
       }
     }
     if (j != INT32_MAX && lane == 0) c.first[s] = INT32_MAX;
@@ -126,16 +140,18 @@ __global__ __launch_bounds__(256) void cache_admit_kernel(const GatherCache c, c
   if (threadIdx.x == 0) {
     const uint32_t a = red[0][0] + red[0][1] + red[0][2] + red[0][3];
     const uint32_t e = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    if (a) atomicAdd(&c.hdr->counters[CACHE_ADMISSIONS], (unsigned long long)a);
-    if (e) atomicAdd(&c.hdr->counters[CACHE_EVICTIONS], (unsigned long long)e);
+    const int slot = blockIdx.x % kCacheCounterSlots;
+    if (a) atomicAdd(&c.hdr->counters[CACHE_ADMISSIONS][slot], (unsigned long long)a);
+    if (e) atomicAdd(&c.hdr->counters[CACHE_EVICTIONS][slot], (unsigned long long)e);
   }
 }
 
 hipError_t launch_cache_admit(const GatherCache& c, const int32_t* ids, int64_t n_ids, const float* host_table,
-                              int64_t rows, int32_t dim, hipStream_t st) {
+                              int64_t rows, int32_t dim, int64_t max_lookups, hipStream_t st) {
   if (dim < 4 || dim % 4 || dim > 256 || c.sets <= 0) return hipErrorInvalidValue;
   const int per_block = 256 / (dim / 4);
-  const int64_t blocks = ((int64_t)c.sets + per_block - 1) / per_block;
+  const int64_t most = std::max<int64_t>(1, std::min<int64_t>(c.sets, max_lookups));
+  const int64_t blocks = std::min<int64_t>(2048, (most + per_block - 1) / per_block);
   launch_k(cache_admit_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, ids, n_ids, host_table, rows, dim);
   return hipGetLastError();
 }

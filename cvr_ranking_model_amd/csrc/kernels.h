@@ -59,36 +59,43 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- HBM hot-row cache
 // Directory of one table's cache, in caller-owned device memory (see cache_layout):
-// header (epoch, counters), tags [sets][ways] (row held or -1), stamps [sets][ways] (batch of
-// last use), first [sets] (earliest missed lookup of the current batch, INT32_MAX if none),
-// rows [sets * ways][dim] fp32.
+// header (epoch, queue length, counters), tags [sets][ways] (row held or -1), stamps
+// [sets][ways] (batch of last use), first [sets] (earliest missed lookup of the current batch,
+// INT32_MAX if none), queue [sets] (sets that missed in the current batch), rows
+// [sets * ways][dim] fp32.
 constexpr int kMaxCaches = 4;
 constexpr int kCacheMaxWays = 16;
 enum { CACHE_LOOKUPS = 0, CACHE_HITS, CACHE_MISSES, CACHE_ADMISSIONS, CACHE_EVICTIONS, CACHE_NCOUNTERS };
 struct CacheLayout {
-  size_t tags, stamps, first, rows, total;  // byte offsets into the state; total bytes
+  size_t tags, stamps, first, queue, rows, total;  // byte offsets into the state; total bytes
 };
 CacheLayout cache_layout(int64_t sets, int32_t ways, int32_t dim);
+// Each counter is spread over kCacheCounterSlots addresses (block b adds to slot b mod slots)
+// so that thousands of blocks do not queue on one atomic; readers sum the slots.
+constexpr int kCacheCounterSlots = 64;
 struct CacheHeader {
   int32_t epoch;
-  int32_t pad_[15];
-  unsigned long long counters[CACHE_NCOUNTERS];
+  int32_t queued;       // sets in the admission queue of the current batch
+  int32_t pad_[14];
+  unsigned long long counters[CACHE_NCOUNTERS][kCacheCounterSlots];
 };
 struct GatherCache {
   int32_t* tags;
   int32_t* stamps;
   int32_t* first;
+  int32_t* queue;       // [sets]: the sets that missed in the current batch, each once
   float* rows;
   CacheHeader* hdr;
   int32_t sets, ways;
 };
 hipError_t launch_cache_init(const GatherCache& c, hipStream_t st);
-// Starts a batch: every attached cache's epoch advances by one.
+// Starts a batch: every attached cache's epoch advances by one and its queue empties.
 hipError_t launch_cache_begin(CacheHeader* const* hdrs, int n, hipStream_t st);
 // After the gather: each set that missed admits the row of its earliest missed lookup into
 // its least recently used way, copying the row from the host table.
+// max_lookups bounds the queue length (the batch's ids) and sizes the grid.
 hipError_t launch_cache_admit(const GatherCache& c, const int32_t* ids, int64_t n_ids, const float* host_table,
-                              int64_t rows, int32_t dim, hipStream_t st);
+                              int64_t rows, int32_t dim, int64_t max_lookups, hipStream_t st);
 
 // ---------------------------------------------------------------- gather + mean-pool (A1-A2/B1)
 struct GatherFeature {
