@@ -11,7 +11,8 @@
 // exponentials, weighted sum) in fp32; states are merged in a fixed butterfly order across
 // lane groups and then wave by wave, so the result is bitwise reproducible.  The output is
 // written in fp32 as token N+s of the token matrix.  A single pass reads each encoded state
-// once.
+// once.  Multiply-adds are written as explicit fmaf so that the rounding of every step is
+// fixed by the source rather than by the compiler's contraction choices.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -25,9 +26,9 @@ __device__ __forceinline__ void merge_state(SoftState& a, const SoftState& b) {
   const float m = fmaxf(a.m, b.m);
   if (m == -INFINITY) return;  // both empty
   const float ea = expf(a.m - m), eb = expf(b.m - m);
-  a.l = a.l * ea + b.l * eb;
+  a.l = fmaf(a.l, ea, b.l * eb);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) a.o[j] = a.o[j] * ea + b.o[j] * eb;
+  for (int j = 0; j < 16; ++j) a.o[j] = fmaf(a.o[j], ea, b.o[j] * eb);
   a.m = m;
 }
 
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
     }
     float d = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) d += h[j] * q[j];
+    for (int j = 0; j < 16; ++j) d = fmaf(h[j], q[j], d);
     d += __shfl_xor(d, 1);
     d += __shfl_xor(d, 2);
     d += __shfl_xor(d, 4);
@@ -87,9 +88,9 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
     const float mn = fmaxf(st.m, sc);
     const float alpha = expf(st.m - mn);
     const float pe = expf(sc - mn);
-    st.l = st.l * alpha + pe;
+    st.l = fmaf(st.l, alpha, pe);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) st.o[j] = st.o[j] * alpha + pe * h[j];
+    for (int j = 0; j < 16; ++j) st.o[j] = fmaf(pe, h[j], st.o[j] * alpha);
     st.m = mn;
   }
   // merge the 8 position groups of the wave (lanes differing in bits 3..5)
