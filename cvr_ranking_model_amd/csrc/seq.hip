@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   typedef bf16x8 V8;
   __shared__ __align__(16) bf16 Es[2][kM * kEPitch];
   __shared__ __align__(16) bf16 As[2][kM * kAPitch];
-  __shared__ __align__(16) float Bs[4][3 * 64];          // producer w: gate bias, up bias, -log2(e) * gate bias
+  __shared__ __align__(16) float Bs[4][2 * 64];          // producer w: gate bias, up bias
   __shared__ __align__(16) bf16 Hs[2][kM * kEPitch];     // finished H tile of a chunk
   __shared__ __align__(16) float Cs[2][kD];              // its pool partials
   __shared__ int2 Ds[2];                                  // descriptor of the producers' next chunk
@@ -167,15 +167,23 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
           const float bg = bgu[0], bu = bgu[kHid];
           bs[lane] = bg;
           bs[64 + lane] = bu;
-          bs[128 + lane] = -1.4426950408889634f * bg;
           cur_s = s;
         }
         const int b = i & 1;
+        // The accumulators start at the biases (gate tiles 0-1, up tiles 2-3): element v of tile
+        // j is hidden unit (j & 1) * 32 + 8 * (v / 4) + 4 * (lane / 32) + v % 4.
         f32x16 acc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const float4 bb = *reinterpret_cast<const float4*>(
+                &bs[(j < 2 ? 0 : 64) + (j & 1) * 32 + 8 * v4 + 4 * (lane >> 5)]);
+            acc[j][4 * v4] = bb.x;
+            acc[j][4 * v4 + 1] = bb.y;
+            acc[j][4 * v4 + 2] = bb.z;
+            acc[j][4 * v4 + 3] = bb.w;
+          }
 #pragma unroll
         for (int k = 0; k < kD / 16; ++k) {
           const V8 e = *reinterpret_cast<const V8*>(&Es[b][lr * kEPitch + k * 16 + lk]);
@@ -184,25 +192,19 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         }
         // The tiles are hidden units x positions: lane holds units 8*v4 + 4*(lane/32) .. +3 of
         // each tile for position lane%32, so SiLU(gate) * up of 4 units leaves as 8 bytes.
-        // exp(-g) = exp2(-log2(e) * acc - log2(e) * b_gate): the bias folds into one FMA.
+        // exp(-g) = exp2(-log2(e) * g); g and up already hold their biases.
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
             const int h = j * 32 + 8 * v4 + 4 * (lane >> 5);
-            const float4 bg4 = *reinterpret_cast<const float4*>(&bs[h]);
-            const float4 bu4 = *reinterpret_cast<const float4*>(&bs[64 + h]);
-            const float4 cg4 = *reinterpret_cast<const float4*>(&bs[128 + h]);
-            const float bgv[4] = {bg4.x, bg4.y, bg4.z, bg4.w};
-            const float buv[4] = {bu4.x, bu4.y, bu4.z, bu4.w};
-            const float cgv[4] = {cg4.x, cg4.y, cg4.z, cg4.w};
             bf16x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float ag = acc[j][4 * v4 + q], au = acc[j + 2][4 * v4 + q];
-              const float e2 = __builtin_amdgcn_exp2f(fmaf(ag, -1.4426950408889634f, cgv[q]));
+              const float g = acc[j][4 * v4 + q], u = acc[j + 2][4 * v4 + q];
+              const float e2 = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
               const float r = __builtin_amdgcn_rcpf(1.0f + e2);
-              o[q] = (bf16)(((ag + bgv[q]) * (au + buv[q])) * r);
+              o[q] = (bf16)((g * u) * r);
             }
             *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + h]) = o;
           }
