@@ -8,8 +8,9 @@
 //   per layer l:
 //     query GEMM (grouped over sequences) <- rows 0..N-1 of `cur` and the pooled mean (B6)
 //     attention                           -> rows N..N+S-1 of `cur`                     (B7)
-//     mixer fc1 (grouped over mixed tokens) reads the Split layout of `cur` in place,
-//     mixer fc2 writes Y + FFN in the Revert layout into the other buffer               (B8)
+//     token mixer: one fused kernel for 16 tokens x 128 (heads of 8, FFN 128-256-128) reads
+//     the Split layout of `cur` and writes Y + FFN in the Revert layout into the other
+//     buffer; other shapes take mixer fc1 / fc2 as grouped GEMMs with the same addressing (B8)
 //     the other buffer becomes `cur`: its rows 0..N-1 are the next layer's tokens       (B9)
 //   expert GEMM, gates + mixture, head fc1 GEMM, head output + sigmoid                  (B10-B11)
 #include <hip/hip_runtime.h>
@@ -160,51 +161,72 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       if (e != hipSuccess) return e;
     }
     const int mw = T * d / H;  // mixed-token width; one 8-wide chunk per token
-    {
-      GemmParams g{};
-      g.M = n;
-      g.N = mh;
-      g.K = mw;
-      g.groups = H;
-      g.nseg = 1;
-      // Split: mixed token h, element t*8 + j = token t, column h*8 + j
-      g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, d / H, mw, d, 0, 1};
-      g.W = m->wptr(Lp + ".mix.0.fc1.weight");
-      g.w_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.weight"; }, H, 2);
-      g.bias = (const float*)m->wptr(Lp + ".mix.0.fc1.bias");
-      g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.bias"; }, H, 4);
-      if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
-      g.C = ws + w.mixhid;
-      g.ldc = mh;
-      g.c_gstride = (int64_t)n * mh;
-      g.c_nstride8 = 8;
-      g.relu = 1;
-      e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
+    if (token_mix_supported(T, d, H, mh)) {
+      TokenMixParams t{};
+      t.Y = (const float*)tok[cur];
+      t.Z = (float*)tok[1 - cur];
+      t.n = n;
+      t.T = T;
+      t.d = d;
+      t.H = H;
+      t.W1 = (const __bf16*)m->wptr(Lp + ".mix.0.fc1.weight");
+      t.w1_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.weight"; }, H, 2);
+      t.b1 = (const float*)m->wptr(Lp + ".mix.0.fc1.bias");
+      t.b1_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.bias"; }, H, 4);
+      t.W2 = (const __bf16*)m->wptr(Lp + ".mix.0.fc2.weight");
+      t.w2_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.weight"; }, H, 2);
+      t.b2 = (const float*)m->wptr(Lp + ".mix.0.fc2.bias");
+      t.b2_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.bias"; }, H, 4);
+      if (t.w1_gstride < 0 || t.b1_gstride < 0 || t.w2_gstride < 0 || t.b2_gstride < 0) return hipErrorInvalidValue;
+      e = L(STAGE_MIXER_GEMM, [&] { return launch_token_mix(t, s); });
       if (e != hipSuccess) return e;
-    }
-    {
-      GemmParams g{};
-      g.M = n;
-      g.N = mw;
-      g.K = mh;
-      g.groups = H;
-      g.nseg = 1;
-      g.seg[0] = ASeg{ws + w.mixhid, nullptr, mh, (int64_t)n * mh, mh, 8, 0, 0};
-      g.W = m->wptr(Lp + ".mix.0.fc2.weight");
-      g.w_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.weight"; }, H, 2);
-      g.bias = (const float*)m->wptr(Lp + ".mix.0.fc2.bias");
-      g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.bias"; }, H, 4);
-      if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
-      // Revert + residual: output element t*8 + j of mixed token h lands on token t, column h*8 + j
-      g.C = tok[1 - cur];
-      g.R = tok[cur];
-      g.ldc = (int64_t)T * d;
-      g.c_nstride8 = d;
-      g.c_gstride = d / H;
-      g.out_f32 = 1;
-      g.r_f32 = 1;
-      e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
-      if (e != hipSuccess) return e;
+    } else {
+      {
+        GemmParams g{};
+        g.M = n;
+        g.N = mh;
+        g.K = mw;
+        g.groups = H;
+        g.nseg = 1;
+        // Split: mixed token h, element t*8 + j = token t, column h*8 + j
+        g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, d / H, mw, d, 0, 1};
+        g.W = m->wptr(Lp + ".mix.0.fc1.weight");
+        g.w_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.weight"; }, H, 2);
+        g.bias = (const float*)m->wptr(Lp + ".mix.0.fc1.bias");
+        g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc1.bias"; }, H, 4);
+        if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
+        g.C = ws + w.mixhid;
+        g.ldc = mh;
+        g.c_gstride = (int64_t)n * mh;
+        g.c_nstride8 = 8;
+        g.relu = 1;
+        e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
+        if (e != hipSuccess) return e;
+      }
+      {
+        GemmParams g{};
+        g.M = n;
+        g.N = mw;
+        g.K = mh;
+        g.groups = H;
+        g.nseg = 1;
+        g.seg[0] = ASeg{ws + w.mixhid, nullptr, mh, (int64_t)n * mh, mh, 8, 0, 0};
+        g.W = m->wptr(Lp + ".mix.0.fc2.weight");
+        g.w_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.weight"; }, H, 2);
+        g.bias = (const float*)m->wptr(Lp + ".mix.0.fc2.bias");
+        g.bias_gstride = group_stride(m, [&](int i) { return Lp + ".mix." + S_(i) + ".fc2.bias"; }, H, 4);
+        if (g.w_gstride < 0 || g.bias_gstride < 0) return hipErrorInvalidValue;
+        // Revert + residual: output element t*8 + j of mixed token h lands on token t, column h*8 + j
+        g.C = tok[1 - cur];
+        g.R = tok[cur];
+        g.ldc = (int64_t)T * d;
+        g.c_nstride8 = d;
+        g.c_gstride = d / H;
+        g.out_f32 = 1;
+        g.r_f32 = 1;
+        e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
+        if (e != hipSuccess) return e;
+      }
     }
     m->last_attn_tok = cur;
     cur = 1 - cur;

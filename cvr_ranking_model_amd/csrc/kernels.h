@@ -223,6 +223,25 @@ struct AttnParams {
 };
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
 
+// ---------------------------------------------------------------- fused token mixer (B8)
+// Z = Y + Revert(FFN_h(Mix_h(Y))) for all heads h in one launch (16 tokens x 128, heads of 8,
+// FFN 128 -> 256 -> 128); other shapes take the two grouped GEMMs.
+struct TokenMixParams {
+  const float* Y;               // [n][T][d] fp32
+  float* Z;                     // [n][T][d] fp32
+  int32_t n, T, d, H;
+  const __bf16* W1;             // head h: W1 + h*w1_gstride, [256][T*8]
+  int64_t w1_gstride;
+  const float* b1;
+  int64_t b1_gstride;
+  const __bf16* W2;             // head h: W2 + h*w2_gstride, [T*8][256]
+  int64_t w2_gstride;
+  const float* b2;
+  int64_t b2_gstride;
+};
+bool token_mix_supported(int32_t T, int32_t d, int32_t H, int32_t hidden);
+hipError_t launch_token_mix(const TokenMixParams& p, hipStream_t st);
+
 // ---------------------------------------------------------------- PLE gates and heads (B10-B11)
 struct PleGateParams {
   const float* Z;               // [n][zdim] (rounded to bf16 as the gates' Linear input)
