@@ -126,6 +126,15 @@ def test_c3_task_specific_experts(task_experts):
     check_cvr(spec, m, synth.make_batch(spec, requests=16), "stress")
 
 
+def test_mixer_gemm_path():
+    """A mixer hidden width the fused token-mix kernel does not take (128) runs the two grouped
+    GEMMs with Split/Revert addressing instead; both layers against the oracle."""
+    spec = dict(synth.load_spec("c4"), mixer_hidden=128)
+    banner("c4 shapes with mixer hidden 128 (grouped-GEMM mixer), 6 samples, stress")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec, requests=6), "stress")
+
+
 def test_c3_full_sampled():
     spec = synth.load_spec("c3")
     banner("c3 full: 512 samples, oracle on samples 0, 200, 511")
