@@ -160,10 +160,18 @@ static void plan_weights(cvr_model* m) {
       for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc2.bias", mw, 1, false);
     }
     const int zd = T * d;
+    // Expert rows, then every task's gate rows, back to back: one GEMM computes the experts and
+    // the gate logits.  Its bias vector is the internal entry "_ple.bias" (expert biases, then
+    // gate biases), assembled from the given biases at create time.
+    int gates = 0;
     for (int e = 0; e < s.n_experts; ++e) add("ple.expert." + std::to_string(e) + ".weight", s.expert_dim, zd, true);
+    for (int k = 0; k < s.n_tasks; ++k) {
+      add("ple.gate." + std::to_string(k) + ".weight", __builtin_popcount(m->task_mask[k]), zd, true);
+      gates += __builtin_popcount(m->task_mask[k]);
+    }
     for (int e = 0; e < s.n_experts; ++e) add("ple.expert." + std::to_string(e) + ".bias", s.expert_dim, 1, false);
-    for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".weight", __builtin_popcount(m->task_mask[k]), zd, true);
     for (int k = 0; k < s.n_tasks; ++k) add("ple.gate." + std::to_string(k) + ".bias", __builtin_popcount(m->task_mask[k]), 1, false);
+    add("_ple.bias", (int64_t)s.n_experts * s.expert_dim + gates, 1, false);
     for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc1.weight", s.head_hidden, s.expert_dim, true);
     for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc1.bias", s.head_hidden, 1, false);
     for (int k = 0; k < s.n_tasks; ++k) add("head." + std::to_string(k) + ".fc2.weight", 1, s.head_hidden, true);
@@ -270,7 +278,20 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
     if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("packing weights: ") + hipGetErrorString(he)); }
   }
   for (size_t i = 0; i < seen.size(); ++i)
-    if (!seen[i]) { std::string n = m->w[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "missing weight " + n); }
+    if (!seen[i] && m->w[i].name[0] != '_') { std::string n = m->w[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "missing weight " + n); }
+  if (m->spec.model == CVR_MODEL_HYFORMER) {
+    // the expert GEMM's bias vector: expert biases, then the gate biases task by task
+    char* dst = m->arena + m->w[m->widx.at("_ple.bias")].off;
+    std::vector<std::string> parts;
+    for (int e = 0; e < m->spec.n_experts; ++e) parts.push_back("ple.expert." + std::to_string(e) + ".bias");
+    for (int k = 0; k < m->spec.n_tasks; ++k) parts.push_back("ple.gate." + std::to_string(k) + ".bias");
+    for (const std::string& name : parts) {
+      const WEntry& e = m->w[m->widx.at(name)];
+      hipError_t he = hipMemcpyAsync(dst, m->arena + e.off, (size_t)e.rows * 4, hipMemcpyDeviceToDevice, s);
+      if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("packing biases: ") + hipGetErrorString(he)); }
+      dst += (size_t)e.rows * 4;
+    }
+  }
   hipError_t he = hipStreamSynchronize(s);
   if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("create sync: ") + hipGetErrorString(he)); }
   if (const char* pr = getenv("CVR_DLRM_PASS_ROWS")) m->pass_rows = std::max(0ll, atoll(pr));  // tuning override
@@ -333,7 +354,7 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     w.seq_pool = take((size_t)S * R * d * 4);
     w.query = take((size_t)S * n * d * 4);
     w.mixhid = take((size_t)s.mixer_heads * n * s.mixer_hidden * lp);
-    w.experts = take((size_t)n * s.n_experts * s.expert_dim * 4);
+    w.experts = take((size_t)n * ((s.n_experts * s.expert_dim + s.n_tasks * s.n_experts + 31) / 32 * 32) * 4);
     w.gates = take((size_t)n * s.n_tasks * s.n_experts * 4);
     w.task_in = take((size_t)s.n_tasks * n * s.expert_dim * lp);
     w.head_hid = take((size_t)s.n_tasks * n * s.head_hidden * lp);

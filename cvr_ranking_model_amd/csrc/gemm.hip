@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             float x = acc[i][j][v] + bn;
-            if (p.relu) x = x > 0.f ? x : 0.f;
+            if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
             st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * OP + nl] = x;
           }
         }
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             float x = acc[i][j][v] + bn;
-            if (p.relu) x = x > 0.f ? x : 0.f;
+            if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
             st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * OP + nl] = Lowp<T>::from_f32(x);
           }
         }
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         float x = acc[i][j][v] + bn;
         if (p.R) x += p.r_f32 ? reinterpret_cast<const float*>(p.R)[addr]
                               : Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[addr]);
-        if (p.relu) x = x > 0.f ? x : 0.f;
+        if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
         if (p.out_f32)
           reinterpret_cast<float*>(p.C)[addr] = x;
         else
@@ -655,6 +655,7 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   const char* env = getenv("CVR_GEMM_TILE");
   int tile = env ? atoi(env) : 0;
   const bool big_ok = !AF32 && !p.out_f32 && p.N % 128 == 0 && p.N <= kBigMaxN && p.c_nstride8 == 8 && !p.R &&
+                      p.relu_end == 0 &&
                       (p.ldc & 7) == 0 && (p.c_gstride & 7) == 0;
   if (tile == 256 && !big_ok) tile = 0;
   if (!tile) {

@@ -233,42 +233,55 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   }
   m->last_tok = cur;
 
-  // ---- B10: experts over the flattened token matrix, then gates and mixture
+  // ---- B10: experts and gate logits over the flattened token matrix in one GEMM (the gate
+  // rows follow the expert rows in the arena; ReLU on the expert columns only), then the gate
+  // softmax and mixture
+  int gates = 0;
+  int goff[kMaxTasks];
+  for (int k = 0; k < K; ++k) {
+    goff[k] = gates;
+    gates += __builtin_popcount(m->task_mask[k]);
+  }
+  const int64_t ld = ((int64_t)E * ed + gates + 31) / 32 * 32;  // rows stay 128-byte aligned
   {
     GemmParams g{};
     g.M = n;
-    g.N = E * ed;
+    g.N = E * ed + gates;
     g.K = T * d;
     g.groups = 1;
     g.nseg = 1;
     g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, T * d, 8, 0, 1};
     g.W = m->wptr("ple.expert.0.weight");
-    g.bias = (const float*)m->wptr("ple.expert.0.bias");
-    if (group_stride(m, [](int i) { return "ple.expert." + S_(i) + ".weight"; }, E, 2) != (int64_t)ed * T * d ||
-        group_stride(m, [](int i) { return "ple.expert." + S_(i) + ".bias"; }, E, 4) != ed)
+    g.bias = (const float*)m->wptr("_ple.bias");
+    // the rows must be contiguous: experts back to back, then the gates task by task
+    const char* w0 = (const char*)m->wptr("ple.expert.0.weight");
+    if (group_stride(m, [](int i) { return "ple.expert." + S_(i) + ".weight"; }, E, 2) != (int64_t)ed * T * d)
       return hipErrorInvalidValue;
+    for (int k = 0; k < K; ++k)
+      if ((const char*)m->wptr("ple.gate." + S_(k) + ".weight") != w0 + ((int64_t)E * ed + goff[k]) * T * d * 2)
+        return hipErrorInvalidValue;
     g.C = ws + w.experts;
-    g.ldc = (int64_t)E * ed;
+    g.ldc = ld;
     g.c_nstride8 = 8;
     g.relu = 1;
+    g.relu_end = E * ed;
     g.out_f32 = 1;
     e = L(STAGE_PLE_GEMM, [&] { return launch_gemm(g, lowp, s); });
     if (e != hipSuccess) return e;
   }
   {
     PleGateParams p{};
-    p.Z = (const float*)tok[cur];
+    p.experts = (const float*)(ws + w.experts);
+    p.ld = ld;
     p.n = n;
-    p.zdim = T * d;
-    for (int k = 0; k < K; ++k) {
-      p.wg[k] = (const __bf16*)m->wptr("ple.gate." + S_(k) + ".weight");
-      p.bg[k] = (const float*)m->wptr("ple.gate." + S_(k) + ".bias");
-      p.emask[k] = m->task_mask[k];
-    }
     p.E = E;
     p.K = K;
-    p.experts = (const float*)(ws + w.experts);
     p.edim = ed;
+    p.gate0 = E * ed;
+    for (int k = 0; k < K; ++k) {
+      p.goff[k] = goff[k];
+      p.emask[k] = m->task_mask[k];
+    }
     p.task_in = (__bf16*)(ws + w.task_in);
     e = L(STAGE_PLE_GATE, [&] { return launch_ple_gate(p, s); });
     if (e != hipSuccess) return e;

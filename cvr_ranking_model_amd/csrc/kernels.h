@@ -159,6 +159,7 @@ struct GemmParams {
   int32_t c_nstride8;
   const void* R;        // residual (same addressing as C) or null
   int32_t relu;
+  int32_t relu_end;     // with relu: only columns n < relu_end (0: all columns)
   int32_t out_f32;      // 1: C is fp32, else the low-precision type
   int32_t r_f32;        // 1: R is fp32, else the low-precision type
 };
@@ -244,14 +245,13 @@ hipError_t launch_token_mix(const TokenMixParams& p, hipStream_t st);
 
 // ---------------------------------------------------------------- PLE gates and heads (B10-B11)
 struct PleGateParams {
-  const float* Z;               // [n][zdim] (rounded to bf16 as the gates' Linear input)
-  int32_t n, zdim;
-  const __bf16* wg[kMaxTasks];  // task k: one row of zdim per expert it mixes, in expert order
-  const float* bg[kMaxTasks];   // task k: one bias per expert it mixes
+  // Row c of the expert GEMM output (row stride ld): the E expert outputs [E][edim] (after
+  // ReLU), then the gate logits of every task, task k's at columns gate0 + goff[k] ...
+  const float* experts;
+  int64_t ld;
+  int32_t n, E, K, edim, gate0;
+  int32_t goff[kMaxTasks];
   int32_t emask[kMaxTasks];     // task k mixes expert e iff bit e is set
-  int32_t E, K;
-  const float* experts;         // [n][E*edim]
-  int32_t edim;
   __bf16* task_in;              // [K][n][edim]
 };
 hipError_t launch_ple_gate(const PleGateParams& p, hipStream_t st);

@@ -5,12 +5,12 @@
 // fully-connected layers with a nonlinearity.  The expert Linear+ReLU and the first head
 // Linear+ReLU run as MFMA GEMMs; this file holds the two small pieces between and after:
 //
-// ple_gate_kernel (one wave per candidate): the per-task gate logits W_g z + b_g over the
-//   flattened token matrix z (rounded to bf16 as a Linear input; fp32 dot products with a
-//   fixed-order wave reduction), a softmax in fp32 over the experts the task mixes (all of
-//   them when the experts are shared; its own plus the shared ones for PLE with
-//   task-specific experts), and the gated mixture t_k = sum_e g_ke h_e of those experts'
-//   fp32 outputs, rounded to bf16 (it is the input of the head's first Linear).
+// ple_gate_kernel (one wave per candidate): the gate logits W_g z + b_g come from the expert
+//   GEMM (the gate rows sit after the expert rows, so one MFMA pass over z yields both); this
+//   kernel takes a softmax in fp32 over the experts each task mixes (all of them when the
+//   experts are shared; its own plus the shared ones for PLE with task-specific experts) and
+//   forms the gated mixture t_k = sum_e g_ke h_e of those experts' fp32 outputs, rounded to
+//   bf16 (it is the input of the head's first Linear).
 // head_out_kernel (one thread per candidate and task): y = w2 . u + b2 with fp32
 //   accumulation and the fp32 sigmoid; writes out[c * n_tasks + k].
 #include "device_common.h"
@@ -22,39 +22,21 @@ __global__ __launch_bounds__(256) void ple_gate_kernel(const PleGateParams p) {
   const int c = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   if (c >= p.n) return;
-  const float* z = p.Z + (int64_t)c * p.zdim;
-  // logit[k * E + e] for the experts task k mixes; the others take no part.
-  float logit[kMaxTasks * kMaxExperts];
-#pragma unroll 1
-  for (int k = 0; k < p.K; ++k) {
-    int row = 0;
-#pragma unroll 1
-    for (int e = 0; e < p.E; ++e) {
-      if (!((p.emask[k] >> e) & 1)) continue;
-      const bf16* w = p.wg[k] + (int64_t)row * p.zdim;
-      float acc = 0.f;
-      for (int j = lane * 8; j < p.zdim; j += 512) {
-        const float4 z0 = *reinterpret_cast<const float4*>(z + j);
-        const float4 z1 = *reinterpret_cast<const float4*>(z + j + 4);
-        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        const bf16x8 wv = *reinterpret_cast<const bf16x8*>(w + j);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += (float)(bf16)zv[u] * (float)wv[u];
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      logit[k * p.E + e] = acc + p.bg[k][row];
-      ++row;
-    }
-  }
+  const float* row = p.experts + (int64_t)c * p.ld;
   for (int k = 0; k < p.K; ++k) {
     const int mask = p.emask[k];
+    const float* lg = row + p.gate0 + p.goff[k];  // one logit per expert the task mixes
+    float logit[kMaxExperts];
     float mx = -INFINITY;
+    int r = 0;
     for (int e = 0; e < p.E; ++e)
-      if ((mask >> e) & 1) mx = fmaxf(mx, logit[k * p.E + e]);
+      if ((mask >> e) & 1) {
+        logit[e] = lg[r++];
+        mx = fmaxf(mx, logit[e]);
+      }
     float g[kMaxExperts], sum = 0.f;
     for (int e = 0; e < p.E; ++e) {
-      g[e] = (mask >> e) & 1 ? expf(logit[k * p.E + e] - mx) : 0.f;
+      g[e] = (mask >> e) & 1 ? expf(logit[e] - mx) : 0.f;
       sum += g[e];
     }
     const float inv = 1.0f / sum;
@@ -62,7 +44,7 @@ __global__ __launch_bounds__(256) void ple_gate_kernel(const PleGateParams p) {
     for (int j = lane; j < p.edim; j += 64) {
       float t = 0.f;
       for (int e = 0; e < p.E; ++e)
-        if ((mask >> e) & 1) t += g[e] * p.experts[(int64_t)c * p.E * p.edim + e * p.edim + j];
+        if ((mask >> e) & 1) t += g[e] * row[e * p.edim + j];
       p.task_in[((int64_t)k * p.n + c) * p.edim + j] = (bf16)t;
     }
   }

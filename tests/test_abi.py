@@ -57,6 +57,10 @@ def test_arena_size_matches_weight_shapes():
         for wname, shape in synth.weight_shapes(spec).items():
             n = int(np.prod(shape))
             want += ((n * (2 if wname.endswith(".weight") else 4)) + 255) // 256 * 256
+        if spec["model"] == "hyformer":
+            # one internal fp32 bias vector for the expert GEMM: expert biases, then gate biases
+            gates = spec["n_tasks"] * spec["n_experts"]
+            want += ((spec["n_experts"] * spec["expert_dim"] + gates) * 4 + 255) // 256 * 256
         assert nbytes == want, name
 
 
