@@ -123,3 +123,24 @@ def test_attach_errors():
         m.attach_cache(0, 4, 2)            # already cached
     with pytest.raises(cv.CvrError):
         m.cache_stats(1)                   # not cached
+
+
+def test_cvr_model_with_cached_table():
+    """The CVR model reads a cached non-sequence table through the same gather; a
+    sequence-column table cannot take a cache."""
+    spec = synth.load_spec("c3")
+    dev = cv.device_tables(spec, "stress")
+    t0 = spec["features"][0]["table"]
+    host = list(dev)
+    host[t0] = pinned(dev[t0])
+    banner(f"c3 stress: non-sequence table {t0} in host memory behind a 4096 x 4 cache; 3 calls")
+    m, _ = build_model(spec, "stress", tables=host, debug=False)
+    ref, _ = build_model(spec, "stress", tables=dev, debug=False)
+    m.attach_cache(t0, 4096, 4)
+    sims = {t0: oc.HotRowCache(4096, 4)}
+    for call in range(3):
+        b = synth.make_batch(spec, requests=16, seed_offset=call % 2)
+        check_call(m, ref, spec, b, sims, f"call {call}")
+    seq_table = spec["seq"]["columns"][0]["table"]
+    with pytest.raises(cv.CvrError):
+        m.attach_cache(seq_table, 64, 2)
