@@ -13,6 +13,8 @@
 // written in fp32 as token N+s of the token matrix.  A single pass reads each encoded state
 // once.  Multiply-adds are written as explicit fmaf so that the rounding of every step is
 // fixed by the source rather than by the compiler's contraction choices.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -126,9 +128,214 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------- many candidates per request
+// When a request carries many candidates, their queries share the request's keys and values,
+// so attention over one sequence is two dense products per request and runs on MFMA:
+//   S^T = H Q^T / tau  (positions x candidates),  O^T = H^T softmax(S)^T  (dims x candidates).
+// One block per (tile of 32 consecutive candidates, sequence): its four waves take every fourth
+// block of 32 of the request's positions (loading the next one while computing), each with an
+// online softmax (fp32 state per candidate, the candidate's lane keeps it), and the four
+// states are merged in wave order at the end.
+// Queries are split into a bf16 high part and a bf16 remainder, and so are the softmax
+// weights, so both products keep about 16 bits of the fp32 operand (the encoded states are
+// bf16 already).  A tile that straddles requests takes one pass per request, with the other
+// candidates' columns masked.
+//
+// MFMA 32x32x16 layouts: lane l holds A[l%32][8(l/32)..+7] and B[8(l/32)..+7][l%32]; result
+// element v sits at row 8(v/4) + 4(l/32) + v%4, column l%32.  In S^T a lane therefore holds 16
+// positions of candidate l%32 (the other 16 are in lane l^32), and the weights it feeds as the
+// B operand of the value product cover the positions of k-step kk in the order
+// 16kk + 8(i/4) + 4(l/32) + i%4, i = 0..7 -- the states are stored transposed in LDS in that
+// order (slot = position with bits 2 and 3 swapped).
+constexpr int kMqPitch = 32 + 8;  // bf16 per transposed row: 16-byte reads of 16 rows hit distinct banks
+
+__global__ __launch_bounds__(256) void attention_mq_kernel(const AttnParams p) {
+  __shared__ __align__(16) bf16 Ht[4][128 * kMqPitch];
+  __shared__ float Ms[3][2][32];        // waves 1-3: running max and sum per candidate
+  __shared__ float4 Os[3][16][64];      // waves 1-3: weighted sums, in the lanes' own layout
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ntiles = (p.n + 31) / 32;
+  const int task = blockIdx.x;
+  const int s = p.S - 1 - task / ntiles;  // longest sequences first
+  const int c0 = (task % ntiles) * 32;
+  const int lr = lane & 31, hf = lane >> 5, h8 = hf * 8;
+  const bool cvalid = c0 + lr < p.n;
+  const int cl = cvalid ? c0 + lr : p.n - 1;
+  const int myreq = p.cand_req[cl];
+  bf16* ht = Ht[wave];
+
+  // B operand of S^T: Q[candidate lr][16k + 8(l/32) .. +7], as high and remainder parts
+  bf16x8 qh[8], ql[8];
+  {
+    const float* qrow = p.q + ((int64_t)s * p.n + cl) * 128;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qrow + 16 * k + h8);
+      const float4 x1 = *reinterpret_cast<const float4*>(qrow + 16 * k + h8 + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qh[k][i] = (bf16)xs[i];
+        ql[k][i] = (bf16)(xs[i] - (float)qh[k][i]);
+      }
+    }
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int slot = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);  // this lane's position -> LDS slot
+
+  // One block of 32 positions starting at t0 (rows already in hv).
+  auto block = [&](const bf16x8 (&hv)[8], int64_t t0, int64_t e, bool active) {
+    f32x16 sc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sc = Lowp<bf16>::mfma32(hv[k], qh[k], sc);
+      sc = Lowp<bf16>::mfma32(hv[k], ql[k], sc);
+    }
+    // transposed copy of the block for the value product
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ht[(16 * k + h8 + i) * kMqPitch + slot] = hv[k][i];
+    // online softmax for candidate lr over the block's positions
+    float x[16];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t pos = t0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+      x[v] = active && pos < e ? sc[v] * p.inv_tau : -INFINITY;
+      bm = fmaxf(bm, x[v]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float alpha = mn == -INFINITY ? 1.f : expf(m - mn);
+    float pv[16], ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      pv[v] = x[v] == -INFINITY ? 0.f : expf(x[v] - mn);
+      ps += pv[v];
+    }
+    ps += __shfl_xor(ps, 32);
+    l = fmaf(l, alpha, ps);
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+    // O^T += H^T P^T: A = transposed states (dims x slots), B = weights (slots x candidates)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ph[i] = (bf16)pv[8 * kk + i];
+        pl[i] = (bf16)(pv[8 * kk + i] - (float)ph[i]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&ht[(32 * dt + lr) * kMqPitch + 16 * kk + h8]);
+        acc[dt] = Lowp<bf16>::mfma32(av, ph, acc[dt]);
+        acc[dt] = Lowp<bf16>::mfma32(av, pl, acc[dt]);
+      }
+    }
+  };
+  // A operand rows: the state row of position t0 + lr (past the end: the last row, masked)
+  auto load = [&](bf16x8 (&hv)[8], int64_t t0, int64_t e) {
+    const int64_t tr = t0 + lr < e ? t0 + lr : e - 1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) hv[k] = *reinterpret_cast<const bf16x8*>(p.H + tr * 128 + 16 * k + h8);
+  };
+
+  const int r_first = p.cand_req[c0], r_last = p.cand_req[min(c0 + 31, p.n - 1)];
+#pragma unroll 1
+  for (int r = r_first; r <= r_last; ++r) {
+    const bool active = cvalid && myreq == r;
+    if (!__any(active)) continue;
+    int64_t a = p.seq_offsets[(int64_t)s * (p.R + 1) + r], e = p.seq_offsets[(int64_t)s * (p.R + 1) + r + 1];
+    a = a < 0 ? 0 : (a > p.n_positions ? p.n_positions : a);
+    e = e < a ? a : (e > p.n_positions ? p.n_positions : e);
+    // the waves take every fourth block of 32 positions; each loads its next block early
+    int64_t t0 = a + 32 * wave;
+    if (t0 >= e) continue;
+    bf16x8 hv[8], hn[8];
+    load(hv, t0, e);
+#pragma unroll 1
+    while (true) {
+      const int64_t tn = t0 + 128;
+      if (tn < e) load(hn, tn, e);
+      block(hv, t0, e, active);
+      if (tn >= e) break;
+      t0 = tn;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hv[k] = hn[k];
+    }
+  }
+  // merge the waves' states in wave order
+  if (wave > 0) {
+    if (lane < 32) {
+      Ms[wave - 1][0][lr] = m;
+      Ms[wave - 1][1][lr] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        Os[wave - 1][4 * dt + v4][lane] =
+            make_float4(acc[dt][4 * v4], acc[dt][4 * v4 + 1], acc[dt][4 * v4 + 2], acc[dt][4 * v4 + 3]);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 0; w < 3; ++w) {
+    const float mw = Ms[w][0][lr], lw = Ms[w][1][lr];
+    const float mn = fmaxf(m, mw);
+    if (mn == -INFINITY) continue;
+    const float a0 = expf(m - mn), aw = expf(mw - mn);
+    l = fmaf(l, a0, lw * aw);
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const float4 o = Os[w][4 * dt + v4][lane];
+        acc[dt][4 * v4] = fmaf(acc[dt][4 * v4], a0, o.x * aw);
+        acc[dt][4 * v4 + 1] = fmaf(acc[dt][4 * v4 + 1], a0, o.y * aw);
+        acc[dt][4 * v4 + 2] = fmaf(acc[dt][4 * v4 + 2], a0, o.z * aw);
+        acc[dt][4 * v4 + 3] = fmaf(acc[dt][4 * v4 + 3], a0, o.w * aw);
+      }
+  }
+  if (cvalid) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float* out = p.Y + ((int64_t)(c0 + lr) * p.T + p.N + s) * 128;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        *reinterpret_cast<float4*>(out + 32 * dt + 8 * v4 + 4 * hf) =
+            make_float4(acc[dt][4 * v4] * inv, acc[dt][4 * v4 + 1] * inv, acc[dt][4 * v4 + 2] * inv,
+                        acc[dt][4 * v4 + 3] * inv);
+  }
+}
+
+bool attention_many_candidates(int32_t n, int32_t R) {
+  if (const char* e = getenv("CVR_ATTN_MQ")) return atoi(e) != 0;
+  return (int64_t)n >= 16 * (int64_t)R;
+}
+
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
   if (p.n <= 0 || p.S <= 0) return hipSuccess;
-  launch_k(attention_kernel, dim3(p.n, p.S), dim3(256), 0, st, p);
+  if (attention_many_candidates(p.n, p.R)) {
+    const int64_t tasks = (int64_t)((p.n + 31) / 32) * p.S;
+    launch_k(attention_mq_kernel, dim3((unsigned)tasks), dim3(256), 0, st, p);
+  } else {
+    launch_k(attention_kernel, dim3(p.n, p.S), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

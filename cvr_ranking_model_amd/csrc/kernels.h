@@ -223,6 +223,9 @@ struct AttnParams {
   int32_t T, N;
 };
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
+// The MFMA form is used when requests carry 16 or more candidates on average (CVR_ATTN_MQ=0/1
+// overrides).
+bool attention_many_candidates(int32_t n, int32_t R);
 
 // ---------------------------------------------------------------- fused token mixer (B8)
 // Z = Y + Revert(FFN_h(Mix_h(Y))) for all heads h in one launch (16 tokens x 128, heads of 8,

@@ -163,6 +163,23 @@ def test_one_user_many_candidates():
     check_cvr(spec, m, synth.make_batch(spec, requests=2, candidates=500), "stress", requests=[1])
 
 
+@pytest.mark.parametrize("counts", [[40, 0, 70, 3, 33, 1, 64], [5, 7, 2, 9, 4, 6, 3, 8, 1, 11]])
+def test_attention_mfma_path_ragged(monkeypatch, counts):
+    """The MFMA attention (queries of a request batched against its states) on ragged
+    requests: tiles of 32 candidates straddling requests, empty requests, empty and
+    one-position sequences, many small requests in one tile.  Against the oracle."""
+    monkeypatch.setenv("CVR_ATTN_MQ", "1")
+    spec = synth.load_spec("c3")
+    R = len(counts)
+    rng = np.random.default_rng(len(counts))
+    lens = [[int(x) for x in rng.integers(0, L + 1, R)] for L in spec["seq"]["lengths"]]
+    lens[0][0], lens[1][2], lens[2][4] = 0, 1, 0
+    banner(f"c3 stress, MFMA attention forced, candidates per request {counts}")
+    m, _ = build_model(spec, "stress")
+    b = synth.make_batch(spec, cand_counts=counts, seq_lengths=lens)
+    check_cvr(spec, m, b, "stress")
+
+
 def test_ragged_multi_candidate():
     spec = synth.load_spec("c3")
     banner("c3 ragged: several candidates per request, empty and length-1 sequences, empty bags")
