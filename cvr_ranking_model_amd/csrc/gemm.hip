@@ -645,8 +645,10 @@ static int big_grid(int tiles, int per_cu) {
 
 // Tile choice: the persistent wide-layer kernel when its layout requirements hold and there is
 // at least a tile per CU (256 x 256 tiles when N allows, else 256 x 128); otherwise 128x128
-// (64-wide slices when every K-segment boundary allows, else 32-wide); 64x64 when even 128x128
-// cannot cover the chip (the per-candidate GEMMs of the CVR model at small batch).
+// (64-wide slices when every K-segment boundary allows, else 32-wide) when its tiles keep at
+// least three quarters of the CUs busy (measured: the CVR expert GEMM, 224 tiles of K = 2048,
+// runs 36 us against 58 us as 64x64); 64x64 below that (the per-candidate GEMMs of the CVR
+// model at small batch).
 template <typename T, bool AF32>
 static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
@@ -660,7 +662,7 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   if (tile == 256 && !big_ok) tile = 0;
   if (!tile) {
     if (big_ok && (int64_t)tiles(256, 128) * p.groups >= 256) tile = 256;
-    else if ((int64_t)tiles(128, 128) * p.groups >= 256) tile = 128;
+    else if ((int64_t)tiles(128, 128) * p.groups >= 192) tile = 128;  // 3/4 of the CUs busy beats 4x the tiles
     else tile = 64;
   }
   const dim3 blk(256);
