@@ -113,6 +113,12 @@ static void derive(cvr_model* m) {
     else m->segs.push_back({item, k + dim, m->fcol[f]});
     k += dim;
   }
+  m->tok_split = s.model == CVR_MODEL_HYFORMER && m->D_req > 0 && m->D_item > 0;
+  int kb = 0;
+  for (const InputSeg& sg : m->segs) {
+    if ((sg.k_end - kb) % 32) m->tok_split = false;
+    kb = sg.k_end;
+  }
 }
 
 // Weight arena plan.  Entries listed together are placed back to back so that grouped GEMMs
@@ -141,6 +147,11 @@ static void plan_weights(cvr_model* m) {
     const int mw = T * d / s.mixer_heads;
     add("tok.weight", (int64_t)N * d, m->e_dim, true);
     add("tok.bias", (int64_t)N * d, 1, false);
+    if (m->tok_split) {
+      // the tokenizer's request-side and item-side columns as matrices of their own
+      add("_tok.req.weight", (int64_t)N * d, m->D_req, true);
+      add("_tok.item.weight", (int64_t)N * d, m->D_item, true);
+    }
     for (int q = 0; q < S; ++q) {
       // gate and up back to back: one [2*hs][d] matrix per sequence
       add("seq." + std::to_string(q) + ".gate.weight", hs, d, true);
@@ -279,6 +290,24 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
   }
   for (size_t i = 0; i < seen.size(); ++i)
     if (!seen[i] && m->w[i].name[0] != '_') { std::string n = m->w[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "missing weight " + n); }
+  if (m->tok_split) {
+    // column runs of the packed tokenizer weight into its request-side and item-side halves
+    const WEntry& wt = m->w[m->widx.at("tok.weight")];
+    const WEntry& wr = m->w[m->widx.at("_tok.req.weight")];
+    const WEntry& wi = m->w[m->widx.at("_tok.item.weight")];
+    int kb = 0, creq = 0, citem = 0;
+    for (const InputSeg& sg : m->segs) {
+      const int width = sg.k_end - kb;
+      const WEntry& dst = sg.item ? wi : wr;
+      int& c = sg.item ? citem : creq;
+      hipError_t he = hipMemcpy2DAsync(m->arena + dst.off + (size_t)c * 2, (size_t)dst.cols * 2,
+                                       m->arena + wt.off + (size_t)kb * 2, (size_t)wt.cols * 2, (size_t)width * 2,
+                                       (size_t)wt.rows, hipMemcpyDeviceToDevice, s);
+      if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("splitting tokenizer: ") + hipGetErrorString(he)); }
+      c += width;
+      kb = sg.k_end;
+    }
+  }
   if (m->spec.model == CVR_MODEL_HYFORMER) {
     // the expert GEMM's bias vector: expert biases, then the gate biases task by task
     char* dst = m->arena + m->w[m->widx.at("_ple.bias")].off;
@@ -347,6 +376,7 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     const int64_t d = s.d, S = s.n_seq, T = s.n_tokens + s.n_seq;
     w.tok[0] = take((size_t)n * T * d * 4);
     w.tok[1] = take((size_t)n * T * d * 4);
+    w.tok_req = take((size_t)R * s.n_tokens * d * 4);
     w.hseq = take((size_t)P * d * lp);
     w.chunk_off = take((size_t)(S * R + 1) * 4);
     w.pool_part = take((size_t)(P / kSeqChunk + S * R + 1) * d * 4);

@@ -219,7 +219,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   const float* bias = p.bias ? p.bias + (int64_t)g * p.bias_gstride : nullptr;
   constexpr bool kCanStageF32 = 4 * 32 * (WTN + 8) * 4 <= kSmemElems * (int)sizeof(T);
   constexpr bool kCanStageLp = 4 * 32 * (WTN + 8) * (int)sizeof(T) <= kSmemElems * (int)sizeof(T);
-  if ((p.out_f32 ? kCanStageF32 : kCanStageLp) && p.c_nstride8 == 8 && !p.R && (p.ldc & 7) == 0) {
+  // an fp32 residual (no ReLU to follow it) is added on the way out of the staging area
+  const bool stage_r = !p.R || (p.out_f32 && p.r_f32 && !p.relu && (!p.r_rowmap || (p.r_ld & 3) == 0));
+  if ((p.out_f32 ? kCanStageF32 : kCanStageLp) && p.c_nstride8 == 8 && stage_r && (p.ldc & 7) == 0) {
     // Contiguous output rows: stage each wave's tile 32 rows at a time through LDS (free after
     // the K loop) and write it back as 16-byte row segments.  Every thread runs the same number
     // of rounds, so the block barriers below are uniform.
@@ -248,15 +250,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
           const int m = m0 + wm * WTM + i * 32 + rl;
           const int n = n0 + wn * WTN + cc * 4;
           if (m < p.M && n < p.N) {
-            const float4 v = *reinterpret_cast<const float4*>(&st[rl * OP + cc * 4]);
-            float* dst = reinterpret_cast<float*>(p.C) + (int64_t)g * p.c_gstride + (int64_t)m * p.ldc + n;
+            float4 v = *reinterpret_cast<const float4*>(&st[rl * OP + cc * 4]);
+            const int64_t off = (int64_t)g * p.c_gstride + (int64_t)m * p.ldc + n;
+            float* dst = reinterpret_cast<float*>(p.C) + off;
+            const float* res = p.R ? reinterpret_cast<const float*>(p.R) +
+                                         (p.r_rowmap ? (int64_t)p.r_rowmap[m] * p.r_ld + n : off)
+                                   : nullptr;
             if (n + 4 <= p.N) {
+              if (res) {
+                const float4 r4 = *reinterpret_cast<const float4*>(res);
+                v.x += r4.x;
+                v.y += r4.y;
+                v.z += r4.z;
+                v.w += r4.w;
+              }
               *reinterpret_cast<float4*>(dst) = v;
             } else {
               const int cnt = p.N - n;
-              dst[0] = v.x;
-              if (cnt > 1) dst[1] = v.y;
-              if (cnt > 2) dst[2] = v.z;
+              dst[0] = res ? v.x + res[0] : v.x;
+              if (cnt > 1) dst[1] = res ? v.y + res[1] : v.y;
+              if (cnt > 2) dst[2] = res ? v.z + res[2] : v.z;
             }
           }
         }
@@ -315,9 +328,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m >= p.M) continue;
         const int64_t addr = (int64_t)m * p.ldc + ncol;
+        const int64_t raddr = p.r_rowmap ? (int64_t)p.r_rowmap[m] * p.r_ld + ncol : addr;
         float x = acc[i][j][v] + bn;
-        if (p.R) x += p.r_f32 ? reinterpret_cast<const float*>(p.R)[addr]
-                              : Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[addr]);
+        if (p.R) x += p.r_f32 ? reinterpret_cast<const float*>(p.R)[raddr]
+                              : Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[raddr]);
         if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
         if (p.out_f32)
           reinterpret_cast<float*>(p.C)[addr] = x;

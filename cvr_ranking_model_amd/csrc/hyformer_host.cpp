@@ -15,6 +15,8 @@
 //   expert GEMM, gates + mixture, head fc1 GEMM, head output + sigmoid                  (B10-B11)
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include <string>
 
 #include "kernels.h"
@@ -47,8 +49,12 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   int32_t* flag = (int32_t*)(ws + w.flag);
   hipError_t e;
 
-  // ---- B2: tokenization, X = E W_tok^T + b into token rows 0..N-1
-  {
+  // ---- B2: tokenization, X = E W_tok^T + b into token rows 0..N-1.  When requests carry several
+  // candidates, the request-side columns are multiplied once per request (U = E_req W_req^T)
+  // and every candidate adds its request's row of U to its item-side product.
+  bool share = m->tok_split && (int64_t)n >= 4 * (int64_t)R;
+  if (const char* ev = getenv("CVR_TOK_SHARE")) share = m->tok_split && atoi(ev) != 0;
+  if (!share) {
     GemmParams g{};
     g.M = n;
     g.N = N * d;
@@ -68,6 +74,38 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     g.out_f32 = 1;
     e = L(STAGE_TOKENIZE_GEMM, [&] { return launch_gemm(g, lowp, s); });
     if (e != hipSuccess) return e;
+  } else {
+    for (int side = 0; side < 2; ++side) {  // 0: request side (M = R), 1: item side (M = n)
+      const bool item = side == 1;
+      GemmParams g{};
+      g.M = item ? n : R;
+      g.N = N * d;
+      g.K = item ? m->D_item : m->D_req;
+      g.groups = 1;
+      int kb = 0, k = 0;
+      for (const InputSeg& sg : m->segs) {
+        if (sg.item == item) {
+          k += sg.k_end - kb;
+          g.seg[g.nseg++] = ASeg{ws + (item ? w.x_item : w.x_req), nullptr,
+                                 (int64_t)(item ? m->ld_item : m->ld_req), 0, k, 8, sg.col0, 0};
+        }
+        kb = sg.k_end;
+      }
+      g.W = m->wptr(item ? "_tok.item.weight" : "_tok.req.weight");
+      g.C = item ? tok[0] : ws + w.tok_req;
+      g.ldc = item ? (int64_t)T * d : (int64_t)N * d;
+      g.c_nstride8 = 8;
+      g.out_f32 = 1;
+      if (item) {
+        g.bias = (const float*)m->wptr("tok.bias");
+        g.R = ws + w.tok_req;
+        g.r_f32 = 1;
+        g.r_rowmap = cand_req;
+        g.r_ld = (int64_t)N * d;
+      }
+      e = L(STAGE_TOKENIZE_GEMM, [&] { return launch_gemm(g, lowp, s); });
+      if (e != hipSuccess) return e;
+    }
   }
 
   // ---- B3-B5: sequence encoding and mean pools (per request)

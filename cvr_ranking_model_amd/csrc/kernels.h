@@ -158,6 +158,8 @@ struct GemmParams {
   int64_t c_gstride;
   int32_t c_nstride8;
   const void* R;        // residual (same addressing as C) or null
+  const int32_t* r_rowmap;  // if set: the residual of row m is row r_rowmap[m] of R, rows r_ld apart
+  int64_t r_ld;
   int32_t relu;
   int32_t relu_end;     // with relu: only columns n < relu_end (0: all columns)
   int32_t out_f32;      // 1: C is fp32, else the low-precision type

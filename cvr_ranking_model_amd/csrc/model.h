@@ -51,7 +51,7 @@ struct WsPlan {
   size_t flag = 0, cand_req = 0, x_req = 0, x_item = 0, logits = 0, pooled = 0, pooled_bytes = 0;
   size_t h[2] = {0, 0};
   size_t tok[2] = {0, 0}, hseq = 0, chunk_off = 0, chunk_desc = 0, pool_part = 0, seq_pool = 0, query = 0,
-         mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0;
+         mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0, tok_req = 0;
   size_t total = 0;
 };
 
@@ -91,6 +91,9 @@ struct cvr_model {
   std::vector<int> fcol;
   int D_req = 0, D_item = 0, ld_req = 0, ld_item = 0, e_dim = 0;
   std::vector<cvr::InputSeg> segs;
+  // CVR: the tokenizer split into its request-side and item-side columns (both present and every
+  // run a multiple of 32 wide), so requests with many candidates tokenize their own columns once
+  bool tok_split = false;
   // weights
   std::vector<cvr::WEntry> w;
   std::map<std::string, int> widx;

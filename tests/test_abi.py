@@ -61,6 +61,21 @@ def test_arena_size_matches_weight_shapes():
             # one internal fp32 bias vector for the expert GEMM: expert biases, then gate biases
             gates = spec["n_tasks"] * spec["n_experts"]
             want += ((spec["n_experts"] * spec["expert_dim"] + gates) * 4 + 255) // 256 * 256
+            # the tokenizer's request-side and item-side columns as two more matrices
+            dims = [spec["tables"][f["table"]]["dim"] for f in spec["features"]]
+            item = [f["side"] == "item" for f in spec["features"]]
+            runs, prev = [], None
+            for dmn, it in zip(dims, item):
+                if prev is not None and it == prev:
+                    runs[-1] += dmn
+                else:
+                    runs.append(dmn)
+                prev = it
+            d_item = sum(dmn for dmn, it in zip(dims, item) if it)
+            d_req = sum(dims) - d_item
+            if d_req and d_item and all(r % 32 == 0 for r in runs):
+                rows = spec["n_tokens"] * spec["d"]
+                want += (rows * d_req * 2 + 255) // 256 * 256 + (rows * d_item * 2 + 255) // 256 * 256
         assert nbytes == want, name
 
 

@@ -180,6 +180,18 @@ def test_attention_mfma_path_ragged(monkeypatch, counts):
     check_cvr(spec, m, b, "stress")
 
 
+@pytest.mark.parametrize("share", ["0", "1"])
+def test_tokenizer_request_side_once(monkeypatch, share):
+    """Tokenization with the request-side columns multiplied once per request (forced on and
+    off) on ragged requests with empty ones: tokens and scores against the oracle."""
+    monkeypatch.setenv("CVR_TOK_SHARE", share)
+    spec = synth.load_spec("c3")
+    banner(f"c3 stress, request-side tokenizer block once per request = {share}")
+    m, _ = build_model(spec, "stress")
+    b = synth.make_batch(spec, cand_counts=[7, 0, 40, 1, 3])
+    check_cvr(spec, m, b, "stress")
+
+
 def test_ragged_multi_candidate():
     spec = synth.load_spec("c3")
     banner("c3 ragged: several candidates per request, empty and length-1 sequences, empty bags")
