@@ -416,11 +416,14 @@ void Timing::reset() {
   calls = 0;
   max_calls = 0;
   launch_in_call = 0;
+  mask = 0;
 }
 
-extern "C" cvr_status cvr_timing_begin(cvr_handle h, int32_t max_calls) {
+extern "C" cvr_status cvr_timing_begin(cvr_handle h, int32_t max_calls, uint32_t stage_mask) {
   if (!h || max_calls <= 0 || max_calls > 100000) return fail(h, CVR_ERR_ARG, "bad timing request");
+  if (stage_mask >> kNumStages) return fail(h, CVR_ERR_ARG, "timing mask names an unknown stage");
   h->timing.reset();
+  h->timing.mask = stage_mask;
   h->timing.ev.resize((size_t)max_calls * kMaxLaunchesPerCall * 2);
   h->timing.stage.assign((size_t)max_calls * kMaxLaunchesPerCall, -1);
   for (auto& e : h->timing.ev)

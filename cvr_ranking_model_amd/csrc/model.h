@@ -74,6 +74,7 @@ struct Timing {
   int max_calls = 0;
   int calls = 0;
   int launch_in_call = 0;
+  uint32_t mask = 0;            // stages that carry events (bit per stage); 0 = every stage
   std::vector<hipEvent_t> ev;   // [call][launch][begin,end]
   std::vector<int> stage;       // [call][launch], -1 = unused
   void reset();
@@ -143,7 +144,8 @@ struct Launcher {
   }
   template <typename F>
   hipError_t operator()(int stage, F&& fn) {
-    const bool rec = slot_base >= 0 && li < kMaxLaunchesPerCall;
+    const uint32_t mask = m->timing.mask;
+    const bool rec = slot_base >= 0 && li < kMaxLaunchesPerCall && (mask == 0 || ((mask >> stage) & 1u));
     const size_t slot = (size_t)slot_base + li;
     LaunchTiming& lt = launch_timing();
     if (rec) {

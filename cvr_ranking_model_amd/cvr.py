@@ -66,7 +66,7 @@ _PROTOS = {
     "cvr_sync_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "cvr_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
     "cvr_debug_export": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t), C.c_void_p]),
-    "cvr_timing_begin": (C.c_int, [C.c_void_p, C.c_int32]),
+    "cvr_timing_begin": (C.c_int, [C.c_void_p, C.c_int32, C.c_uint32]),
     "cvr_timing_end": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int32), C.c_int32,
                                  C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "cvr_stage_name": (C.c_char_p, [C.c_void_p, C.c_int32]),
@@ -179,8 +179,8 @@ def cvr_cache_export(h, table, entries, stream):
     return tags, stamps
 
 
-def cvr_timing_begin(h, max_calls):
-    _check(lib().cvr_timing_begin(h, max_calls), h)
+def cvr_timing_begin(h, max_calls, stage_mask=0):
+    _check(lib().cvr_timing_begin(h, max_calls, stage_mask), h)
 
 
 def cvr_timing_end(h):
@@ -422,8 +422,24 @@ class Model:
         assert n <= dst.numel() * dst.element_size()
         return dst
 
-    def timing_begin(self, max_calls):
-        cvr_timing_begin(self.h, max_calls)
+    def stage_names(self):
+        """Stage names in cvr_stage_name order (bit s of a timing mask is stage s)."""
+        names = []
+        while True:
+            nm = cvr_stage_name(self.h, len(names))
+            if not nm:
+                return names
+            names.append(nm)
+
+    def timing_begin(self, max_calls, stages=None):
+        """Arm per-stage event timing for the next max_calls scoring calls; stages: names of
+        the stages to time (None = all of them)."""
+        mask = 0
+        if stages:
+            names = self.stage_names()
+            for st in stages:
+                mask |= 1 << names.index(st)
+        cvr_timing_begin(self.h, max_calls, mask)
 
     def timing_end(self):
         return cvr_timing_end(self.h)

@@ -280,10 +280,15 @@ cvr_status cvr_cache_export(cvr_handle h, int32_t table, int32_t* tags, int32_t*
 
 /* Per-stage kernel timing with HIP events recorded on the scoring stream.
  * cvr_timing_begin arms up to max_calls subsequent cvr_score calls;
+ * stage_mask selects the stages that are timed (bit s for stage s, as
+ * numbered by cvr_stage_name; 0 = every stage; a bit past the last stage is
+ * CVR_ERR_ARG).  The events ride on the timed stages' kernel dispatches, and
+ * such a dispatch costs a few microseconds more than a plain one: timing one
+ * stage disturbs a step less than timing all of them.
  * cvr_timing_end waits for them and writes, per stage, the summed
- * milliseconds and the number of kernel launches.  Stage names come from
- * cvr_stage_name. */
-cvr_status cvr_timing_begin(cvr_handle h, int32_t max_calls);
+ * milliseconds and the number of kernel launches (0 for stages not timed).
+ * Stage names come from cvr_stage_name. */
+cvr_status cvr_timing_begin(cvr_handle h, int32_t max_calls, uint32_t stage_mask);
 cvr_status cvr_timing_end(cvr_handle h, double* stage_ms, int32_t* stage_launches, int32_t max_stages,
                           int32_t* n_stages, int32_t* n_calls);
 const char* cvr_stage_name(cvr_handle h, int32_t stage);
