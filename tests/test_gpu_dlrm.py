@@ -250,3 +250,31 @@ def test_host_errors():
     with pytest.raises(cv.CvrError) as e:
         cv.cvr_score(m.h, db.c, cv.C.c_void_p(ws.data_ptr()), ws.numel(), cv.C.c_void_p(out.data_ptr()), cv._stream_ptr())
     assert e.value.status == cv.CVR_ERR_WORKSPACE
+
+
+def test_stage_timing_mask():
+    """Per-stage timing: every stage when the mask is 0, only the selected ones otherwise;
+    the scores do not depend on it; a bit past the last stage is an argument error."""
+    spec = _tiny()
+    tables = [torch.as_tensor(t).cuda() for t in _host_tables(spec)]
+    banner("tiny: stage timing masks")
+    m, _ = build_model(spec, "stress", tables=tables, debug=False)
+    b = synth.make_batch(spec, requests=3, candidates=4)
+    _, ref, st = run(m, b)
+    assert st == cv.CVR_OK
+    ref = ref.cpu().numpy().copy()
+    m.timing_begin(2)
+    for _ in range(2):
+        _, out, _ = run(m, b)
+        assert np.array_equal(out.cpu().numpy(), ref)
+    stages, calls = m.timing_end()
+    assert calls == 2 and {"expand", "gather_pool", "mlp_gemm", "dlrm_output"} <= set(stages)
+    m.timing_begin(3, ["mlp_gemm"])
+    for _ in range(3):
+        _, out, _ = run(m, b)
+        assert np.array_equal(out.cpu().numpy(), ref)
+    stages, calls = m.timing_end()
+    assert calls == 3 and set(stages) == {"mlp_gemm"}
+    assert stages["mlp_gemm"][1] == 3 * len(spec["mlp_hidden"]) and stages["mlp_gemm"][0] > 0
+    with pytest.raises(cv.CvrError):
+        cv.cvr_timing_begin(m.h, 1, 1 << len(m.stage_names()))
