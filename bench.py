@@ -30,6 +30,21 @@ WORKLOAD_TEXT = {
 }
 
 
+def dlrm_output_bytes(spec, n):
+    """Bytes the DLRM output stage moves per step.  The library runs the MLP over slices of the
+    candidates (128 MB per activation buffer); a slice whose last hidden layer runs on the wide
+    GEMM kernel (at least 256 tiles of 256 x 128) hands the output stage per-row partials of
+    64 columns instead of the activations (this mirrors the library's choice)."""
+    maxw, N = max(spec["mlp_hidden"]), spec["mlp_hidden"][-1]
+    rows = max(256, (128 << 20) // (maxw * 2) // 256 * 256)
+    total = 0
+    for r0 in range(0, n, rows):
+        M = min(rows, n - r0)
+        fused = N % 128 == 0 and N <= 1024 and -(-M // 256) * (N // 128) >= 256
+        total += (M * (N // 64) * 4 if fused else M * N * 2) + M * 4
+    return total
+
+
 def stage_work(spec, batch):
     """Algorithmic work per step, per stage: ("flop"|"byte", amount).
 
@@ -55,7 +70,7 @@ def stage_work(spec, batch):
     if spec["model"] == "dlrm":
         work["mlp_gemm"] = ("flop", n * sum(lin(k) for k in shapes if k.startswith("mlp.") and k.endswith(".weight")
                                           and shapes[k][0] > 1))
-        work["dlrm_output"] = ("byte", n * spec["mlp_hidden"][-1] * 2 + n * 4)
+        work["dlrm_output"] = ("byte", dlrm_output_bytes(spec, n))
         return work
     S = len(spec["seq"]["lengths"])
     P = int(batch["seq_ids"].shape[0])

@@ -372,6 +372,8 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     const int64_t hr = dlrm_pass_rows(m, n);
     w.h[0] = take((size_t)hr * maxw * lp);
     w.h[1] = take((size_t)hr * maxw * lp);
+    const int wl = s.n_hidden > 0 ? m->hidden[s.n_hidden - 1] : 0;
+    w.opart = take((size_t)((wl + kOutGroup - 1) / kOutGroup) * hr * 4);
   } else {
     const int64_t d = s.d, S = s.n_seq, T = s.n_tokens + s.n_seq;
     w.tok[0] = take((size_t)n * T * d * 4);
@@ -600,10 +602,14 @@ static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsP
   const int64_t pr = dlrm_pass_rows(m, n);
   if (sp.n_hidden < 1) return hipErrorInvalidValue;  // zero hidden layers: not supported by the output kernel
   hipError_t e = hipSuccess;
+  const int L_ = sp.n_hidden;
+  const void* w_out = m->wptr("mlp." + std::to_string(L_) + ".weight");
+  const float* b_out = (const float*)m->wptr("mlp." + std::to_string(L_) + ".bias");
   for (int64_t r0 = 0; r0 < n; r0 += pr) {
     const int mc = (int)std::min(pr, n - r0);
     int in = m->e_dim;
     int cur = -1;
+    bool fused = false;
     for (int i = 0; i < sp.n_hidden; ++i) {
       const int width = m->hidden[i];
       GemmParams g{};
@@ -623,6 +629,15 @@ static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsP
       g.ldc = width;
       g.c_nstride8 = 8;
       g.relu = 1;
+      // The last hidden layer takes the output layer into its epilogue when the wide kernel runs
+      // it (per-row partials per 64 columns instead of the activations); debug mode keeps the
+      // activations for export.
+      if (i == L_ - 1 && !m->debug && gemm_fuses_output(g)) {
+        g.ow = w_out;
+        g.opart = (float*)(ws + w.opart);
+        g.opart_ld = mc;
+        fused = true;
+      }
       e = L(STAGE_MLP_GEMM, [&] { return launch_gemm(g, sp.lowp, s); });
       if (e != hipSuccess) return e;
       cur = nxt;
@@ -630,11 +645,11 @@ static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsP
     }
     m->last_hidden_buf = cur;
     const void* H = ws + w.h[cur];
-    const int L_ = sp.n_hidden;
     e = L(STAGE_DLRM_OUTPUT, [&] {
-      return launch_dlrm_output(H, mc, in, m->wptr("mlp." + std::to_string(L_) + ".weight"),
-                                (const float*)m->wptr("mlp." + std::to_string(L_) + ".bias"),
-                                (float*)(ws + w.logits) + r0, out + r0, sp.lowp, s);
+      if (fused)
+        return launch_dlrm_logit((const float*)(ws + w.opart), in / kOutGroup, mc, mc, b_out,
+                                 (float*)(ws + w.logits) + r0, out + r0, s);
+      return launch_dlrm_output(H, mc, in, w_out, b_out, (float*)(ws + w.logits) + r0, out + r0, sp.lowp, s);
     });
     if (e != hipSuccess) return e;
   }
@@ -787,6 +802,9 @@ extern "C" cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, si
     case CVR_DBG_ATTN: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_attn_tok]; bytes = n * T * d * 4; break;
     case CVR_DBG_HIDDEN:
       if (cvr || sp.n_hidden == 0) return fail(h, CVR_ERR_ARG, "DLRM with hidden layers only");
+      if (!h->last_debug)
+        return fail(h, CVR_ERR_ARG, "hidden activations need cvr_set_debug(1) before scoring (otherwise the last "
+                                    "hidden layer may be fused into the output layer)");
       off = w.h[h->last_hidden_buf]; bytes = n * h->hidden[sp.n_hidden - 1] * 2; break;
     default: return fail(h, CVR_ERR_ARG, "unknown export");
   }

@@ -415,16 +415,19 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
   static_assert(BM == 256, "two 128-row wave tiles along M");
   static_assert(TPA >= 1 && TPB >= 1 && BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "loader shape");
   static_assert(NS >= 2 && L * (NS - 2) < 64, "ring depth");
-  // One LDS allocation: the ring, the per-wave staging areas, the bias of all N columns.
+  // One LDS allocation: the ring, the per-wave staging areas, the bias of all N columns and the
+  // output-layer weights of all N columns (fused output layer only).
   constexpr int kRingBytes = NS * kSlot * (int)sizeof(T);
   // Staged output rows per pass: a whole 32-row m-tile, or half of it when the ring leaves too
   // little LDS.
-  constexpr int SR = kRingBytes + NW * 32 * kStagePitch + kBigMaxN * 4 <= 160 * 1024 ? 32 : 16;
+  constexpr int SR = kRingBytes + NW * 32 * kStagePitch + 2 * kBigMaxN * 4 <= 160 * 1024 ? 32 : 16;
   constexpr int kStageBytes = NW * SR * kStagePitch;
-  __shared__ __align__(1024) char lds[kRingBytes + kStageBytes + kBigMaxN * 4];
+  __shared__ __align__(1024) char lds[kRingBytes + kStageBytes + 2 * kBigMaxN * 4];
   T* const smem = reinterpret_cast<T*>(lds);
   char* const stage = lds + kRingBytes + (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * SR * kStagePitch;
   float* const bias_s = reinterpret_cast<float*>(lds + kRingBytes + kStageBytes);
+  float* const ow_s = bias_s + kBigMaxN;
+  static_assert(WTN == kOutGroup, "one output-layer partial per wave column group");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -438,6 +441,8 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
   const int last = (x + 1) * tq + (x + 1 < trem ? x + 1 : trem);
   if (first >= last) return;
   for (int c = tid; c < p.N; c += NT) bias_s[c] = p.bias ? p.bias[(int64_t)g * p.bias_gstride + c] : 0.f;
+  if (p.ow)
+    for (int c = tid; c < p.N; c += NT) ow_s[c] = Lowp<T>::to_f32(reinterpret_cast<const T*>(p.ow)[c]);
 
   auto swz = [](int row) { return KC == 4 ? (row >> 2) & 3 : (row >> 1) & 7; };
   // Loader: transfer (NW i + wave) fills rows RPI*(NW i+wave) .. +RPI-1; lane l lands in row
@@ -597,6 +602,51 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
     // writes its 32 x WTN block into its own staging area (8-byte writes; a pitch that is an
     // odd multiple of 8 bytes keeps 32 rows on distinct banks) and reads it back as rows.
     const int m0 = (tc / ntn) * BM, ncol0 = (tc % ntn) * BN + wn * WTN;
+    if (p.ow) {
+      // Fused output layer: per row, the rounded activations of this wave's WTN columns times
+      // the output weights, in a fixed order: a lane half holds every other 4-column run (the
+      // lower half the runs starting at 8r, the upper half those at 8r + 4); each half sums its
+      // runs in column order, every run a fused multiply-add chain over its 4 columns, and the
+      // row's partial is the lower half's sum plus the upper half's.  Nothing of C is stored.
+      float dot[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) dot[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = ncol0 + j * 32 + 8 * q + 4 * lc;
+          const float4 b4 = *reinterpret_cast<const float4*>(&bias_s[col]);
+          const float4 w4 = *reinterpret_cast<const float4*>(&ow_s[col]);
+          const float bq[4] = {b4.x, b4.y, b4.z, b4.w}, wq[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            float run = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v = acc[i][j][4 * q + e] + bq[e];
+              if (p.relu) v = v > 0.f ? v : 0.f;
+              run = fmaf(Lowp<T>::to_f32(Lowp<T>::from_f32(v)), wq[e], run);
+            }
+            dot[i] += run;
+          }
+        }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const float upper = __shfl_xor(dot[i], 32);  // lanes 0-31 receive the upper half's sums
+        dot[i] += upper;
+      }
+      wait_vmcnt<0>();  // the next tile's first slices land before any store
+      if (lc == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int m = m0 + wm * WTM + i * 32 + lr;
+          if (m < p.M) p.opart[(int64_t)(ncol0 / kOutGroup) * p.opart_ld + m] = dot[i];
+        }
+      }
+      landed = true;
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int mrow0 = m0 + wm * WTM + i * 32;
@@ -663,14 +713,11 @@ static int big_grid(int tiles, int per_cu) {
 // least three quarters of the CUs busy (measured: the CVR expert GEMM, 224 tiles of K = 2048,
 // runs 36 us against 58 us as 64x64); 64x64 below that (the per-candidate GEMMs of the CVR
 // model at small batch).
-template <typename T, bool AF32>
-static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
+static int choose_tile(const GemmParams& p, bool af32) {
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
-  bool bk64 = p.K % 64 == 0;
-  for (int s = 0; s < p.nseg; ++s) bk64 = bk64 && p.seg[s].k_end % 64 == 0;
   const char* env = getenv("CVR_GEMM_TILE");
   int tile = env ? atoi(env) : 0;
-  const bool big_ok = !AF32 && !p.out_f32 && p.N % 128 == 0 && p.N <= kBigMaxN && p.c_nstride8 == 8 && !p.R &&
+  const bool big_ok = !af32 && !p.out_f32 && p.N % 128 == 0 && p.N <= kBigMaxN && p.c_nstride8 == 8 && !p.R &&
                       p.relu_end == 0 &&
                       (p.ldc & 7) == 0 && (p.c_gstride & 7) == 0;
   if (tile == 256 && !big_ok) tile = 0;
@@ -679,6 +726,20 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
     else if ((int64_t)tiles(128, 128) * p.groups >= 192) tile = 128;  // 3/4 of the CUs busy beats 4x the tiles
     else tile = 64;
   }
+  return tile;
+}
+
+bool gemm_fuses_output(const GemmParams& p) {
+  return p.M > 0 && p.N > 0 && p.nseg > 0 && choose_tile(p, p.seg[0].f32 != 0) == 256;
+}
+
+template <typename T, bool AF32>
+static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
+  auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
+  bool bk64 = p.K % 64 == 0;
+  for (int s = 0; s < p.nseg; ++s) bk64 = bk64 && p.seg[s].k_end % 64 == 0;
+  const int tile = choose_tile(p, AF32);
+  if (p.ow && (tile != 256 || !p.opart || p.opart_ld < p.M)) return hipErrorInvalidValue;  // wide kernel only
   const dim3 blk(256);
   if (tile == 256) {
     if constexpr (AF32) return hipErrorInvalidValue;  // excluded above
@@ -744,6 +805,27 @@ __global__ __launch_bounds__(256) void dlrm_output_kernel(const T* __restrict__ 
     if (logits) logits[row] = z;
     out[row] = sigmoid_f32(z);
   }
+}
+
+// One thread per candidate: the partials of the fused last hidden layer summed in group order.
+__global__ __launch_bounds__(256) void dlrm_logit_kernel(const float* __restrict__ part, int parts, int64_t ld, int M,
+                                                         const float* __restrict__ b, float* __restrict__ logits,
+                                                         float* __restrict__ out) {
+  const int row = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (row >= M) return;
+  float acc = 0.f;
+  for (int c = 0; c < parts; ++c) acc += part[(int64_t)c * ld + row];
+  const float z = acc + b[0];
+  if (logits) logits[row] = z;
+  out[row] = sigmoid_f32(z);
+}
+
+hipError_t launch_dlrm_logit(const float* part, int32_t parts, int64_t ld, int32_t M, const float* b, float* logits,
+                             float* out, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (parts <= 0 || ld < M) return hipErrorInvalidValue;
+  launch_k(dlrm_logit_kernel, dim3((M + 255) / 256), dim3(256), 0, st, part, parts, ld, M, b, logits, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_dlrm_output(const void* H, int32_t M, int32_t K, const void* w, const float* b,

@@ -164,13 +164,27 @@ struct GemmParams {
   int32_t relu_end;     // with relu: only columns n < relu_end (0: all columns)
   int32_t out_f32;      // 1: C is fp32, else the low-precision type
   int32_t r_f32;        // 1: R is fp32, else the low-precision type
+  // Output-layer fusion (wide kernel only, see gemm_fuses_output): when ow is set, C is not
+  // written; for every row m and every 64-column group c, opart[c * opart_ld + m] receives the
+  // sum over the group's columns n, in a fixed order, of y[m][n] * ow[n] in fp32, where y is
+  // the activation C would have held (bias, ReLU, rounded to the low-precision type).
+  const void* ow;
+  float* opart;
+  int64_t opart_ld;
 };
 hipError_t launch_gemm(const GemmParams& p, int lowp, hipStream_t st);
+// True when launch_gemm runs p on the wide kernel, which can take the output-layer fusion.
+bool gemm_fuses_output(const GemmParams& p);
+constexpr int kOutGroup = 64;  // columns per output-layer partial
 
 // ---------------------------------------------------------------- DLRM output (A4)
 // z[m] = sum_k H[m][k] * w[k] + b  (fp32 accumulation), out[m] = sigmoid(z[m]).
 hipError_t launch_dlrm_output(const void* H, int32_t M, int32_t K, const void* w, const float* b,
                               float* logits, float* out, int lowp, hipStream_t st);
+// The same from the partials of a fused last hidden layer: z[m] = sum over c = 0..parts-1, in
+// order, of part[c * ld + m], plus b; out[m] = sigmoid(z[m]).
+hipError_t launch_dlrm_logit(const float* part, int32_t parts, int64_t ld, int32_t M, const float* b, float* logits,
+                             float* out, hipStream_t st);
 
 // ---------------------------------------------------------------- CVR sequences (B3-B5)
 constexpr int kMaxSeqCols = 8;

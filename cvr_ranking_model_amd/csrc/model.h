@@ -50,6 +50,7 @@ struct InputSeg {
 struct WsPlan {
   size_t flag = 0, cand_req = 0, x_req = 0, x_item = 0, logits = 0, pooled = 0, pooled_bytes = 0;
   size_t h[2] = {0, 0};
+  size_t opart = 0;  // DLRM: output-layer partials of a fused last hidden layer
   size_t tok[2] = {0, 0}, hseq = 0, chunk_off = 0, chunk_desc = 0, pool_part = 0, seq_pool = 0, query = 0,
          mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0, tok_req = 0;
   size_t total = 0;

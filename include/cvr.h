@@ -191,7 +191,12 @@ cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_c
  * 65536 candidates at width 1024; the environment variable
  * CVR_DLRM_PASS_ROWS, read by cvr_create, sets another slice size, 0 meaning
  * one slice).  Scores do not depend on the slicing.  With debug on, one slice
- * covers the batch so that the last hidden layer can be exported whole. */
+ * covers the batch so that the last hidden layer can be exported whole.  With
+ * debug off, a last hidden layer that runs on the wide GEMM kernel also forms
+ * the output layer's per-row partial sums over 64-column groups and stores
+ * no activations; a small kernel adds the partials in group order, adds the
+ * bias and applies the sigmoid (the same values as the separate output
+ * kernel up to the order of the fp32 additions). */
 cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
                      float* out_scores, void* hip_stream);
 
@@ -230,7 +235,9 @@ enum {
   CVR_DBG_TOKENS = 7,       /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix Z */
   CVR_DBG_QUERY = 8,        /* (CVR) fp32 [n_seq][n][d]: last layer's queries */
   CVR_DBG_ATTN = 9,         /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix before mixing (attention outputs in rows N..) */
-  CVR_DBG_HIDDEN = 10       /* (DLRM) lowp [n][width]: activations of the last hidden layer */
+  CVR_DBG_HIDDEN = 10       /* (DLRM, debug mode) lowp [n][width]: activations of the last hidden
+                               layer (outside debug mode that layer may hand per-row partials of
+                               the output layer to it instead of storing its activations) */
 };
 cvr_status cvr_set_debug(cvr_handle h, int32_t debug);
 cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, size_t dst_bytes, size_t* written,

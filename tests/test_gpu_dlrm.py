@@ -278,3 +278,44 @@ def test_stage_timing_mask():
     assert stages["mlp_gemm"][1] == 3 * len(spec["mlp_hidden"]) and stages["mlp_gemm"][0] > 0
     with pytest.raises(cv.CvrError):
         cv.cvr_timing_begin(m.h, 1, 1 << len(m.stage_names()))
+
+
+@pytest.mark.parametrize("variant", ["bench", "stress"])
+def test_fused_output_layer(variant):
+    """Outside debug mode the last hidden layer of a C2 batch runs on the wide kernel and forms
+    the output layer's per-row partials in its epilogue (the launch configuration bench.py
+    times).  Its logits must match the separate output kernel's (debug mode) up to the order of
+    the fp32 additions, and its scores the oracle on sampled requests."""
+    spec = synth.load_spec("c2")
+    banner(f"c2 full {variant}: fused output layer vs separate output kernel and the oracle")
+    m, weights = build_model(spec, variant, debug=False)
+    b = synth.make_batch(spec)
+    db, out, st = run(m, b)
+    assert st == cv.CVR_OK
+    n = db.n_candidates
+    s_fused = out.cpu().numpy().copy()
+    z_fused = m.export(cv.CVR_DBG_LOGITS, torch.float32, (n,)).cpu().numpy().copy()
+    with pytest.raises(cv.CvrError, match="debug"):
+        m.export(cv.CVR_DBG_HIDDEN, torch.float16, (n, spec["mlp_hidden"][-1]))
+    m.set_debug(True)
+    _, out2, st = run(m, b)
+    assert st == cv.CVR_OK
+    s_sep = out2.cpu().numpy()
+    z_sep = m.export(cv.CVR_DBG_LOGITS, torch.float32, (n,)).cpu().numpy()
+    # The same fp16 activations and weights: only the summation order of the 1024 fp32 products
+    # differs, each partial sum rounding by at most 2^-24 of the running magnitude.
+    w_out = weights[f"mlp.{len(spec['mlp_hidden'])}.weight"].astype(np.float64)
+    hid = m.export(cv.CVR_DBG_HIDDEN, torch.float16, (n, spec["mlp_hidden"][-1])).double().cpu().numpy()
+    bound = 1024 * 2.0 ** -24 * (np.abs(hid) @ np.abs(w_out.reshape(-1)) + 1.0) * 2
+    dz = np.abs(z_fused.astype(np.float64) - z_sep)
+    banner(f"  fused vs separate: max|dz| {dz.max():.3e} (bound {bound.min():.3e}..{bound.max():.3e}), "
+           f"max|ds| {np.abs(s_fused - s_sep).max():.3e}")
+    assert (dz <= bound).all()
+    assert np.abs(s_fused - s_sep).max() <= 1e-5
+    # against the oracle on requests 0, 31 and 63
+    ref = oracle.score(spec, synth.make_tables(spec, variant), weights, b, requests=[0, 31, 63])
+    cands = ref["cand"]
+    assert np.abs(z_fused[cands] - ref["logits"]).max() <= logit_tol(ref["logits"], spec)
+    assert np.abs(s_fused[cands] - ref["scores"]).max() <= SCORE_TOL
+    del m
+    torch.cuda.empty_cache()
