@@ -94,12 +94,12 @@ def stage_work(spec, batch):
     return work
 
 
-def measured_traffic(stage):
+def measured_traffic(workload, stage):
     """HBM bytes per launch of a stage's kernel from the committed byte-counter summaries.
 
-    Each summary under profiles/ carries "traffic-json:" lines naming the kernel's source file
-    and its sha256 at the time the counters were taken; a figure whose source has changed
-    since is stale and is not reported.
+    Each summary under profiles/ carries "traffic-json:" lines naming the workload, the stage,
+    the kernel's source file and its sha256 at the time the counters were taken; a figure whose
+    source has changed since is stale and is not reported.
     """
     import glob
     import hashlib
@@ -108,7 +108,7 @@ def measured_traffic(stage):
             if not line.startswith("traffic-json:"):
                 continue
             rec = json.loads(line[len("traffic-json:"):])
-            if rec.get("stage") != stage or rec.get("bytes_per_launch") is None:
+            if rec.get("workload", "c2") != workload or rec.get("stage") != stage or rec.get("bytes_per_launch") is None:
                 continue
             src = os.path.join(ROOT, rec["source"])
             if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
@@ -313,7 +313,8 @@ def main():
         d_entry["frac"] = round(d_entry["achieved"] / d_entry["peak"], 4)
     roof = None
     if "bound" in d_entry:
-        traffic, source = measured_traffic(dom) if args.workload == "c2" and not args.uniform_ids else (None, None)
+        traffic, source = measured_traffic(args.workload, dom) if args.batch is None and args.candidates is None and not args.uniform_ids \
+            and not args.cache else (None, None)
         roof = {"bound": d_entry["bound"], "kernel": dom, "achieved": d_entry["achieved"], "peak": d_entry["peak"],
                 "unit": d_entry["unit"], "frac": d_entry["frac"], "traffic": traffic,
                 "per_launch": d_entry["per_launch"], "avg_launch_us": d_entry["avg_launch_us"]}
