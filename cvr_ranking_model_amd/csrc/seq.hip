@@ -184,30 +184,45 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
             acc[j][4 * v4 + 2] = bb.z;
             acc[j][4 * v4 + 3] = bb.w;
           }
+        V8 e[kD / 16];
 #pragma unroll
-        for (int k = 0; k < kD / 16; ++k) {
-          const V8 e = *reinterpret_cast<const V8*>(&Es[b][lr * kEPitch + k * 16 + lk]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = Lowp<bf16>::mfma32(wg[j][k], e, acc[j]);
-        }
+        for (int k = 0; k < kD / 16; ++k) e[k] = *reinterpret_cast<const V8*>(&Es[b][lr * kEPitch + k * 16 + lk]);
         // The tiles are hidden units x positions: lane holds units 8*v4 + 4*(lane/32) .. +3 of
         // each tile for position lane%32, so SiLU(gate) * up of 4 units leaves as 8 bytes.
         // exp(-g) = exp2(-log2(e) * g); g and up already hold their biases.
+        auto silu_q = [&](int j, int v4, int q) {
+          const float g = acc[j][4 * v4 + q], u = acc[j + 2][4 * v4 + q];
+          const float e2 = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+          const float r = __builtin_amdgcn_rcpf(1.0f + e2);
+          return (bf16)((g * u) * r);
+        };
+        auto put = [&](int j, int v4, const bf16x4& o) {
+          *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + j * 32 + 8 * v4 + 4 * (lane >> 5)]) = o;
+        };
+        // Units 0-31 of the gate and up tiles first; their SiLU (vector and transcendental
+        // instructions) is interleaved with the matrix instructions of units 32-63.
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int k = 0; k < kD / 16; ++k) {
+          acc[0] = Lowp<bf16>::mfma32(wg[0][k], e[k], acc[0]);
+          acc[2] = Lowp<bf16>::mfma32(wg[2][k], e[k], acc[2]);
+        }
+        bf16x4 o;
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int h = j * 32 + 8 * v4 + 4 * (lane >> 5);
-            bf16x4 o;
+        for (int k = 0; k < kD / 16; ++k) {
+          acc[1] = Lowp<bf16>::mfma32(wg[1][k], e[k], acc[1]);
+          acc[3] = Lowp<bf16>::mfma32(wg[3][k], e[k], acc[3]);
+          const int v4 = k >> 1, q0 = (k & 1) * 2;
+          o[q0] = silu_q(0, v4, q0);
+          o[q0 + 1] = silu_q(0, v4, q0 + 1);
+          if (k & 1) put(0, v4, o);
+          __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs and SiLU together
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float g = acc[j][4 * v4 + q], u = acc[j + 2][4 * v4 + q];
-              const float e2 = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-              const float r = __builtin_amdgcn_rcpf(1.0f + e2);
-              o[q] = (bf16)((g * u) * r);
-            }
-            *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + h]) = o;
-          }
+        for (int v4 = 0; v4 < 4; ++v4) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = silu_q(1, v4, q);
+          put(1, v4, o);
+        }
       }
       if (i >= 2) store_out(i);
       dm2 = dm1;
