@@ -14,7 +14,8 @@
 //   2. gate|up = W_gu E^T (MFMA 32x32x16, fp32 accumulate); producer w owns gate units
 //      64w..64w+63 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
 //      registers and written to LDS as bf16 (the input of the down projection);
-//   3. H = A W_down^T + b (MFMA 32x32x16), rounded to bf16, staged through LDS and stored as
+//   3. H = A W_down^T + b (MFMA 32x32x16; the bias starts one of the two accumulators),
+//      rounded to bf16, staged through LDS and stored as
 //      rows; the rounded values are summed per column over the chunk's positions for the
 //      mean pool.
 #include "device_common.h"
@@ -338,9 +339,10 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       }
       const bf16* A = As[(i - 1) & 1];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc2[h][v] = 0.f;
+      for (int v = 0; v < 16; ++v) {  // the even-k accumulator starts at the bias
+        acc2[0][v] = bd;
+        acc2[1][v] = 0.f;
+      }
 #pragma unroll
       for (int k = 0; k < kHid / 16; ++k) {
         const V8 a = *reinterpret_cast<const V8*>(&A[lr * kAPitch + k * 16 + lk]);
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
+          const bf16 h = (bf16)(acc2[0][v] + acc2[1][v]);
           hdst[m * kEPitch + ncol] = h;
           colsum += (float)h;
         }
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bf16 h = (bf16)((acc2[0][v] + acc2[1][v]) + bd);
+          const bf16 h = (bf16)(acc2[0][v] + acc2[1][v]);
           hdst[m * kEPitch + ncol] = h;
           if (m < np) colsum += (float)h;
         }
