@@ -465,7 +465,7 @@ extern "C" cvr_status cvr_timing_end(cvr_handle h, double* stage_ms, int32_t* st
 extern "C" const char* cvr_stage_name(cvr_handle, int32_t stage) {
   static const char* names[kNumStages] = {"expand", "gather_pool", "mlp_gemm", "dlrm_output", "tokenize_gemm",
                                           "swiglu", "seq_pool", "query_gemm", "attention", "mixer_gemm",
-                                          "ple_gemm", "ple_gate", "head_gemm", "head_out", "cache"};
+                                          "ple_gemm", "ple_gate", "head_gemm", "head_out", "cache", "seq_chunks"};
   return (stage >= 0 && stage < kNumStages) ? names[stage] : "";
 }
 

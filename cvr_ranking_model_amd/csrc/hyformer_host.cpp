@@ -111,7 +111,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   // ---- B3-B5: sequence encoding and mean pools (per request)
   int32_t* chunk_off = (int32_t*)(ws + w.chunk_off);
   int2* chunk_desc = (int2*)(ws + w.chunk_desc);
-  e = L(STAGE_SWIGLU, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, chunk_desc, s); });
+  e = L(STAGE_SEQ_CHUNKS, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, chunk_desc, s); });
   if (e != hipSuccess) return e;
   {
     SwigluParams p{};

@@ -26,6 +26,7 @@ enum Stage {
   STAGE_HEAD_GEMM,
   STAGE_HEAD_OUT,
   STAGE_CACHE,
+  STAGE_SEQ_CHUNKS,
   kNumStages
 };
 constexpr int kMaxLaunchesPerCall = 64;
