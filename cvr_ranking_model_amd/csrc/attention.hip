@@ -25,7 +25,7 @@ struct SoftState {
 };
 
 __device__ __forceinline__ void merge_state(SoftState& a, const SoftState& b) {
-  const float m = fmaxf(a.m, b.m);
+  const float m = max_nan(a.m, b.m);
   if (m == -INFINITY) return;  // both empty
   const float ea = expf(a.m - m), eb = expf(b.m - m);
   a.l = fmaf(a.l, ea, b.l * eb);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
     d += __shfl_xor(d, 2);
     d += __shfl_xor(d, 4);
     const float sc = d * p.inv_tau;
-    const float mn = fmaxf(st.m, sc);
+    const float mn = max_nan(st.m, sc);
     const float alpha = expf(st.m - mn);
     const float pe = expf(sc - mn);
     st.l = fmaf(st.l, alpha, pe);
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
       for (int j = 0; j < 16; ++j) o2.o[j] = sm[w][sub][2 + j];
       merge_state(st, o2);
     }
-    const float inv = st.l > 0.f ? 1.0f / st.l : 0.f;
+    const float inv = st.l == 0.f ? 0.f : 1.0f / st.l;  // an empty sequence gives 0; NaN passes
     float4* out = reinterpret_cast<float4*>(p.Y + ((int64_t)c * p.T + p.N + s) * 128 + sub * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -210,10 +210,10 @@ __global__ __launch_bounds__(256) void attention_mq_kernel(const AttnParams p) {
     for (int v = 0; v < 16; ++v) {
       const int64_t pos = t0 + 8 * (v >> 2) + 4 * hf + (v & 3);
       x[v] = active && pos < e ? sc[v] * p.inv_tau : -INFINITY;
-      bm = fmaxf(bm, x[v]);
+      bm = max_nan(bm, x[v]);
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);
+    bm = max_nan(bm, __shfl_xor(bm, 32));
+    const float mn = max_nan(m, bm);
     const float alpha = mn == -INFINITY ? 1.f : expf(m - mn);
     float pv[16], ps = 0.f;
 #pragma unroll
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void attention_mq_kernel(const AttnParams p) {
 #pragma unroll 1
   for (int w = 0; w < 3; ++w) {
     const float mw = Ms[w][0][lr], lw = Ms[w][1][lr];
-    const float mn = fmaxf(m, mw);
+    const float mn = max_nan(m, mw);
     if (mn == -INFINITY) continue;
     const float a0 = expf(m - mn), aw = expf(mw - mn);
     l = fmaf(l, a0, lw * aw);
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void attention_mq_kernel(const AttnParams p) {
       }
   }
   if (cvalid) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float inv = l == 0.f ? 0.f : 1.0f / l;  // an empty sequence gives 0; NaN passes
     float* out = p.Y + ((int64_t)(c0 + lr) * p.T + p.N + s) * 128;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

@@ -55,10 +55,17 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return h;
 }
 
-// Clamp to [-c, c]; NaN passes through (comparisons with NaN are false).
-__device__ __forceinline__ float clamp_keep_nan(float v, float c) {
-  return v < -c ? -c : (v > c ? c : v);
-}
+// IEEE 754-2019 maximum and minimum (v_maximum3_f32 / v_minimum3_f32 on gfx950): a NaN operand
+// gives NaN, where fmaxf / fminf and a compare-and-select would return the other operand.  Every
+// operator of the path lets NaN through, as the method's plain definition does.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float min_nan(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
+// Clamp to [-c, c]; NaN passes through.
+__device__ __forceinline__ float clamp_keep_nan(float v, float c) { return min_nan(max_nan(v, -c), c); }
+
+// ReLU; NaN passes through.
+__device__ __forceinline__ float relu_f32(float v) { return max_nan(v, 0.f); }
 
 // Logistic sigmoid in fp32 from the device exp.
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             float x = acc[i][j][v] + bn;
-            if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
+            if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = relu_f32(x);
             st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * OP + nl] = x;
           }
         }
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             float x = acc[i][j][v] + bn;
-            if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
+            if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = relu_f32(x);
             st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * OP + nl] = Lowp<T>::from_f32(x);
           }
         }
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         float x = acc[i][j][v] + bn;
         if (p.R) x += p.r_f32 ? reinterpret_cast<const float*>(p.R)[raddr]
                               : Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[raddr]);
-        if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = x > 0.f ? x : 0.f;
+        if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = relu_f32(x);
         if (p.out_f32)
           reinterpret_cast<float*>(p.C)[addr] = x;
         else
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float v = acc[i][j][4 * q + e] + bq[e];
-              if (p.relu) v = v > 0.f ? v : 0.f;
+              if (p.relu) v = relu_f32(v);
               run = fmaf(Lowp<T>::to_f32(Lowp<T>::from_f32(v)), wq[e], run);
             }
             dot[i] += run;
@@ -662,7 +662,7 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float v = acc[i][j][4 * q + e] + bq[e];
-            if (p.relu) v = v > 0.f ? v : 0.f;
+            if (p.relu) v = relu_f32(v);
             o[j][q][e] = Lowp<T>::from_f32(v);
           }
         }

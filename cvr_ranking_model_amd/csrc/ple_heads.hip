@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void ple_gate_kernel(const PleGateParams p) {
     for (int e = 0; e < p.E; ++e)
       if ((mask >> e) & 1) {
         logit[e] = lg[r++];
-        mx = fmaxf(mx, logit[e]);
+        mx = max_nan(mx, logit[e]);
       }
     float g[kMaxExperts], sum = 0.f;
     for (int e = 0; e < p.E; ++e) {

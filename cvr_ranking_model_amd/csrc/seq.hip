@@ -238,8 +238,8 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   // Granule i of a consumer thread covers position (bt + 256 i) / 32 and columns
   // 4 * (bt % 32) .. +3, which sit in one sequence column (table, rows and width fixed).
   const float* gtab;
-  uint32_t grows;
-  int gstride, gcol;
+  uint32_t grows, growb;  // rows of the column's table, bytes per row
+  int gcol;
   {
     const int col = (bt & 31) * 4;
     int ci = 0;
@@ -249,36 +249,33 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
     gcol = ci;
     gtab = p.col_table[ci] + (col - p.col_off[ci]);
     grows = p.col_rows[ci] > 0x7fffffff ? 0x7fffffffu : (uint32_t)p.col_rows[ci];  // ids are int32
-    gstride = p.col_dim[ci];
+    growb = (uint32_t)p.col_dim[ci] * 4u;
   }
   const int gpos0 = bt >> 5;  // granule i is at position gpos0 + 8 i
   bool bad = false;
   auto load_ids = [&](int2 d, int32_t (&id)[4]) {
     const int np = d.y & 255;
+    const int32_t* chunk_ids = p.seq_ids + (int64_t)d.x * p.ncols;  // the same for every lane
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pos = gpos0 + 8 * i;
-      id[i] = p.seq_ids[((int64_t)d.x + (pos < np ? pos : 0)) * p.ncols + gcol];
+      id[i] = chunk_ids[(pos < np ? pos : 0) * p.ncols + gcol];
     }
   };
   // Rows of positions past the chunk's length are loaded but never used: row m of H depends on
   // row m of E alone and such rows are neither stored nor summed.  An out-of-range id raises
-  // the error flag and reads row 0 instead.
-  auto load_rows = [&](int2 d, const int32_t (&id)[4], float4 (&row)[4]) {
-    const int np = d.y & 255;
+  // the error flag and reads row 0 instead.  Such a position reads the id of the chunk's first
+  // position, which is checked on its own account, so its check needs no length test.
+  auto load_rows = [&](const int32_t (&id)[4], float4 (&row)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t r = (uint32_t)id[i];
       const bool ok = r < grows;
-      if (!ok && gpos0 + 8 * i < np) bad = true;
-      row[i] = *reinterpret_cast<const float4*>(gtab + (ok ? r : 0u) * (uint64_t)gstride);
+      bad |= !ok;
+      row[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(gtab) + (uint64_t)(ok ? r : 0u) * growb);
     }
   };
-  // clamp to [-c, c] keeping NaN, as one median-of-three and a NaN select
-  auto clampv = [&](float x) {
-    const float m = __builtin_amdgcn_fmed3f(x, -p.clamp, p.clamp);
-    return x != x ? x : m;
-  };
+  auto clampv = [&](float x) { return clamp_keep_nan(x, p.clamp); };
   auto convert = [&](const float4 (&row)[4], int b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -303,12 +300,12 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   int32_t ids[4];
   float4 rowA[4], rowB[4];
   load_ids(d0, ids);
-  load_rows(d0, ids, rowA);
+  load_rows(ids, rowA);
   load_ids(d1, ids);
   convert(rowA, 0);
-  load_rows(d1, ids, rowA);
+  load_rows(ids, rowA);
   load_ids(d2, ids);
-  load_rows(d2, ids, rowB);
+  load_rows(ids, rowB);
   load_ids(d3, ids);
   if (bt == 0) Ds[0] = d0;
   __syncthreads();  // E(0) and Ds[0] complete (pairs with the producers' first wait)
@@ -320,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
     int2 d5 = d4;
     if (i + 1 < n) {
       convert(cur, (i + 1) & 1);
-      load_rows(d3, ids, cur);
+      load_rows(ids, cur);
       load_ids(d4, ids);
       d5 = desc_of(i + 5);
       if (bt == 0) Ds[(i + 1) & 1] = d1;

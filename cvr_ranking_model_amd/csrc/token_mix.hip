@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p) 
         for (int b = 0; b < 2; ++b) {
           bf16x4 o;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (bf16)fmaxf(acc[a][b][4 * v4 + q] + bv[q], 0.f);
+          for (int q = 0; q < 4; ++q) o[q] = (bf16)relu_f32(acc[a][b][4 * v4 + q] + bv[q]);
           *reinterpret_cast<bf16x4*>(&Hs[(32 * b + lr) * kHPitch + u]) = o;
         }
       }

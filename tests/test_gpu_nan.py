@@ -1,0 +1,96 @@
+"""GPU: a NaN in a table row passes the +-10 clamp (the clamp bounds finite values only) and
+reaches the scores of exactly the candidates that read that row; every other candidate's
+score is unchanged bit for bit, since no stage mixes candidates' values."""
+import numpy as np
+import pytest
+import torch
+
+from cvr_ranking_model_amd import synth
+from cvr_ranking_model_amd import cvr as cv
+from gpu_common import banner, build_model, run
+
+pytestmark = pytest.mark.gpu
+
+
+def _scores(out, n, k):
+    return out.cpu().numpy().reshape(n, k).copy()
+
+
+def _id_used_once(ids, owner):
+    """An id that appears in exactly one owner's entries (owner[i] owns ids[i]), and that owner."""
+    uniq = {}
+    for i, o in zip(ids.tolist(), owner.tolist()):
+        uniq.setdefault(i, set()).add(o)
+    for i in sorted(uniq):
+        if len(uniq[i]) == 1:
+            return i, next(iter(uniq[i]))
+    raise AssertionError("no id owned by a single request")
+
+
+def test_nan_passes_the_clamps_cvr():
+    spec = synth.load_spec("c3")
+    R, K = 8, spec["n_tasks"]
+    batch = synth.make_batch(spec, requests=R)
+    tables = cv.device_tables(spec, "stress")
+    m, _ = build_model(spec, "stress", debug=False, tables=tables)
+    _, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    clean = _scores(out, R, K)
+    assert np.isfinite(clean).all()
+
+    # a sequence item-ID row read by one request only (one position or several, any sequence)
+    so, sid = batch["seq_offsets"], batch["seq_ids"]
+    owner = np.empty(sid.shape[0], np.int64)
+    for s in range(so.shape[0]):
+        for r in range(R):
+            owner[so[s, r]:so[s, r + 1]] = r
+    x, r_seq = _id_used_once(sid[:, 0], owner)
+    # a non-sequence row of feature 0 (one bag per request) read by another request only
+    bo, ids = batch["bag_offsets"], batch["ids"]
+    f0 = np.concatenate([ids[bo[r]:bo[r + 1]] for r in range(R)])
+    f0_owner = np.concatenate([np.full(bo[r + 1] - bo[r], r) for r in range(R)])
+    keep = f0_owner != r_seq
+    y, r_tok = _id_used_once(f0[keep], f0_owner[keep])
+    seq_table = spec["seq"]["columns"][0]["table"]
+    tok_table = spec["features"][0]["table"]
+    banner(f"c3 NaN: sequence table {seq_table} row {x} (request {r_seq}), table {tok_table} row {y} (request {r_tok})")
+    tables[seq_table][x, 5] = float("nan")
+    tables[tok_table][y, 7] = float("nan")
+    torch.cuda.synchronize()
+    _, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    dirty = _scores(out, R, K)
+    assert np.isnan(dirty[r_seq]).all() and np.isnan(dirty[r_tok]).all()
+    others = [r for r in range(R) if r not in (r_seq, r_tok)]
+    assert np.array_equal(dirty[others], clean[others])
+    m.close()
+
+
+def test_nan_passes_the_clamp_dlrm():
+    spec = synth.load_spec("c1")
+    batch = synth.make_batch(spec)
+    n = int(batch["cand_offsets"][-1])
+    tables = cv.device_tables(spec, "stress")
+    m, _ = build_model(spec, "stress", debug=False, tables=tables)
+    _, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    clean = _scores(out, n, 1)
+    assert np.isfinite(clean).all()
+    # first item feature: bags n, one per candidate, after the user features' one bag each
+    fi = next(i for i, f in enumerate(spec["features"]) if f["side"] == "item")
+    base = sum(1 if f["side"] != "item" else n for f in spec["features"][:fi])
+    bo, ids = batch["bag_offsets"], batch["ids"]
+    vals = np.concatenate([ids[bo[base + c]:bo[base + c + 1]] for c in range(n)])
+    owner = np.concatenate([np.full(bo[base + c + 1] - bo[base + c], c) for c in range(n)])
+    z, c0 = _id_used_once(vals, owner)
+    t = spec["features"][fi]["table"]
+    banner(f"c1 NaN: table {t} row {z} (candidate {c0})")
+    tables[t][z, 3] = float("nan")
+    torch.cuda.synchronize()
+    _, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    dirty = _scores(out, n, 1)
+    assert np.isnan(dirty[c0]).all()
+    others = np.array([c for c in range(n) if c != c0])
+    assert np.array_equal(dirty[others], clean[others])
+    m.close()
