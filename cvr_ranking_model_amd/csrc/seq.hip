@@ -88,6 +88,8 @@ hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t 
   return hipGetLastError();
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;        // token width
 constexpr int kHid = 256;      // SwiGLU hidden width
 constexpr int kEPitch = kD + 8;
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       if (bt == 0) Ds[(i + 1) & 1] = d1;
     }
     const bool down = i >= 1 && i <= n;
-    f32x16 acc2[2];
+    f32x16 hacc[2];
     if (down) {
       // chunk i-1: down projection on the SiLU tile, while the producer runs its SiLU
       const int s = (dprev.y >> 8) / p.R;
@@ -336,36 +338,41 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       }
       const bf16* A = As[(i - 1) & 1];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {  // the even-k accumulator starts at the bias
-        acc2[0][v] = bd;
-        acc2[1][v] = 0.f;
+      for (int v = 0; v < 16; ++v) {  // even and odd k in two accumulators, the even one starts at the bias
+        hacc[0][v] = bd;
+        hacc[1][v] = 0.f;
       }
 #pragma unroll
       for (int k = 0; k < kHid / 16; ++k) {
         const V8 a = *reinterpret_cast<const V8*>(&A[lr * kAPitch + k * 16 + lk]);
-        acc2[k & 1] = Lowp<bf16>::mfma32(a, wd[k], acc2[k & 1]);
+        hacc[k & 1] = Lowp<bf16>::mfma32(a, wd[k], hacc[k & 1]);
       }
     }
     if (down) {
-      // bf16 H staged for the producers; lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of ncol
+      // bf16 H staged for the producers; lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of ncol,
+      // converted two rows at a time
       const int np = dprev.y & 255;
       bf16* hdst = Hs[(i - 1) & 1];
       float colsum = 0.f;
       if (np == kM) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bf16 h = (bf16)(acc2[0][v] + acc2[1][v]);
-          hdst[m * kEPitch + ncol] = h;
-          colsum += (float)h;
+          const bf16x2 h = __builtin_convertvector((float2_t){hacc[0][v] + hacc[1][v], hacc[0][v + 1] + hacc[1][v + 1]}, bf16x2);
+          hdst[m * kEPitch + ncol] = h[0];
+          hdst[(m + 1) * kEPitch + ncol] = h[1];
+          colsum += (float)h[0];
+          colsum += (float)h[1];
         }
       } else {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bf16 h = (bf16)(acc2[0][v] + acc2[1][v]);
-          hdst[m * kEPitch + ncol] = h;
-          if (m < np) colsum += (float)h;
+          const bf16x2 h = __builtin_convertvector((float2_t){hacc[0][v] + hacc[1][v], hacc[0][v + 1] + hacc[1][v + 1]}, bf16x2);
+          hdst[m * kEPitch + ncol] = h[0];
+          hdst[(m + 1) * kEPitch + ncol] = h[1];
+          if (m < np) colsum += (float)h[0];
+          if (m + 1 < np) colsum += (float)h[1];
         }
       }
       colsum += __shfl_xor(colsum, 32);
