@@ -403,26 +403,50 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) 
   return hipGetLastError();
 }
 
-// Mean pool per segment: sum the chunk partials in chunk order, divide by the length.
-__global__ __launch_bounds__(128) void seq_pool_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_off,
+// Mean pool per segment: the chunk partials summed in eight interleaved chains (chunk c goes to
+// chain c % 8, each chain in chunk order), the chains added in chain order, divided by the length.
+// The order depends only on the segment's chunk count, so a request's pools do not depend on the
+// rest of the batch.  Lane t reads four columns of every eighth chunk (16-byte loads).
+__global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ seq_offsets, int R, int S,
                                                        int64_t n_positions, float* __restrict__ pool) {
+  constexpr int kChains = 8;
+  __shared__ float4 sm[kChains][kD / 4];
   const int g = blockIdx.x;
-  const int j = threadIdx.x;
+  const int t = threadIdx.x, q = t % (kD / 4), chain = t / (kD / 4);
   const int s = g / R, r = g % R;
   int64_t a = seq_offsets[(int64_t)s * (R + 1) + r], e = seq_offsets[(int64_t)s * (R + 1) + r + 1];
   a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
   e = e < a ? a : (e > n_positions ? n_positions : e);
-  float acc = 0.f;
-  for (int c = chunk_off[g]; c < chunk_off[g + 1]; ++c) acc += part[(int64_t)c * kD + j];
-  const float v = e > a ? acc / (float)(e - a) : 0.f;
-  pool[(int64_t)g * kD + j] = v;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = chunk_off[g] + chain; c < chunk_off[g + 1]; c += kChains) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)c * kD + 4 * q);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  sm[chain][q] = acc;
+  __syncthreads();
+  if (chain == 0) {
+#pragma unroll
+    for (int k = 1; k < kChains; ++k) {
+      const float4 v = sm[k][q];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const float len = (float)(e - a);
+    const float4 o = e > a ? make_float4(acc.x / len, acc.y / len, acc.z / len, acc.w / len) : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(pool + (int64_t)g * kD + 4 * q) = o;
+  }
 }
 
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
                            int64_t n_positions, float* pool, hipStream_t st) {
   if (R * S <= 0) return hipSuccess;
-  launch_k(seq_pool_kernel, dim3(R * S), dim3(kD), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, pool);
+  launch_k(seq_pool_kernel, dim3(R * S), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, pool);
   return hipGetLastError();
 }
 
