@@ -1,0 +1,84 @@
+"""Host logic of bench.py: algorithmic work per stage, the counter-derived traffic lookup, the
+one-GPU guard.  No GPU is touched."""
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from cvr_ranking_model_amd import synth  # noqa: E402
+
+
+def test_dlrm_stage_work_matches_the_layer_shapes():
+    spec = synth.load_spec("c2")
+    batch = synth.make_batch(spec)
+    n = int(batch["cand_offsets"][-1])
+    work = bench.stage_work(spec, batch)
+    # 640 -> 1024, then four 1024 -> 1024 hidden layers; the 1024 -> 1 output is its own stage
+    assert work["mlp_gemm"] == ("flop", 2 * n * (640 * 1024 + 4 * 1024 * 1024))
+    # table rows once per id, the ids and offsets read, the fp16 inputs written
+    kind, nbytes = work["gather_pool"]
+    lens = [int(b) - int(a) for a, b in zip(batch["bag_offsets"][:-1], batch["bag_offsets"][1:])]
+    rows = out = o = 0
+    R = len(batch["cand_offsets"]) - 1
+    for f in spec["features"]:
+        nb = n if f["side"] == "item" else R
+        dim = spec["tables"][f["table"]]["dim"]
+        rows += sum(lens[o:o + nb]) * dim * 4
+        out += nb * dim * 2
+        o += nb
+    assert kind == "byte" and nbytes == rows + 4 * len(batch["ids"]) + 4 * len(batch["bag_offsets"]) + out
+
+
+def test_cvr_stage_work_counts_swiglu_per_position():
+    spec = synth.load_spec("c3")
+    batch = synth.make_batch(spec, requests=4)
+    work = bench.stage_work(spec, batch)
+    P = int(batch["seq_ids"].shape[0])
+    assert work["swiglu"] == ("flop", P * 2 * (128 * 512 + 256 * 128))
+
+
+def _write_profile(root, src_text, records):
+    os.makedirs(os.path.join(root, "profiles"))
+    os.makedirs(os.path.join(root, "src"))
+    with open(os.path.join(root, "src", "k.hip"), "w") as f:
+        f.write(src_text)
+    digest = hashlib.sha256(src_text.encode()).hexdigest()
+    with open(os.path.join(root, "profiles", "x.md"), "w") as f:
+        f.write("# counters\n\n")
+        for wl, stage, nbytes in records:
+            rec = {"workload": wl, "stage": stage, "kernel": "k", "source": "src/k.hip", "source_sha256": digest,
+                   "bytes_per_launch": nbytes}
+            f.write("traffic-json: " + json.dumps(rec) + "\n")
+
+
+def test_traffic_lookup_matches_workload_and_stage_and_drops_stale_figures(tmp_path, monkeypatch):
+    root = str(tmp_path)
+    _write_profile(root, "kernel v1\n", [("c2", "mlp_gemm", 111), ("c5", "mlp_gemm", 222), ("c2", "gather_pool", 333)])
+    monkeypatch.setattr(bench, "ROOT", root)
+    assert bench.measured_traffic("c2", "mlp_gemm") == (111, "x.md")
+    assert bench.measured_traffic("c5", "mlp_gemm") == (222, "x.md")
+    assert bench.measured_traffic("c2", "gather_pool") == (333, "x.md")
+    assert bench.measured_traffic("c4", "swiglu") == (None, None)
+    with open(os.path.join(root, "src", "k.hip"), "w") as f:
+        f.write("kernel v2\n")
+    nbytes, source = bench.measured_traffic("c2", "mlp_gemm")
+    assert nbytes is None and "stale" in source
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("workload", ["c2", "c5"])
+def test_committed_traffic_records_name_existing_sources(workload):
+    nbytes, source = bench.measured_traffic(workload, "mlp_gemm")
+    assert source is not None
