@@ -174,8 +174,9 @@ def main():
                          "hardware-counter run can scale its byte counters against a known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with no "
-              "collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library scores on one GPU (requests would shard across GPUs "
+              "with no collective, each GPU holding its own copy of tables and weights). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
