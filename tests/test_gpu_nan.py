@@ -94,3 +94,49 @@ def test_nan_passes_the_clamp_dlrm():
     others = np.array([c for c in range(n) if c != c0])
     assert np.array_equal(dirty[others], clean[others])
     m.close()
+
+
+def test_nan_passes_the_clamps_cvr_many_candidates():
+    """Requests of 48 candidates: sequences encoded once per request, the MFMA attention over a
+    request's shared states and the per-request tokenizer block.  A NaN in a row of one request's
+    sequence makes all of that request's candidates NaN; a NaN in an item row read by one
+    candidate makes that candidate NaN; every other candidate is unchanged bit for bit."""
+    spec = synth.load_spec("c3")
+    R, C, K = 3, 48, spec["n_tasks"]
+    batch = synth.make_batch(spec, requests=R, candidates=C)
+    n = R * C
+    tables = cv.device_tables(spec, "stress")
+    m, _ = build_model(spec, "stress", debug=False, tables=tables)
+    _, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    clean = _scores(out, n, K)
+    assert np.isfinite(clean).all()
+
+    so, sid = batch["seq_offsets"], batch["seq_ids"]
+    owner = np.empty(sid.shape[0], np.int64)
+    for s in range(so.shape[0]):
+        for r in range(R):
+            owner[so[s, r]:so[s, r + 1]] = r
+    x, r_seq = _id_used_once(sid[:, 0], owner)
+    fi = next(i for i, f in enumerate(spec["features"]) if f["side"] == "item")
+    base = sum(R if f["side"] != "item" else n for f in spec["features"][:fi])
+    bo, ids = batch["bag_offsets"], batch["ids"]
+    keep = [c for c in range(n) if c // C != r_seq]
+    vals = np.concatenate([ids[bo[base + c]:bo[base + c + 1]] for c in keep])
+    own = np.concatenate([np.full(bo[base + c + 1] - bo[base + c], c) for c in keep])
+    z, c_item = _id_used_once(vals, own)
+    seq_table = spec["seq"]["columns"][0]["table"]
+    item_table = spec["features"][fi]["table"]
+    banner(f"c3 x48 NaN: sequence table {seq_table} row {x} (request {r_seq}), table {item_table} row {z} "
+           f"(candidate {c_item})")
+    tables[seq_table][x, 9] = float("nan")
+    tables[item_table][z, 2] = float("nan")
+    torch.cuda.synchronize()
+    _, out, st = run(m, batch)
+    assert st == cv.CVR_OK
+    dirty = _scores(out, n, K)
+    hit = set(range(r_seq * C, (r_seq + 1) * C)) | {c_item}
+    assert np.isnan(dirty[sorted(hit)]).all()
+    others = [c for c in range(n) if c not in hit]
+    assert np.array_equal(dirty[others], clean[others])
+    m.close()
