@@ -202,6 +202,9 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         auto put = [&](int j, int v4, const bf16x4& o) {
           *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + j * 32 + 8 * v4 + 4 * (lane >> 5)]) = o;
         };
+        // The matrix phase runs at a raised wave priority, so the consumer on this SIMD fills the
+        // vector unit around it rather than the other way round (measured: 1-3% per launch).
+        __builtin_amdgcn_s_setprio(2);
         // Units 0-31 of the gate and up tiles first; their SiLU (vector and transcendental
         // instructions) is interleaved with the matrix instructions of units 32-63.
 #pragma unroll
@@ -220,6 +223,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
           if (k & 1) put(0, v4, o);
           __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs and SiLU together
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
 #pragma unroll
