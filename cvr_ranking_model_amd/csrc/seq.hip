@@ -11,7 +11,7 @@
 //
 // swiglu_kernel, per chunk of 32 positions (4 producer + 4 consumer waves):
 //   1. gather: each position's 4 rows (fp32) -> clamp -> bf16 -> LDS tile E [32][128];
-//   2. gate|up = W_gu E^T (MFMA 32x32x16, fp32 accumulate); producer w owns gate units
+//   2. gate|up = W_gu E^T (MFMA 16x16x32, fp32 accumulate); producer w owns gate units
 //      64w..64w+63 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
 //      registers and written to LDS as bf16 (the input of the down projection);
 //   3. H = A W_down^T + b (MFMA 32x32x16; the bias starts one of the two accumulators),
@@ -133,7 +133,9 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   auto desc_of = [&](int i) { return p.desc[c_begin + (i < n ? i : n - 1)]; };
 
   if (producer) {
-    V8 wg[4][kD / 16];  // gate tiles 0,1 and up tiles 2,3: units 64w + 32(j%2) + lane%32
+    // gate (h = 0) and up (h = 1) weights of unit group q (units 64w + 16q + lane%16), k step ks:
+    // the 16x16x32 A operand, k = 32ks + 8(lane/16) .. +7
+    V8 wg[4][2][kD / 32];
     float* bs = Bs[rw];
     int cur_s = -1;
     int2 dm1 = make_int2(0, 0), dm2 = make_int2(0, 0);  // descriptors of chunks i-1, i-2
@@ -161,11 +163,14 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         if (s != cur_s) {
           const bf16* Wgu = p.Wgu + (int64_t)s * p.wgu_gstride;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int u = (j < 2 ? 0 : kHid) + rw * 64 + (j & 1) * 32 + lr;
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int k = 0; k < kD / 16; ++k) wg[j][k] = *reinterpret_cast<const V8*>(Wgu + (int64_t)u * kD + k * 16 + lk);
-          }
+            for (int h = 0; h < 2; ++h) {
+              const int u = h * kHid + rw * 64 + 16 * q + (lane & 15);
+#pragma unroll
+              for (int ks = 0; ks < kD / 32; ++ks)
+                wg[q][h][ks] = *reinterpret_cast<const V8*>(Wgu + (int64_t)u * kD + 32 * ks + 8 * (lane >> 4));
+            }
           const float* bgu = p.bgu + (int64_t)s * p.bgu_gstride + rw * 64 + lane;
           const float bg = bgu[0], bu = bgu[kHid];
           bs[lane] = bg;
@@ -173,63 +178,64 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
           cur_s = s;
         }
         const int b = i & 1;
-        // The accumulators start at the biases (gate tiles 0-1, up tiles 2-3): element v of tile
-        // j is hidden unit (j & 1) * 32 + 8 * (v / 4) + 4 * (lane / 32) + v % 4.
-        f32x16 acc[4];
+        // Tiles of 16 hidden units x 16 positions (MFMA 16x16x32): unit group q, gate (h = 0) or
+        // up (h = 1), positions 16pg .. +15.  Lane holds units 16q + 4(lane/16) + v, v = 0..3,
+        // for position 16pg + lane%16; the accumulators start at the biases.
+        f32x4 acc[4][2][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const float4 bb = *reinterpret_cast<const float4*>(
-                &bs[(j < 2 ? 0 : 64) + (j & 1) * 32 + 8 * v4 + 4 * (lane >> 5)]);
-            acc[j][4 * v4] = bb.x;
-            acc[j][4 * v4 + 1] = bb.y;
-            acc[j][4 * v4 + 2] = bb.z;
-            acc[j][4 * v4 + 3] = bb.w;
+          for (int h = 0; h < 2; ++h) {
+            const float4 bb = *reinterpret_cast<const float4*>(&bs[64 * h + 16 * q + 4 * (lane >> 4)]);
+#pragma unroll
+            for (int pg = 0; pg < 2; ++pg) acc[q][h][pg] = (f32x4){bb.x, bb.y, bb.z, bb.w};
           }
-        V8 e[kD / 16];
+        V8 e[2][kD / 32];  // B operand: position 16pg + lane%16, k = 32ks + 8(lane/16) .. +7
 #pragma unroll
-        for (int k = 0; k < kD / 16; ++k) e[k] = *reinterpret_cast<const V8*>(&Es[b][lr * kEPitch + k * 16 + lk]);
-        // The tiles are hidden units x positions: lane holds units 8*v4 + 4*(lane/32) .. +3 of
-        // each tile for position lane%32, so SiLU(gate) * up of 4 units leaves as 8 bytes.
-        // exp(-g) = exp2(-log2(e) * g); g and up already hold their biases.
-        auto silu_q = [&](int j, int v4, int q) {
-          const float g = acc[j][4 * v4 + q], u = acc[j + 2][4 * v4 + q];
+        for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+          for (int ks = 0; ks < kD / 32; ++ks)
+            e[pg][ks] = *reinterpret_cast<const V8*>(&Es[b][(16 * pg + (lane & 15)) * kEPitch + 32 * ks + 8 * (lane >> 4)]);
+        // SiLU(gate) * up of element v of unit group q, positions 16pg + lane%16; four units of
+        // one position leave as 8 bytes.  exp(-g) = exp2(-log2(e) * g).
+        auto silu_v = [&](int q, int pg, int v) {
+          const float g = acc[q][0][pg][v], u = acc[q][1][pg][v];
           const float e2 = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
           const float r = __builtin_amdgcn_rcpf(1.0f + e2);
           return (bf16)((g * u) * r);
         };
-        auto put = [&](int j, int v4, const bf16x4& o) {
-          *reinterpret_cast<bf16x4*>(&As[b][lr * kAPitch + rw * 64 + j * 32 + 8 * v4 + 4 * (lane >> 5)]) = o;
+        auto silu_put = [&](int q, int pg) {
+          bf16x4 o;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] = silu_v(q, pg, v);
+          *reinterpret_cast<bf16x4*>(&As[b][(16 * pg + (lane & 15)) * kAPitch + rw * 64 + 16 * q + 4 * (lane >> 4)]) = o;
+        };
+        auto mfma_step = [&](int q, int ks) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int pg = 0; pg < 2; ++pg)
+              acc[q][h][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[q][h][ks], e[pg][ks], acc[q][h][pg], 0, 0, 0);
         };
         // The matrix phase runs at a raised wave priority, so the consumer on this SIMD fills the
-        // vector unit around it rather than the other way round (measured: 1-3% per launch).
+        // vector unit around it rather than the other way round.
         __builtin_amdgcn_s_setprio(2);
-        // Units 0-31 of the gate and up tiles first; their SiLU (vector and transcendental
-        // instructions) is interleaved with the matrix instructions of units 32-63.
+        // Unit group q's SiLU (vector and transcendental instructions) is interleaved with the
+        // matrix instructions of group q+1; only the last group's SiLU runs on its own.
 #pragma unroll
-        for (int k = 0; k < kD / 16; ++k) {
-          acc[0] = Lowp<bf16>::mfma32(wg[0][k], e[k], acc[0]);
-          acc[2] = Lowp<bf16>::mfma32(wg[2][k], e[k], acc[2]);
-        }
-        bf16x4 o;
+        for (int ks = 0; ks < kD / 32; ++ks) mfma_step(0, ks);
 #pragma unroll
-        for (int k = 0; k < kD / 16; ++k) {
-          acc[1] = Lowp<bf16>::mfma32(wg[1][k], e[k], acc[1]);
-          acc[3] = Lowp<bf16>::mfma32(wg[3][k], e[k], acc[3]);
-          const int v4 = k >> 1, q0 = (k & 1) * 2;
-          o[q0] = silu_q(0, v4, q0);
-          o[q0 + 1] = silu_q(0, v4, q0 + 1);
-          if (k & 1) put(0, v4, o);
-          __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs and SiLU together
-        }
+        for (int q = 1; q < 4; ++q)
+#pragma unroll
+          for (int ks = 0; ks < kD / 32; ++ks) {
+            mfma_step(q, ks);
+            if (ks == 1) silu_put(q - 1, 0);
+            if (ks == 3) silu_put(q - 1, 1);
+            __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs and SiLU together
+          }
         __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = silu_q(1, v4, q);
-          put(1, v4, o);
-        }
+        silu_put(3, 0);
+        silu_put(3, 1);
       }
       if (i >= 2) store_out(i);
       dm2 = dm1;
