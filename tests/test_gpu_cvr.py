@@ -220,3 +220,44 @@ def test_determinism_and_errors():
     assert st == cv.CVR_ERR_RANGE
     _, _, st = run(m, b)
     assert st == cv.CVR_OK
+
+
+def _request_alone(spec, b, r):
+    """The CSR batch of request r of batch b on its own (its bags and its sequence positions)."""
+    ex = oracle.expand(spec, b)
+    lo, hi = ex["cand_offsets"][r], ex["cand_offsets"][r + 1]
+    bags, ids = [0], []
+    for fi, f in enumerate(spec["features"]):
+        local = np.arange(lo, hi) if f["side"] == "item" else np.array([r])
+        for g in ex["bag_base"][fi] + local:
+            ids.append(ex["ids"][ex["bag_offsets"][g]:ex["bag_offsets"][g + 1]])
+            bags.append(bags[-1] + ids[-1].size)
+    so = b["seq_offsets"]
+    pos = [np.arange(so[s_, r], so[s_, r + 1]) for s_ in range(so.shape[0])]
+    lens = np.array([0] + [len(x) for x in pos])
+    alone = {"cand_offsets": np.array([0, hi - lo], np.int32), "bag_offsets": np.array(bags, np.int32),
+             "ids": np.concatenate(ids).astype(np.int32),
+             "seq_offsets": np.stack([[int(lens[:s_ + 1].sum()), int(lens[:s_ + 2].sum())] for s_ in range(so.shape[0])]
+                                     ).astype(np.int32),
+             "seq_ids": np.concatenate([b["seq_ids"][x] for x in pos]).astype(np.int32)}
+    return alone, lo, hi
+
+
+@pytest.mark.parametrize("requests,candidates", [(8, 1), (3, 48)])
+def test_request_alone_equals_in_batch(requests, candidates):
+    """A request's scores do not depend on the rest of the batch: scored alone they are bit-identical
+    to its rows in the batch (one candidate per request: per-candidate attention; 48: sequences
+    encoded once per request, MFMA attention, per-request tokenizer block)."""
+    spec = synth.load_spec("c3")
+    banner(f"c3 stress: request alone vs in batch, {requests} x {candidates}")
+    m, _ = build_model(spec, "stress", debug=False)
+    b = synth.make_batch(spec, requests=requests, candidates=candidates)
+    _, out, st = run(m, b)
+    assert st == cv.CVR_OK
+    K = spec["n_tasks"]
+    full = out.cpu().numpy().reshape(-1, K).copy()
+    for r in [0, requests - 1]:
+        alone, lo, hi = _request_alone(spec, b, r)
+        _, out1, st = run(m, alone)
+        assert st == cv.CVR_OK
+        assert np.array_equal(out1.cpu().numpy().reshape(-1, K), full[lo:hi]), r
