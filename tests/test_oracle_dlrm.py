@@ -107,3 +107,29 @@ def test_c2_shapes_and_counts():
     b = synth.make_batch(spec, requests=2)
     out = oracle.score(spec, synth.make_tables(spec), w, b)
     assert out["scores"].shape == (1000,) and out["scores"].dtype == np.float32
+
+
+def test_nan_row_reaches_exactly_its_readers():
+    """A NaN in an item row passes the clamp and the ReLUs: the candidates whose bags hold the row
+    score NaN, every other score is unchanged."""
+    spec = tiny_dlrm_spec(rows=32)
+    tables = array_tables(spec, seed=3)
+    w = synth.make_weights(spec, "stress")
+    b = synth.make_batch(spec, requests=2, candidates=6)
+    clean = oracle.score(spec, tables, w, b)["scores"]
+    assert np.isfinite(clean).all()
+    ex = oracle.expand(spec, b)
+    fi = next(i for i, f in enumerate(spec["features"]) if f["side"] == "item")
+    bags = ex["bag_base"][fi] + np.arange(ex["nbags"][fi])
+    readers = {}
+    for c, g in enumerate(bags):
+        for v in set(ex["ids"][ex["bag_offsets"][g]:ex["bag_offsets"][g + 1]].tolist()):
+            readers.setdefault(v, set()).add(c)
+    z = min(readers)
+    hit = sorted(readers[z])
+    t = [np.array(x, copy=True) for x in tables]
+    t[spec["features"][fi]["table"]][z, 1] = np.nan
+    s = oracle.score(spec, t, w, b)["scores"]
+    assert np.isnan(s[hit]).all()
+    rest = np.setdiff1d(np.arange(clean.shape[0]), hit)
+    assert np.array_equal(s[rest], clean[rest])

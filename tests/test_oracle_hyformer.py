@@ -380,3 +380,44 @@ def test_c3_shapes():
     b = synth.make_batch(spec, requests=2)
     out = oracle.score(spec, synth.make_tables(spec), w, b)
     assert out["scores"].shape == (2, 2) and out["scores"].dtype == np.float32
+
+
+def test_nan_row_reaches_exactly_its_readers():
+    """A NaN in a table row passes the clamp, the ReLUs and the softmax maxima: the candidates
+    that read the row score NaN and every other score is unchanged (the plain definition of each
+    operator; nothing in the model mixes candidates)."""
+    spec, tables, w, b = _tiny_model(C=2, rows=64)
+    clean = oracle.score(spec, tables, w, b)["scores"]
+    assert np.isfinite(clean).all()
+    ex = oracle.expand(spec, b)
+    # a row of the first sequence column read by one request only
+    so, sid = b["seq_offsets"], b["seq_ids"]
+    owner = np.full(sid.shape[0], -1)
+    for s in range(so.shape[0]):
+        for r in range(so.shape[1] - 1):
+            owner[so[s, r]:so[s, r + 1]] = r
+    col_t = spec["seq"]["columns"][0]["table"]
+    x, r1 = next((v, int(owner[sid[:, 0] == v][0])) for v in np.unique(sid[:, 0])
+                 if len(set(owner[sid[:, 0] == v])) == 1)
+    t_seq = [np.array(t, copy=True) for t in tables]
+    t_seq[col_t][x, 1] = np.nan
+    s1 = oracle.score(spec, t_seq, w, b)["scores"]
+    req1 = np.arange(ex["cand_offsets"][r1], ex["cand_offsets"][r1 + 1])
+    assert np.isnan(s1[req1]).all()
+    rest = np.setdiff1d(np.arange(clean.shape[0]), req1)
+    assert np.array_equal(s1[rest], clean[rest])
+    # a row of the first item feature read by one candidate only
+    fi = next(i for i, f in enumerate(spec["features"]) if f["side"] == "item")
+    bags = ex["bag_base"][fi] + np.arange(ex["nbags"][fi])
+    rows = [ex["ids"][ex["bag_offsets"][g]:ex["bag_offsets"][g + 1]] for g in bags]
+    users = {}
+    for c, rr in enumerate(rows):
+        for v in set(rr.tolist()):
+            users.setdefault(v, set()).add(c)
+    z, cz = next((v, next(iter(u))) for v, u in sorted(users.items()) if len(u) == 1)
+    t_item = [np.array(t, copy=True) for t in tables]
+    t_item[spec["features"][fi]["table"]][z, 0] = np.nan
+    s2 = oracle.score(spec, t_item, w, b)["scores"]
+    assert np.isnan(s2[cz]).all()
+    others = np.setdiff1d(np.arange(clean.shape[0]), [cz])
+    assert np.array_equal(s2[others], clean[others])
