@@ -23,59 +23,80 @@
 
 namespace cvr {
 
-// Exclusive scan of ceil(len / kSeqChunk) over the S*R segments (one block).
+// Positions of segment g = s * R + r, clamped to [0, n_positions] and non-decreasing.
+__device__ __forceinline__ void segment_range(const int32_t* __restrict__ seq_offsets, int R, int g, int64_t n_positions,
+                                              int64_t& a, int64_t& e) {
+  const int s = g / R, r = g % R;
+  a = seq_offsets[(int64_t)s * (R + 1) + r];
+  e = seq_offsets[(int64_t)s * (R + 1) + r + 1];
+  a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
+  e = e < a ? a : (e > n_positions ? n_positions : e);
+}
+
+// Exclusive scan of ceil(len / kSeqChunk) over the S*R segments (one block of 1024 threads):
+// thread t owns a run of consecutive segments; the run totals are scanned within each wave by
+// shuffles, then across the 16 waves.
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* __restrict__ seq_offsets, int R, int S,
                                                            int64_t n_positions, int32_t* __restrict__ chunk_off) {
-  __shared__ int32_t part[1024];
+  __shared__ int32_t wsum[16];
   const int SR = S * R;
   const int per = (SR + 1023) / 1024;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g0 = t * per;
   int32_t local = 0;
   for (int g = g0; g < g0 + per && g < SR; ++g) {
-    const int s = g / R, r = g % R;
-    int64_t a = seq_offsets[(int64_t)s * (R + 1) + r], b = seq_offsets[(int64_t)s * (R + 1) + r + 1];
-    a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
-    b = b < a ? a : (b > n_positions ? n_positions : b);
-    local += (int32_t)((b - a + kSeqChunk - 1) / kSeqChunk);
+    int64_t a, e;
+    segment_range(seq_offsets, R, g, n_positions, a, e);
+    local += (int32_t)((e - a + kSeqChunk - 1) / kSeqChunk);
   }
-  part[t] = local;
+  int32_t incl = local;  // inclusive scan within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    const int32_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  if (w == 0) {
+    int32_t x = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int32_t v = __shfl_up(x, off);
+      if (lane >= off) x += v;
+    }
+    if (lane < 16) wsum[lane] = x;  // inclusive totals of waves 0..lane
   }
-  int32_t run = part[t] - local;  // exclusive prefix of this thread's range
+  __syncthreads();
+  int32_t run = (w > 0 ? wsum[w - 1] : 0) + incl - local;  // exclusive prefix of this thread's run
   for (int g = g0; g < g0 + per && g < SR; ++g) {
     chunk_off[g] = run;
-    const int s = g / R, r = g % R;
-    int64_t a = seq_offsets[(int64_t)s * (R + 1) + r], b = seq_offsets[(int64_t)s * (R + 1) + r + 1];
-    a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
-    b = b < a ? a : (b > n_positions ? n_positions : b);
-    run += (int32_t)((b - a + kSeqChunk - 1) / kSeqChunk);
+    int64_t a, e;
+    segment_range(seq_offsets, R, g, n_positions, a, e);
+    run += (int32_t)((e - a + kSeqChunk - 1) / kSeqChunk);
   }
-  if (t == 1023) chunk_off[SR] = part[1023];
+  if (t == 1023) chunk_off[SR] = wsum[15];
 }
 
 // One descriptor per chunk: x = first position, y = (segment << 8) | positions in the chunk.
+// One thread per chunk finds its segment by binary search over the chunk offsets.
 __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restrict__ seq_offsets, int R, int S,
                                                          int64_t n_positions, const int32_t* __restrict__ chunk_off,
                                                          int2* __restrict__ desc) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= S * R) return;
-  const int s = g / R, r = g % R;
-  int64_t a = seq_offsets[(int64_t)s * (R + 1) + r], e = seq_offsets[(int64_t)s * (R + 1) + r + 1];
-  a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
-  e = e < a ? a : (e > n_positions ? n_positions : e);
-  const int c0 = chunk_off[g], c1 = chunk_off[g + 1];
-  for (int c = c0; c < c1; ++c) {
-    const int64_t p0 = a + (int64_t)(c - c0) * kSeqChunk;
-    const int64_t left = e - p0;
-    const int np = left > kSeqChunk ? kSeqChunk : (int)left;
-    desc[c] = make_int2((int)p0, (g << 8) | np);
+  const int SR = S * R;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunk_off[SR]) return;
+  int lo = 0, hi = SR;  // chunk_off[lo] <= c < chunk_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_off[mid] <= c) lo = mid;
+    else hi = mid;
   }
+  int64_t a, e;
+  segment_range(seq_offsets, R, lo, n_positions, a, e);
+  const int64_t p0 = a + (int64_t)(c - chunk_off[lo]) * kSeqChunk;
+  const int64_t left = e - p0;
+  const int np = left > kSeqChunk ? kSeqChunk : (int)left;
+  desc[c] = make_int2((int)p0, (lo << 8) | np);
 }
 
 hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
@@ -83,8 +104,9 @@ hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t 
   launch_k(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, chunk_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S * R == 0) return e;
-  launch_k(chunk_desc_kernel, dim3((S * R + 255) / 256), dim3(256), 0, st, seq_offsets, R, S, n_positions,
-                     chunk_off, desc);
+  const int64_t max_chunks = n_positions / kSeqChunk + (int64_t)S * R;  // every segment adds at most one partial chunk
+  launch_k(chunk_desc_kernel, dim3((unsigned)((max_chunks + 255) / 256)), dim3(256), 0, st, seq_offsets, R, S,
+           n_positions, chunk_off, desc);
   return hipGetLastError();
 }
 
