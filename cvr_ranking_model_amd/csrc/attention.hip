@@ -43,7 +43,7 @@ __device__ __forceinline__ void shfl_state(SoftState& dst, const SoftState& src,
 
 __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
   const int c = blockIdx.x;
-  const int s = blockIdx.y;
+  const int s = p.S - 1 - (int)blockIdx.y;  // the last (longest) sequence first: a shorter tail
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 3, sub = lane & 7;
   const int r = p.cand_req[c];
