@@ -169,6 +169,11 @@ static void plan_weights(cvr_model* m) {
       for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc1.bias", s.mixer_hidden, 1, false);
       for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc2.weight", mw, s.mixer_hidden, true);
       for (int h = 0; h < s.mixer_heads; ++h) add(L + ".mix." + std::to_string(h) + ".fc2.bias", mw, 1, false);
+      if (token_mix_supported(T, d, s.mixer_heads, s.mixer_hidden))
+        for (int h = 0; h < s.mixer_heads; ++h) {
+          m->w[m->widx.at(L + ".mix." + std::to_string(h) + ".fc1.weight")].pack = 1;
+          m->w[m->widx.at(L + ".mix." + std::to_string(h) + ".fc2.weight")].pack = 2;
+        }
     }
     const int zd = T * d;
     // Expert rows, then every task's gate rows, back to back: one GEMM computes the experts and
@@ -284,7 +289,8 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
     if (!weights[i].data) { delete m; return fail(nullptr, CVR_ERR_ARG, "weight data is null"); }
     if (seen[it->second]++) { std::string n = weights[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "weight given twice: " + n); }
     hipError_t he;
-    if (e.matrix) he = launch_convert(weights[i].data, m->arena + e.off, e.rows * e.cols, m->spec.lowp, s);
+    if (e.pack) he = launch_mix_pack(weights[i].data, m->arena + e.off, e.pack, s);
+    else if (e.matrix) he = launch_convert(weights[i].data, m->arena + e.off, e.rows * e.cols, m->spec.lowp, s);
     else he = hipMemcpyAsync(m->arena + e.off, weights[i].data, (size_t)e.rows * 4, hipMemcpyDeviceToDevice, s);
     if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("packing weights: ") + hipGetErrorString(he)); }
   }

@@ -250,17 +250,21 @@ struct TokenMixParams {
   const float* Y;               // [n][T][d] fp32
   float* Z;                     // [n][T][d] fp32
   int32_t n, T, d, H;
-  const __bf16* W1;             // head h: W1 + h*w1_gstride, [256][T*8]
+  const __bf16* W1;             // head h: W1 + h*w1_gstride, [256][T*8] packed by launch_mix_pack
   int64_t w1_gstride;
   const float* b1;
   int64_t b1_gstride;
-  const __bf16* W2;             // head h: W2 + h*w2_gstride, [T*8][256]
+  const __bf16* W2;             // head h: W2 + h*w2_gstride, [T*8][256] packed by launch_mix_pack
   int64_t w2_gstride;
   const float* b2;
   int64_t b2_gstride;
 };
 bool token_mix_supported(int32_t T, int32_t d, int32_t H, int32_t hidden);
 hipError_t launch_token_mix(const TokenMixParams& p, hipStream_t st);
+// One head's first (which = 1, [256][128]) or second (which = 2, [128][256]) mixer Linear,
+// fp32 row-major, rounded to bf16 and stored in the order the fused mixer's waves read their
+// MFMA operands: every 16-byte piece a lane loads sits next to its neighbours' pieces.
+hipError_t launch_mix_pack(const float* src, void* dst, int which, hipStream_t st);
 
 // ---------------------------------------------------------------- PLE gates and heads (B10-B11)
 struct PleGateParams {

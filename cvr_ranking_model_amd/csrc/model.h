@@ -38,6 +38,8 @@ struct WEntry {
   int64_t rows, cols;
   bool matrix;
   size_t off;
+  // 0: row-major; 1 / 2: the fused token mixer's first / second Linear in MFMA fragment order
+  int pack = 0;
 };
 
 // A run of consecutive same-side features in the model input.

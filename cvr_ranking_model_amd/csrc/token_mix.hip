@@ -15,7 +15,10 @@
 //      outputs 8t + j .. 8t + j + 3, which revert to 4 consecutive columns of token t; the
 //      epilogue adds the bias, then the residual, and writes 16 bytes of Z.
 // Weights are read from global memory (L2-resident: 128 KB per head) straight into MFMA
-// operand registers.  The hidden activations never leave LDS.
+// operand registers.  They are stored in fragment order (packed once, when the model is
+// built): the 16-byte pieces the 64 lanes of a wave take for one MFMA lie back to back, so a
+// load instruction reads 1 KB of whole cache lines instead of 32 bytes from each of 32 rows.
+// The hidden activations never leave LDS.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -43,39 +46,36 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p) 
   constexpr int hw = 8;
 
   // The first Linear's weight fragments do not depend on the tokens: fetch them first.
-  const bf16* W1 = p.W1 + (int64_t)h * p.w1_gstride;
+  // piece (w, k, a, lane): W1[64w + 32a + lane%32][16k + 8(lane/32) .. +7]
+  const bf16x8* W1 = reinterpret_cast<const bf16x8*>(p.W1 + (int64_t)h * p.w1_gstride) + 1024 * wave + lane;
   bf16x8 wa[kMixW / 16][2];
 #pragma unroll
   for (int k = 0; k < kMixW / 16; ++k)
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-      wa[k][a] = *reinterpret_cast<const bf16x8*>(W1 + (int64_t)(64 * wave + 32 * a + lr) * kMixW + 16 * k + lk);
+    for (int a = 0; a < 2; ++a) wa[k][a] = W1[64 * (2 * k + a)];
 
-  // 1. split + mix: row m, element 8t + j <- Y[c0 + m][t][8h + j]; all loads first
-  constexpr int kPer = kMixTM * T / 256;
-  float4 ya[kPer], yb[kPer];
+  // 1. split + mix: row m, element 8t + j <- Y[c0 + m][t][8h + j]; all loads first.  Lanes 2i
+  // and 2i + 1 load the two 16-byte halves of one token's 32 bytes.
+  constexpr int kPer = kMixTM * T * 2 / 256;
+  float4 ya[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const int i = tid + 256 * r, m = i / T, t = i % T, c = c0 + m;
-    ya[r] = yb[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < p.n) {
-      const float4* src = reinterpret_cast<const float4*>(p.Y + ((int64_t)c * T + t) * p.d + h * hw);
-      ya[r] = src[0];
-      yb[r] = src[1];
-    }
+    const int q = tid + 256 * r, m = q >> 5, t = (q >> 1) & (T - 1), half = q & 1, c = c0 + m;
+    ya[r] = c < p.n ? *reinterpret_cast<const float4*>(p.Y + ((int64_t)c * T + t) * p.d + h * hw + 4 * half)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const int i = tid + 256 * r, m = i / T, t = i % T;
-    bf16x8 v;
+    const int q = tid + 256 * r, m = q >> 5, t = (q >> 1) & (T - 1), half = q & 1;
+    bf16x4 v;
     v[0] = (bf16)ya[r].x; v[1] = (bf16)ya[r].y; v[2] = (bf16)ya[r].z; v[3] = (bf16)ya[r].w;
-    v[4] = (bf16)yb[r].x; v[5] = (bf16)yb[r].y; v[6] = (bf16)yb[r].z; v[7] = (bf16)yb[r].w;
-    *reinterpret_cast<bf16x8*>(&Xs[m * kXPitch + t * 8]) = v;
+    *reinterpret_cast<bf16x4*>(&Xs[m * kXPitch + t * 8 + 4 * half]) = v;
   }
   __syncthreads();
 
   // 2. hidden^T (units 64w .. 64w+63, 64 candidates) = W1 X^T, K = 128
-  const bf16* W2 = p.W2 + (int64_t)h * p.w2_gstride;
+  // piece (w, k, lane): W2[32w + lane%32][16k + 8(lane/32) .. +7]
+  const bf16x8* W2 = reinterpret_cast<const bf16x8*>(p.W2 + (int64_t)h * p.w2_gstride) + 1024 * wave + lane;
   bf16x8 w2f[kMixHid / 16];
   {
     const float* b1 = p.b1 + (int64_t)h * p.b1_gstride;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p) 
     // the second Linear's fragments load while the first's results are finished
 #pragma unroll
     for (int k = 0; k < kMixHid / 16; ++k)
-      w2f[k] = *reinterpret_cast<const bf16x8*>(W2 + (int64_t)(32 * wave + lr) * kMixHid + 16 * k + lk);
+      w2f[k] = W2[64 * k];
     // element v of tile (a, b): unit 64w + 32a + 8(v/4) + 4(lane/32) + v%4, candidate 32b + lane%32
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -167,6 +167,30 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p) 
       }
     }
   }
+}
+
+__global__ void mix_pack_kernel(const float* __restrict__ src, bf16* __restrict__ dst, int which) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;  // 16-byte piece of the packed matrix
+  if (g >= kMixW * kMixHid / 8) return;
+  const int lane = g & 63, lr = lane & 31, lk = (lane >> 5) * 8, w = g >> 10;
+  int row, col, ld;
+  if (which == 1) {  // g = ((w * 8 + k) * 2 + a) * 64 + lane
+    row = 64 * w + 32 * ((g >> 6) & 1) + lr;
+    col = 16 * ((g >> 7) & 7) + lk;
+    ld = kMixW;
+  } else {           // g = (w * 16 + k) * 64 + lane
+    row = 32 * w + lr;
+    col = 16 * ((g >> 6) & 15) + lk;
+    ld = kMixHid;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dst[8 * g + j] = Lowp<bf16>::from_f32(src[row * ld + col + j]);
+}
+
+hipError_t launch_mix_pack(const float* src, void* dst, int which, hipStream_t st) {
+  if (which != 1 && which != 2) return hipErrorInvalidValue;
+  launch_k(mix_pack_kernel, dim3(kMixW * kMixHid / 8 / 256), dim3(256), 0, st, src, (bf16*)dst, which);
+  return hipGetLastError();
 }
 
 bool token_mix_supported(int32_t T, int32_t d, int32_t H, int32_t hidden) {
