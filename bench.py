@@ -86,9 +86,17 @@ def stage_work(spec, batch):
     so = batch["seq_offsets"].astype(np.int64)
     cand_req = np.repeat(np.arange(R), np.diff(batch["cand_offsets"]))
     pos_per_cand = sum((so[q, cand_req + 1] - so[q, cand_req]).sum() for q in range(S))
-    work["attention"] = ("byte", L * int(pos_per_cand) * d * 2)
+    if n >= 16 * R:
+        # requests of many candidates take the MFMA kernel, which reads a request's states once
+        # per 32-candidate tile: a score and a weighted sum (2d FLOP each) per (candidate, position)
+        work["attention"] = ("flop", L * int(pos_per_cand) * 4 * d)
+    else:
+        work["attention"] = ("byte", L * int(pos_per_cand) * d * 2)
     H = spec["mixer_heads"]
     work["mixer_gemm"] = ("flop", L * n * H * (lin("layer.0.mix.0.fc1.weight") + lin("layer.0.mix.0.fc2.weight")))
+    # the fused mixer reads and writes the fp32 token matrix once per layer
+    T = spec["n_tokens"] + S
+    work["mixer_gemm_bytes"] = ("byte", L * n * T * d * 4 * 2)
     work["ple_gemm"] = ("flop", n * spec["n_experts"] * lin("ple.expert.0.weight"))
     work["head_gemm"] = ("flop", n * spec["n_tasks"] * lin("head.0.fc1.weight"))
     return work
@@ -312,8 +320,8 @@ def main():
                              frac=round(ach / HBM_PEAK_GBS, 4))
             entry["per_launch"] = per_launch
             entry["avg_launch_us"] = round(avg_s * 1e6, 2)
-        if st == "swiglu" and "swiglu_bytes" in work:
-            b = work["swiglu_bytes"][1] * calls / launches
+        if st + "_bytes" in work:
+            b = work[st + "_bytes"][1] * calls / launches
             entry["hbm_GBs"] = round(b / (ms / launches / 1e3) / 1e9, 1)
         table[st] = entry
     # the dominant stage's figures come from the timed region's own events

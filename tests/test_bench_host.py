@@ -44,6 +44,18 @@ def test_cvr_stage_work_counts_swiglu_per_position():
     assert work["swiglu"] == ("flop", P * 2 * (128 * 512 + 256 * 128))
 
 
+def test_attention_work_follows_the_kernel_choice():
+    spec = synth.load_spec("c3")
+    L, d = spec["n_layers"], spec["d"]
+    for R, C in [(4, 1), (2, 48)]:
+        batch = synth.make_batch(spec, requests=R, candidates=C)
+        so = batch["seq_offsets"].astype(int)
+        pos = sum(C * int(so[q, r + 1] - so[q, r]) for q in range(so.shape[0]) for r in range(R))
+        kind, amount = bench.stage_work(spec, batch)["attention"]
+        # one candidate per request: states streamed per candidate; 48: the MFMA kernel
+        assert (kind, amount) == (("byte", L * pos * d * 2) if C < 16 else ("flop", L * pos * 4 * d))
+
+
 def _write_profile(root, src_text, records):
     os.makedirs(os.path.join(root, "profiles"))
     os.makedirs(os.path.join(root, "src"))
