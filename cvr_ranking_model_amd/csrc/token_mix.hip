@@ -5,47 +5,55 @@
 // own FFN 128 -> 256 (ReLU) -> 128, and the result is scattered back (revert) onto head h of
 // every token and added to the input: Z[t][8h + j] = Y[t][8h + j] + F_h[8t + j].
 //
-// One block of 4 waves per (64 candidates, head h), one kernel for the whole mixer:
-//   1. split + mix: the block gathers Y[c][t][8h .. 8h+7] for its candidates, rounds to bf16
-//      (the Linear input rounding) and stores mixed-token rows in LDS;
+// One block of 4 waves per (head h, run of 64-candidate tiles); the head's weights are loaded
+// into MFMA operand registers once and serve every tile of the run.  Per tile:
+//   1. split + mix: the block holds Y[c][t][8h .. 8h+7] of its 64 candidates in LDS as fp32
+//      (loaded into registers while the previous tile computed);
 //   2. the first Linear as a transposed product, hidden^T = W1 X^T (MFMA 32x32x16, fp32
-//      accumulation): each lane ends with 4 consecutive hidden units of one candidate, adds
-//      the bias, applies ReLU, rounds to bf16 and stores them to LDS as 8 bytes;
+//      accumulation), X rounded to bf16 (the Linear input rounding) as its fragments are read:
+//      each lane ends with 4 consecutive hidden units of one candidate, adds the bias, applies
+//      ReLU, rounds to bf16 and stores them to LDS as 8 bytes;
 //   3. the second Linear the same way, F^T = W2 hidden^T: each lane ends with 4 consecutive
 //      outputs 8t + j .. 8t + j + 3, which revert to 4 consecutive columns of token t; the
-//      epilogue adds the bias, then the residual, and writes 16 bytes of Z.
-// Weights are read from global memory (L2-resident: 128 KB per head) straight into MFMA
-// operand registers.  They are stored in fragment order (packed once, when the model is
-// built): the 16-byte pieces the 64 lanes of a wave take for one MFMA lie back to back, so a
-// load instruction reads 1 KB of whole cache lines instead of 32 bytes from each of 32 rows.
-// The hidden activations never leave LDS.
+//      epilogue adds the bias, then the residual (from the fp32 tile in LDS), and writes 16
+//      bytes of Z.
+// Weights come from global memory (L2-resident: 128 KB per head) in fragment order (packed
+// once, when the model is built): the 16-byte pieces the 64 lanes of a wave take for one MFMA
+// lie back to back, so a load instruction reads 1 KB of whole cache lines.  The hidden
+// activations never leave LDS.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace cvr {
 
-constexpr int kMixTM = 64;            // candidates per block
+constexpr int kMixTM = 64;            // candidates per tile
 constexpr int kMixW = 128;            // mixed-token width (16 tokens x 8)
 constexpr int kMixHid = 256;          // FFN hidden width
-constexpr int kXPitch = kMixW + 8;    // bf16 elements per LDS row (16-byte reads land on distinct banks)
-constexpr int kHPitch = kMixHid + 8;
+constexpr int kYPitch = kMixW + 4;    // fp32 elements per LDS row (16-byte reads of 16 rows cover all banks)
+constexpr int kHPitch = kMixHid + 8;  // bf16 elements per LDS row
+constexpr int kMixBlocks = 256;       // one block per CU: the weights fill the register file
 
-__global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p) {
-  __shared__ __align__(16) bf16 Xs[kMixTM * kXPitch];
+// Block b runs on XCD b % 8.  Its slot b / 8 there picks the head (slot % H) and one of
+// `groups` tile runs (slot / H); run r = group * 8 + XCD takes tiles r, r + 8 * groups, ...
+// The 16 heads of a run sit on one XCD and walk the same tiles together, sharing the token
+// rows through its L2 (each head reads and writes 32 bytes of every 512-byte token row).
+__global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p, int groups) {
+  __shared__ __align__(16) float Ys[kMixTM * kYPitch];
   __shared__ __align__(16) bf16 Hs[kMixTM * kHPitch];
-  // Block b runs on XCD b % 8; its slot b / 8 there picks (tile, head) so that the 16 heads of
-  // a candidate tile follow each other on one XCD and share the token rows through its L2
-  // (each head reads and writes only 32 bytes of every 512-byte token row).
+  __shared__ __align__(16) float bs1[kMixHid];
+  __shared__ __align__(16) float bs2[kMixW];
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int tile = (slot / p.H) * 8 + xcd, h = slot % p.H;
-  const int c0 = tile * kMixTM;
-  if (c0 >= p.n) return;
+  const int h = slot % p.H, run = (slot / p.H) * 8 + xcd, stride = 8 * groups;
+  const int tiles = (p.n + kMixTM - 1) / kMixTM;
+  int tile = run;
+  if (tile >= tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   constexpr int T = kMixW / 8;  // 16 tokens of 8 columns per head (checked at launch)
   constexpr int hw = 8;
 
-  // The first Linear's weight fragments do not depend on the tokens: fetch them first.
   // piece (w, k, a, lane): W1[64w + 32a + lane%32][16k + 8(lane/32) .. +7]
   const bf16x8* W1 = reinterpret_cast<const bf16x8*>(p.W1 + (int64_t)h * p.w1_gstride) + 1024 * wave + lane;
   bf16x8 wa[kMixW / 16][2];
@@ -53,119 +61,125 @@ __global__ __launch_bounds__(256) void token_mix_kernel(const TokenMixParams p) 
   for (int k = 0; k < kMixW / 16; ++k)
 #pragma unroll
     for (int a = 0; a < 2; ++a) wa[k][a] = W1[64 * (2 * k + a)];
-
-  // 1. split + mix: row m, element 8t + j <- Y[c0 + m][t][8h + j]; all loads first.  Lanes 2i
-  // and 2i + 1 load the two 16-byte halves of one token's 32 bytes.
-  constexpr int kPer = kMixTM * T * 2 / 256;
-  float4 ya[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int q = tid + 256 * r, m = q >> 5, t = (q >> 1) & (T - 1), half = q & 1, c = c0 + m;
-    ya[r] = c < p.n ? *reinterpret_cast<const float4*>(p.Y + ((int64_t)c * T + t) * p.d + h * hw + 4 * half)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int q = tid + 256 * r, m = q >> 5, t = (q >> 1) & (T - 1), half = q & 1;
-    bf16x4 v;
-    v[0] = (bf16)ya[r].x; v[1] = (bf16)ya[r].y; v[2] = (bf16)ya[r].z; v[3] = (bf16)ya[r].w;
-    *reinterpret_cast<bf16x4*>(&Xs[m * kXPitch + t * 8 + 4 * half]) = v;
-  }
-  __syncthreads();
-
-  // 2. hidden^T (units 64w .. 64w+63, 64 candidates) = W1 X^T, K = 128
   // piece (w, k, lane): W2[32w + lane%32][16k + 8(lane/32) .. +7]
   const bf16x8* W2 = reinterpret_cast<const bf16x8*>(p.W2 + (int64_t)h * p.w2_gstride) + 1024 * wave + lane;
   bf16x8 w2f[kMixHid / 16];
-  {
-    const float* b1 = p.b1 + (int64_t)h * p.b1_gstride;
-    f32x16 acc[2][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+  for (int k = 0; k < kMixHid / 16; ++k) w2f[k] = W2[64 * k];
+  bs1[tid] = p.b1[(int64_t)h * p.b1_gstride + tid];
+  if (tid < kMixW) bs2[tid] = p.b2[(int64_t)h * p.b2_gstride + tid];
+
+  // Tokens of one tile: row m, element 8t + j <- Y[c0 + m][t][8h + j].  Lanes 2i and 2i + 1
+  // load the two 16-byte halves of one token's 32 bytes.
+  constexpr int kPer = kMixTM * T * 2 / 256;
+  float4 ya[kPer];
+  auto load_tile = [&](int tl) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int r = 0; r < kPer; ++r) {
+      const int q = tid + 256 * r, m = q >> 5, t = (q >> 1) & (T - 1), half = q & 1, c = tl * kMixTM + m;
+      ya[r] = c < p.n ? *reinterpret_cast<const float4*>(p.Y + ((int64_t)c * T + t) * p.d + h * hw + 4 * half)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto stage_tile = [&]() {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMixW / 16; ++k) {
-      bf16x8 xb[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) xb[b] = *reinterpret_cast<const bf16x8*>(&Xs[(32 * b + lr) * kXPitch + 16 * k + lk]);
+    for (int r = 0; r < kPer; ++r) {
+      const int q = tid + 256 * r, m = q >> 5, t = (q >> 1) & (T - 1), half = q & 1;
+      *reinterpret_cast<float4*>(&Ys[m * kYPitch + t * 8 + 4 * half]) = ya[r];
+    }
+  };
+  load_tile(tile);
+  stage_tile();
+  __syncthreads();
+
+  for (;;) {
+    const int next = tile + stride;
+    if (next < tiles) load_tile(next);  // in flight while this tile computes
+    const int c0 = tile * kMixTM;
+
+    // 2. hidden^T (units 64w .. 64w+63, 64 candidates) = W1 X^T, K = 128
+    {
+      f32x16 acc[2][2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = Lowp<bf16>::mfma32(wa[k][a], xb[b], acc[a][b]);
-    }
-    // the second Linear's fragments load while the first's results are finished
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int k = 0; k < kMixHid / 16; ++k)
-      w2f[k] = W2[64 * k];
-    // element v of tile (a, b): unit 64w + 32a + 8(v/4) + 4(lane/32) + v%4, candidate 32b + lane%32
+          for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int u = 64 * wave + 32 * a + 8 * v4 + (lk >> 1);
-        const float4 bb = *reinterpret_cast<const float4*>(b1 + u);
-        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+      for (int k = 0; k < kMixW / 16; ++k) {
+        bf16x8 xb[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          bf16x4 o;
+          const float* src = &Ys[(32 * b + lr) * kYPitch + 16 * k + lk];
+          const float4 x0 = *reinterpret_cast<const float4*>(src), x1 = *reinterpret_cast<const float4*>(src + 4);
+          xb[b][0] = (bf16)x0.x; xb[b][1] = (bf16)x0.y; xb[b][2] = (bf16)x0.z; xb[b][3] = (bf16)x0.w;
+          xb[b][4] = (bf16)x1.x; xb[b][5] = (bf16)x1.y; xb[b][6] = (bf16)x1.z; xb[b][7] = (bf16)x1.w;
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (bf16)relu_f32(acc[a][b][4 * v4 + q] + bv[q]);
-          *reinterpret_cast<bf16x4*>(&Hs[(32 * b + lr) * kHPitch + u]) = o;
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) acc[a][b] = Lowp<bf16>::mfma32(wa[k][a], xb[b], acc[a][b]);
+      }
+      // element v of tile (a, b): unit 64w + 32a + 8(v/4) + 4(lane/32) + v%4, candidate 32b + lane%32
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int u = 64 * wave + 32 * a + 8 * v4 + (lk >> 1);
+          const float4 bb = *reinterpret_cast<const float4*>(&bs1[u]);
+          const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = (bf16)relu_f32(acc[a][b][4 * v4 + q] + bv[q]);
+            *reinterpret_cast<bf16x4*>(&Hs[(32 * b + lr) * kHPitch + u]) = o;
+          }
+        }
+    }
+    __syncthreads();
+
+    // 3. F^T (outputs 32w .. 32w+31, 64 candidates) = W2 hidden^T, K = 256; revert + residual
+    {
+      f32x16 acc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMixHid / 16; ++k) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8 hb = *reinterpret_cast<const bf16x8*>(&Hs[(32 * b + lr) * kHPitch + 16 * k + lk]);
+          acc[b] = Lowp<bf16>::mfma32(w2f[k], hb, acc[b]);
         }
       }
-  }
-  __syncthreads();
-
-  // 3. F^T (outputs 32w .. 32w+31, 64 candidates) = W2 hidden^T, K = 256; revert + residual
-  {
-    const float* b2 = p.b2 + (int64_t)h * p.b2_gstride;
-    // element v of tile b: output 32w + 8(v/4) + 4(lane/32) + v%4 = 8t + j, candidate 32b + lane%32;
-    // the residual rows load before the products
-    float4 y[4][2];
+      // element v of tile b: output 32w + 8(v/4) + 4(lane/32) + v%4 = 8t + j, candidate 32b + lane%32
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int o = 32 * wave + 8 * v4 + (lk >> 1);
-      const int t = o / hw, j = o % hw;
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int o = 32 * wave + 8 * v4 + (lk >> 1);
+        const int t = o / hw, j = o % hw;
+        const float4 bb = *reinterpret_cast<const float4*>(&bs2[o]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int c = c0 + 32 * b + lr;
-        y[v4][b] = c < p.n ? *reinterpret_cast<const float4*>(p.Y + ((int64_t)c * T + t) * p.d + h * hw + j)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int b = 0; b < 2; ++b) {
+          const int c = c0 + 32 * b + lr;
+          if (c >= p.n) continue;
+          const float4 y = *reinterpret_cast<const float4*>(&Ys[(32 * b + lr) * kYPitch + o]);
+          float4 z;
+          z.x = y.x + (acc[b][4 * v4 + 0] + bb.x);
+          z.y = y.y + (acc[b][4 * v4 + 1] + bb.y);
+          z.z = y.z + (acc[b][4 * v4 + 2] + bb.z);
+          z.w = y.w + (acc[b][4 * v4 + 3] + bb.w);
+          *reinterpret_cast<float4*>(p.Z + ((int64_t)c * T + t) * p.d + h * hw + j) = z;
+        }
       }
     }
-    f32x16 acc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMixHid / 16; ++k) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bf16x8 hb = *reinterpret_cast<const bf16x8*>(&Hs[(32 * b + lr) * kHPitch + 16 * k + lk]);
-        acc[b] = Lowp<bf16>::mfma32(w2f[k], hb, acc[b]);
-      }
-    }
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int o = 32 * wave + 8 * v4 + (lk >> 1);
-      const int t = o / hw, j = o % hw;
-      const float4 bb = *reinterpret_cast<const float4*>(b2 + o);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int c = c0 + 32 * b + lr;
-        if (c >= p.n) continue;
-        float4 z;
-        z.x = y[v4][b].x + (acc[b][4 * v4 + 0] + bb.x);
-        z.y = y[v4][b].y + (acc[b][4 * v4 + 1] + bb.y);
-        z.z = y[v4][b].z + (acc[b][4 * v4 + 2] + bb.z);
-        z.w = y[v4][b].w + (acc[b][4 * v4 + 3] + bb.w);
-        *reinterpret_cast<float4*>(p.Z + ((int64_t)c * T + t) * p.d + h * hw + j) = z;
-      }
-    }
+    if (next >= tiles) break;
+    __syncthreads();  // every read of this tile's Ys and Hs is done
+    stage_tile();
+    __syncthreads();
+    tile = next;
   }
 }
 
@@ -201,7 +215,9 @@ hipError_t launch_token_mix(const TokenMixParams& p, hipStream_t st) {
   if (p.n <= 0) return hipSuccess;
   if (!token_mix_supported(p.T, p.d, p.H, kMixHid)) return hipErrorInvalidValue;
   const int tiles = (p.n + kMixTM - 1) / kMixTM;
-  launch_k(token_mix_kernel, dim3((tiles + 7) / 8 * 8 * p.H), dim3(256), 0, st, p);
+  int groups = kMixBlocks / (8 * p.H);
+  groups = std::max(1, std::min(groups, (tiles + 7) / 8));
+  launch_k(token_mix_kernel, dim3(8 * groups * p.H), dim3(256), 0, st, p, groups);
   return hipGetLastError();
 }
 
