@@ -711,8 +711,11 @@ static int big_grid(int tiles, int per_cu) {
 // at least a tile per CU (256 x 256 tiles when N allows, else 256 x 128); otherwise 128x128
 // (64-wide slices when every K-segment boundary allows, else 32-wide) when its tiles keep at
 // least three quarters of the CUs busy (measured: the CVR expert GEMM, 224 tiles of K = 2048,
-// runs 36 us against 58 us as 64x64); 64x64 below that (the per-candidate GEMMs of the CVR
-// model at small batch).
+// runs 36 us against 58 us as 64x64); below that 64x128 when the caller asks for a group's
+// whole width (N <= 128) in one tile (the CVR query GEMM at 500 candidates per request: 23 us
+// against 33 us as 64x64, whose six tiles per row block re-read its 1,792 fp32 A columns; at
+// one candidate per request the 64x64 grid's wider spread is faster), else 64x64 (the
+// per-candidate GEMMs of the CVR model at small batch).
 static int choose_tile(const GemmParams& p, bool af32) {
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
   const char* env = getenv("CVR_GEMM_TILE");
@@ -724,6 +727,7 @@ static int choose_tile(const GemmParams& p, bool af32) {
   if (!tile) {
     if (big_ok && (int64_t)tiles(256, 128) * p.groups >= 256) tile = 256;
     else if ((int64_t)tiles(128, 128) * p.groups >= 192) tile = 128;  // 3/4 of the CUs busy beats 4x the tiles
+    else if (p.full_n && p.N <= 128) tile = 96;                        // 64 x 128
     else tile = 64;
   }
   return tile;
@@ -756,6 +760,9 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   } else if (tile == 128) {
     if (bk64) launch_k((gemm_kernel<T, 128, 128, 2, 2, AF32, 64>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
     else launch_k((gemm_kernel<T, 128, 128, 2, 2, AF32, 32>), dim3(tiles(128, 128), p.groups), blk, 0, st, p);
+  } else if (tile == 96) {
+    if (bk64) launch_k((gemm_kernel<T, 64, 128, 2, 2, AF32, 64>), dim3(tiles(64, 128), p.groups), blk, 0, st, p);
+    else launch_k((gemm_kernel<T, 64, 128, 2, 2, AF32, 32>), dim3(tiles(64, 128), p.groups), blk, 0, st, p);
   } else {
     if (bk64) launch_k((gemm_kernel<T, 64, 64, 2, 2, AF32, 64>), dim3(tiles(64, 64), p.groups), blk, 0, st, p);
     else launch_k((gemm_kernel<T, 64, 64, 2, 2, AF32, 32>), dim3(tiles(64, 64), p.groups), blk, 0, st, p);

@@ -178,6 +178,9 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       g.c_gstride = (int64_t)n * d;
       g.c_nstride8 = 8;
       g.out_f32 = 1;
+      // many candidates per request: the token rows stay cache-resident, and one tile per row
+      // block and query reads them once instead of once per 64 columns
+      g.full_n = (int64_t)n >= 4 * (int64_t)R;
       e = L(STAGE_QUERY_GEMM, [&] { return launch_gemm(g, lowp, s); });
       if (e != hipSuccess) return e;
     }

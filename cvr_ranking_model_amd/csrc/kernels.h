@@ -171,6 +171,9 @@ struct GemmParams {
   const void* ow;
   float* opart;
   int64_t opart_ld;
+  // 1: when N <= 128, one 64 x 128 tile covers a group's whole width, so each group reads its
+  // A rows once (pays when A is shared and cache-resident, e.g. many candidates per request)
+  int32_t full_n;
 };
 hipError_t launch_gemm(const GemmParams& p, int lowp, hipStream_t st);
 // True when launch_gemm runs p on the wide kernel, which can take the output-layer fusion.
