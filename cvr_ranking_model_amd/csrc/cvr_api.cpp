@@ -803,7 +803,12 @@ extern "C" cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, si
     case CVR_DBG_LOGITS: off = w.logits; bytes = n * (cvr ? sp.n_tasks : 1) * 4; break;
     case CVR_DBG_HSEQ: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.hseq; bytes = P * d * 2; break;
     case CVR_DBG_SEQ_POOL: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.seq_pool; bytes = S * R * d * 4; break;
-    case CVR_DBG_TOKENS: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_tok]; bytes = n * T * d * 4; break;
+    case CVR_DBG_TOKENS:
+      if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only");
+      if (h->last_tok_bf16)
+        return fail(h, CVR_ERR_ARG, "the token matrix is kept in fp32 only with cvr_set_debug(1) before scoring (otherwise "
+                                    "the last layer writes it as bf16 for the expert GEMM)");
+      off = w.tok[h->last_tok]; bytes = n * T * d * 4; break;
     case CVR_DBG_QUERY: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.query; bytes = S * n * d * 4; break;
     case CVR_DBG_ATTN: if (!cvr) return fail(h, CVR_ERR_ARG, "CVR only"); off = w.tok[h->last_attn_tok]; bytes = n * T * d * 4; break;
     case CVR_DBG_HIDDEN:

@@ -157,6 +157,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
 
   // ---- B6-B9: stacked interaction layers
   int cur = 0;
+  bool last_bf16 = false;
   for (int l = 0; l < sp.n_layers; ++l) {
     const std::string Lp = "layer." + S_(l);
     {
@@ -206,6 +207,11 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       TokenMixParams t{};
       t.Y = (const float*)tok[cur];
       t.Z = (float*)tok[1 - cur];
+      // The last layer's tokens feed only the expert GEMM, which rounds them to bf16 as it loads
+      // them: written as bf16 they take half the bytes and give the same products.  Debug runs
+      // keep fp32 so that the token matrix can be exported.
+      if (l == sp.n_layers - 1 && !m->debug) t.Zb = (__bf16*)tok[1 - cur];
+      last_bf16 = t.Zb != nullptr;
       t.n = n;
       t.T = T;
       t.d = d;
@@ -273,6 +279,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     cur = 1 - cur;
   }
   m->last_tok = cur;
+  m->last_tok_bf16 = last_bf16;
 
   // ---- B10: experts and gate logits over the flattened token matrix in one GEMM (the gate
   // rows follow the expert rows in the arena; ReLU on the expert columns only), then the gate
@@ -291,7 +298,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     g.K = T * d;
     g.groups = 1;
     g.nseg = 1;
-    g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, T * d, 8, 0, 1};
+    g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, T * d, 8, 0, last_bf16 ? 0 : 1};
     g.W = m->wptr("ple.expert.0.weight");
     g.bias = (const float*)m->wptr("_ple.bias");
     // the rows must be contiguous: experts back to back, then the gates task by task

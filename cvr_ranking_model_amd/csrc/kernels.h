@@ -252,6 +252,7 @@ bool attention_many_candidates(int32_t n, int32_t R);
 struct TokenMixParams {
   const float* Y;               // [n][T][d] fp32
   float* Z;                     // [n][T][d] fp32
+  __bf16* Zb;                   // if set: Z is written here as bf16 instead (Z unused)
   int32_t n, T, d, H;
   const __bf16* W1;             // head h: W1 + h*w1_gstride, [256][T*8] packed by launch_mix_pack
   int64_t w1_gstride;

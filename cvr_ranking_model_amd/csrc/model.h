@@ -113,6 +113,7 @@ struct cvr_model {
   cvr::WsPlan last_plan;
   int64_t last_R = 0, last_n = 0, last_P = 0;
   int last_debug = 0, last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0;
+  int last_tok_bf16 = 0;  // the last layer's token matrix was written as bf16 (debug off)
   cvr::Timing timing;
   cvr::GraphCache graph;
   // HBM hot-row caches attached to host-resident tables (cvr_cache_attach)

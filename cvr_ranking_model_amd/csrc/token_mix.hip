@@ -173,7 +173,14 @@ __global__ __launch_bounds__(512) void token_mix_kernel(const TokenMixParams p, 
           z.y = y.y + (acc[b][4 * v4 + 1] + bb.y);
           z.z = y.z + (acc[b][4 * v4 + 2] + bb.z);
           z.w = y.w + (acc[b][4 * v4 + 3] + bb.w);
-          *reinterpret_cast<float4*>(p.Z + ((int64_t)c * T + t) * p.d + h * hw + j) = z;
+          const int64_t zo = ((int64_t)c * T + t) * p.d + h * hw + j;
+          if (p.Zb) {  // rounded as the next Linear would round it on loading
+            bf16x4 zb;
+            zb[0] = (bf16)z.x; zb[1] = (bf16)z.y; zb[2] = (bf16)z.z; zb[3] = (bf16)z.w;
+            *reinterpret_cast<bf16x4*>(p.Zb + zo) = zb;
+          } else {
+            *reinterpret_cast<float4*>(p.Z + zo) = z;
+          }
         }
       }
     }

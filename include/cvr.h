@@ -232,7 +232,8 @@ enum {
   CVR_DBG_LOGITS = 4,       /* fp32 [n][n_tasks]: pre-sigmoid outputs */
   CVR_DBG_HSEQ = 5,         /* (CVR) bf16 [n_positions][d]: SwiGLU outputs */
   CVR_DBG_SEQ_POOL = 6,     /* (CVR) fp32 [n_seq][n_requests][d]: mean pools */
-  CVR_DBG_TOKENS = 7,       /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix Z */
+  CVR_DBG_TOKENS = 7,       /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix Z (needs debug != 0 at
+                               scoring when the fused token mixer runs: it then writes Z as bf16) */
   CVR_DBG_QUERY = 8,        /* (CVR) fp32 [n_seq][n][d]: last layer's queries */
   CVR_DBG_ATTN = 9,         /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix before mixing (attention outputs in rows N..) */
   CVR_DBG_HIDDEN = 10       /* (DLRM, debug mode) lowp [n][width]: activations of the last hidden

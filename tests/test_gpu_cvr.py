@@ -261,3 +261,24 @@ def test_request_alone_equals_in_batch(requests, candidates):
         _, out1, st = run(m, alone)
         assert st == cv.CVR_OK
         assert np.array_equal(out1.cpu().numpy().reshape(-1, K), full[lo:hi]), r
+
+
+@pytest.mark.parametrize("name,requests,candidates", [("c3", 8, 1), ("c4", 6, 1), ("c3", 3, 48)])
+def test_scores_without_debug_equal_debug_scores(name, requests, candidates):
+    """Without debug the last layer's token matrix is written as bf16 for the expert GEMM, which
+    rounds its fp32 inputs the same way on loading: the scores equal the debug run's (fp32
+    tokens, checked against the oracle above) bit for bit.  The fp32 export then needs debug."""
+    spec = synth.load_spec(name)
+    banner(f"{name} stress: scores with and without debug, {requests} x {candidates}")
+    m, _ = build_model(spec, "stress", debug=True)
+    b = synth.make_batch(spec, requests=requests, candidates=candidates)
+    _, out, st = run(m, b)
+    assert st == cv.CVR_OK
+    ref = out.cpu().numpy().copy()
+    m.set_debug(False)
+    _, out, st = run(m, b)
+    assert st == cv.CVR_OK
+    assert np.array_equal(out.cpu().numpy(), ref)
+    with pytest.raises(cv.CvrError):
+        m.export(cv.CVR_DBG_TOKENS, torch.float32, (requests * candidates, spec["n_tokens"] + 3, spec["d"]))
+    m.close()
