@@ -1,11 +1,14 @@
 """Throughput of the candidate-scoring forward pass on one MI355X.
 
-Default workload: the page-2-shaped DLRM request batch (64 requests x 500
-candidates, 18 fp32 tables of 4.97 GB, fp16 MLP 640 -> 5 x 1024 -> 1).  One
-step = one cvr_score call over the whole batch (expand, gather-pool, every MLP
-layer, output and sigmoid), inputs resident in HBM.  Prints one JSON line.
+Default workload: the CVR model at its largest batch (C4: 4096 samples, 2 interaction layers,
+behaviour sequences of 256/1024/2048 positions, bf16).  One step = one cvr_score call over the
+whole batch (expand, gather-pool, tokenizer, SwiGLU sequence encoding and pools, per layer the
+queries, attention and token mixer, PLE experts, gates and heads), inputs resident in HBM.
+After it, unless --no-extra, the two DLRM workloads (C5: 27 GB of tables, 128k candidates;
+C2: 64 requests x 500 candidates) are measured the same way and reported under "configs".
+Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-extra] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -126,6 +129,7 @@ def measured_traffic(workload, stage):
 
 
 def cpu_baseline(spec, variant, weights, budget_s=10.0):
+    """The oracle timed on the host's cores on a bounded sample of the same workload."""
     import numpy as np
     import oracle
     from cvr_ranking_model_amd import synth
@@ -137,7 +141,6 @@ def cpu_baseline(spec, variant, weights, budget_s=10.0):
     tables = synth.make_tables(spec, variant)
     wl = spec["workload"]
     R = wl["requests"]
-    C = wl["candidates"]
     b1 = synth.make_batch(spec, requests=1, seed_offset=99)
     t0 = time.perf_counter()
     oracle.score(spec, tables, weights, b1)
@@ -148,54 +151,34 @@ def cpu_baseline(spec, variant, weights, budget_s=10.0):
     oracle.score(spec, tables, weights, b)
     dt = time.perf_counter() - t0
     n = int(b["cand_offsets"][-1])
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": n / dt, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{nreq} of {R} requests ({n} candidates) of the same workload, {dt:.1f} s, numpy fp64 dense",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count(), "affinity_cpus": affinity}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--batch", type=int, default=None, help="requests per step (CVR batch sweep)")
-    ap.add_argument("--candidates", type=int, default=None,
-                    help="candidates per request (CVR: 1 user + C candidates sharing its sequences)")
-    ap.add_argument("--variant", default="bench")
-    ap.add_argument("--cache", action="store_true",
-                    help="DLRM: keep the ID tables in pinned host memory behind HBM hot-row caches "
-                         "(CTR article section 二) and cycle through --cache-batches distinct batches")
-    ap.add_argument("--cache-gb", type=float, default=5.0, help="HBM given to the caches (the article's L0: ~5 GB)")
-    ap.add_argument("--cache-ways", type=int, default=8)
-    ap.add_argument("--cache-batches", type=int, default=16)
-    ap.add_argument("--ple-task-experts", default=None,
-                    help="CVR: experts each task's gate mixes, tasks separated by '/', e.g. 0,2/1,2 "
-                         "(PLE with one task-specific expert per task and a shared one)")
-    ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="time graph replays (cvr_score_graph); per-stage rooflines then come from an eager pass "
-                         "of the same steps that follows")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after the timed steps, run one plain 256 MiB fp32 copy kernel (torch.neg) so a "
-                         "hardware-counter run can scale its byte counters against a known size")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library scores on one GPU (requests would shard across GPUs "
-              "with no collective, each GPU holding its own copy of tables and weights). Run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def percentiles(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
 
+
+def run_config(workload, args, steps, warmup, batch=None, candidates=None, uniform_ids=False, cpu_budget=25.0,
+               gather_control=True):
+    """Measure one workload; returns the fields of its JSON entry."""
     import numpy as np
     import torch
     from cvr_ranking_model_amd import synth
     from cvr_ranking_model_amd import cvr as cv
 
-    spec = synth.load_spec(args.workload)
+    spec = synth.load_spec(workload)
     if args.ple_task_experts:
         spec["ple_task_experts"] = [[int(e) for e in t.split(",")] for t in args.ple_task_experts.split("/")]
-    print(f"[bench] workload {args.workload}: filling tables", file=sys.stderr, flush=True)
+    print(f"[bench] workload {workload}: filling tables", file=sys.stderr, flush=True)
     tables = cv.device_tables(spec, args.variant)
     cached = []
     if args.cache:
@@ -227,47 +210,47 @@ def main():
                                                     "hbm_GB": round(sets * args.cache_ways * dim * 4 / 1e9, 3),
                                                     "table_GB": round(rows * dim * 4 / 1e9, 3)}
     nb = args.cache_batches if cached else 1
-    batches = [synth.make_batch(spec, requests=args.batch, candidates=args.candidates, uniform_ids=args.uniform_ids,
+    batches = [synth.make_batch(spec, requests=batch, candidates=candidates, uniform_ids=uniform_ids,
                                 seed_offset=i) for i in range(nb)]
-    batch = batches[0]
     dbs = [cv.DeviceBatch(b) for b in batches]
     db = dbs[0]
     n = db.n_candidates
     out = torch.empty(n * model.n_tasks, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    print(f"[bench] {n} candidates per step; warmup {args.warmup}", file=sys.stderr, flush=True)
-    for i in range(max(args.warmup, nb if cached else 0)):
+    print(f"[bench] {workload}: {n} candidates per step; warmup {warmup}", file=sys.stderr, flush=True)
+    for i in range(max(warmup, nb if cached else 0)):
         model.score(dbs[i % nb], out)
     assert model.sync_status() == cv.CVR_OK
     # Instrumented pass (every stage timed, not the timed region): the per-stage table and the
     # dominant stage.  An event-carrying dispatch costs a few microseconds more than a plain one,
     # so the timed region below carries events on the dominant stage's launches only.
-    model.timing_begin(args.steps)
-    for i in range(args.steps):
+    model.timing_begin(steps)
+    for i in range(steps):
         model.score(dbs[i % nb], out)
     stages, calls = model.timing_end()
     dom = max(stages, key=lambda k: stages[k][0])
     stats0 = {t: model.cache_stats(t) for t in cached}
     graph_dt = None
     if args.graph:
-        for _ in range(max(1, args.warmup)):
+        for _ in range(max(1, warmup)):
             model.score_graph(db, out)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             model.score_graph(db, out)
         torch.cuda.synchronize()
         graph_dt = time.perf_counter() - t0
         assert model.sync_status() == cv.CVR_OK
-    model.timing_begin(args.steps, [dom])
+    print(f"[bench] {workload}: timed region, {steps} steps", file=sys.stderr, flush=True)
+    model.timing_begin(steps, [dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         model.score(dbs[i % nb], out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     live, live_calls = model.timing_end()
-    assert live_calls == args.steps and dom in live
+    assert live_calls == steps and dom in live
     for t in cached:
         st1, st0 = model.cache_stats(t), stats0[t]
         d = {k: st1[k] - st0[k] for k in st1}
@@ -276,6 +259,17 @@ def main():
     eager_dt = dt
     if graph_dt is not None:
         dt = graph_dt
+    # Per-step spread: the same steps again, each between two events on the model's stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(model.stream)
+        if args.graph:
+            model.score_graph(db, out)
+        else:
+            model.score(dbs[i % nb], out)
+        ev[i][1].record(model.stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in ev]
     # End to end from host memory: each step also copies its packed request buffer (pinned
     # host memory) to the device on the model's stream before scoring it.  Reported beside
     # the HBM-resident rate, never as the value.
@@ -283,7 +277,7 @@ def main():
     with torch.cuda.stream(model.stream):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             b = dbs[i % nb]
             b.dev.copy_(b.host, non_blocking=True)
             model.score(b, out)
@@ -297,13 +291,14 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    ms_step = dt * 1e3 / args.steps
-    value = n * args.steps / dt
+    ms_step = dt * 1e3 / steps
+    value = n * steps / dt
 
     # per-stage rooflines from the live event timings; the dominant stage gives "roofline"
     works = [stage_work(spec, b) for b in batches]
     work = {k: (v[0], sum(w[k][1] for w in works) / len(works)) for k, v in works[0].items()}
     peak_f = MFMA_PEAK_TFLOPS[spec["lowp"]]
+    default_shape = batch is None and candidates is None and not uniform_ids and not args.cache
     table = {}
     for st, (ms, launches) in stages.items():
         entry = {"ms_per_step": round(ms / calls, 4), "launches_per_step": launches // max(calls, 1)}
@@ -320,6 +315,15 @@ def main():
                              frac=round(ach / HBM_PEAK_GBS, 4))
             entry["per_launch"] = per_launch
             entry["avg_launch_us"] = round(avg_s * 1e6, 2)
+            if st == "gather_pool":
+                # algorithmic bytes (every row once per id) over time: what the lookup delivers;
+                # the HBM rate proper comes from the byte counters when a record exists
+                entry["achieved_is"] = "effective: algorithmic bytes / kernel time (cache hits not subtracted)"
+                traffic, source = measured_traffic(workload, st) if default_shape else (None, None)
+                if traffic:
+                    hbm = traffic / avg_s / 1e9
+                    entry["hbm_counter"] = {"bytes_per_launch": traffic, "GBs": round(hbm, 1),
+                                            "frac": round(hbm / HBM_PEAK_GBS, 4), "source": source}
         if st + "_bytes" in work:
             b = work[st + "_bytes"][1] * calls / launches
             entry["hbm_GBs"] = round(b / (ms / launches / 1e3) / 1e9, 1)
@@ -336,46 +340,133 @@ def main():
         d_entry["frac"] = round(d_entry["achieved"] / d_entry["peak"], 4)
     roof = None
     if "bound" in d_entry:
-        traffic, source = measured_traffic(args.workload, dom) if args.batch is None and args.candidates is None and not args.uniform_ids \
-            and not args.cache else (None, None)
+        traffic, source = measured_traffic(workload, dom) if default_shape else (None, None)
         roof = {"bound": d_entry["bound"], "kernel": dom, "achieved": d_entry["achieved"], "peak": d_entry["peak"],
                 "unit": d_entry["unit"], "frac": d_entry["frac"], "traffic": traffic,
                 "per_launch": d_entry["per_launch"], "avg_launch_us": d_entry["avg_launch_us"]}
         if source:
             roof["traffic_source"] = source
-    line = {
-        "metric": "scored candidates/sec at 1 GPU",
+    res = {
         "value": round(value, 1),
         "unit": "candidates/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "step_ms": percentiles(step_ms),
+        "value_at_median_step": round(n / (percentiles(step_ms)["median"] / 1e3), 1),
         "dtype": spec["lowp"],
-        "data": f"synthetic ({args.variant} variant: seeded hash tables, Zipf ids, Glorot weights)",
-        "config": dict({"workload": WORKLOAD_TEXT[args.workload], "candidates_per_step": n,
+        "config": dict({"workload": WORKLOAD_TEXT[workload], "candidates_per_step": n,
                         "requests_per_step": db.n_requests},
                        **({"ple_task_experts": spec["ple_task_experts"]} if args.ple_task_experts else {}),
                        **({"hot_row_cache": cache_cfg, "distinct_batches": nb} if cached else {})),
         "roofline": roof,
         "stages": table,
-        "stages_pass": "instrumented pass of the same steps before the timed region (events on every launch); "
-                       "the timed region carries events on the roofline kernel's launches only",
-        "ids": "uniform" if args.uniform_ids else "zipf",
+        "ids": "uniform" if uniform_ids else "zipf",
         "launch": "graph replay" if args.graph else "eager",
-        "with_h2d": {"value": round(n * args.steps / h2d_dt, 1), "unit": "candidates/s",
-                     "ms_per_step": round(h2d_dt * 1e3 / args.steps, 4), "h2d_bytes_per_step": int(h2d_bytes),
+        "with_h2d": {"value": round(n * steps / h2d_dt, 1), "unit": "candidates/s",
+                     "ms_per_step": round(h2d_dt * 1e3 / steps, 4), "h2d_bytes_per_step": int(h2d_bytes),
                      "what": "each step first copies its packed request buffer from pinned host memory"},
     }
     if args.graph:
-        line["eager_ms_per_step"] = round(eager_dt * 1e3 / args.steps, 4)
-        line["roofline_pass"] = "eager steps timed right after the graph replays (events on the roofline kernel)"
+        res["eager_ms_per_step"] = round(eager_dt * 1e3 / steps, 4)
+        res["roofline_pass"] = "eager steps timed right after the graph replays (events on the roofline kernel)"
+    if gather_control and not uniform_ids and not cached and "gather_pool" in table:
+        # cold control: the same workload with uniform ids (no hot rows for the caches to hold)
+        ub = synth.make_batch(spec, requests=batch, candidates=candidates, uniform_ids=True, seed_offset=7)
+        udb = cv.DeviceBatch(ub)
+        uout = torch.empty(udb.n_candidates * model.n_tasks, dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            model.score(udb, uout)
+        model.timing_begin(steps, ["gather_pool"])
+        for _ in range(steps):
+            model.score(udb, uout)
+        ust, ucalls = model.timing_end()
+        assert model.sync_status() == cv.CVR_OK
+        ums, ul = ust["gather_pool"]
+        ubytes = stage_work(spec, ub)["gather_pool"][1] * ucalls / ul
+        ach = ubytes / (ums / ul / 1e3) / 1e9
+        res["gather_uniform_ids"] = {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(ach / HBM_PEAK_GBS, 4), "per_launch": ubytes,
+                                     "avg_launch_us": round(ums / ul * 1e3, 2),
+                                     "what": "gather-pool of the same workload with uniform ids (cold control)"}
+        del udb, uout
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(spec, args.variant, weights)
+        print(f"[bench] {workload}: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(spec, args.variant, weights, budget_s=cpu_budget)
+    model.close()
+    del model, tables, dbs, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--batch", type=int, default=None, help="requests per step (CVR batch sweep)")
+    ap.add_argument("--candidates", type=int, default=None,
+                    help="candidates per request (CVR: 1 user + C candidates sharing its sequences)")
+    ap.add_argument("--variant", default="bench")
+    ap.add_argument("--cache", action="store_true",
+                    help="DLRM: keep the ID tables in pinned host memory behind HBM hot-row caches "
+                         "(CTR article section 二) and cycle through --cache-batches distinct batches")
+    ap.add_argument("--cache-gb", type=float, default=5.0, help="HBM given to the caches (the article's L0: ~5 GB)")
+    ap.add_argument("--cache-ways", type=int, default=8)
+    ap.add_argument("--cache-batches", type=int, default=16)
+    ap.add_argument("--ple-task-experts", default=None,
+                    help="CVR: experts each task's gate mixes, tasks separated by '/', e.g. 0,2/1,2 "
+                         "(PLE with one task-specific expert per task and a shared one)")
+    ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure the named workload only (no further configs, no uniform-id gather control)")
+    ap.add_argument("--extra", default="c5,c2", help="configs measured after the main one (default: c5,c2)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time graph replays (cvr_score_graph); per-stage rooflines then come from an eager pass "
+                         "of the same steps that follows")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one plain 256 MiB fp32 copy kernel (torch.neg) so a "
+                         "hardware-counter run can scale its byte counters against a known size")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library scores on one GPU (requests would shard across GPUs "
+              "with no collective, each GPU holding its own copy of tables and weights). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    main_res = run_config(args.workload, args, args.steps, args.warmup, batch=args.batch,
+                          candidates=args.candidates, uniform_ids=args.uniform_ids,
+                          gather_control=not args.no_extra)
+    line = {
+        "metric": "scored candidates/sec at 1 GPU",
+        "value": main_res.pop("value"),
+        "unit": main_res.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res.pop("dtype"),
+        "data": f"synthetic ({args.variant} variant: seeded hash tables, Zipf ids, Glorot weights)",
+        "config": main_res.pop("config"),
+        "roofline": main_res.pop("roofline"),
+    }
+    cpu = main_res.pop("cpu_baseline", None)
+    line.update(main_res)
+    line["stages_pass"] = ("instrumented pass of the same steps before the timed region (events on every launch); "
+                           "the timed region carries events on the roofline kernel's launches only; step_ms from a "
+                           "further pass with one event pair around each step")
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    if not args.no_extra and args.batch is None and args.candidates is None and not args.uniform_ids \
+            and not args.cache and not args.graph:
+        configs = {}
+        for w in [x for x in args.extra.split(",") if x and x != args.workload]:
+            configs[w] = run_config(w, args, min(args.steps, 20), min(args.warmup, 5), cpu_budget=10.0)
+        line["configs"] = configs
     print(json.dumps(line), flush=True)
 
 

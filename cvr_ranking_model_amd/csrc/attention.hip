@@ -323,14 +323,11 @@ __global__ __launch_bounds__(256) void attention_mq_kernel(const AttnParams p) {
   }
 }
 
-bool attention_many_candidates(int32_t n, int32_t R) {
-  if (const char* e = getenv("CVR_ATTN_MQ")) return atoi(e) != 0;
-  return (int64_t)n >= 16 * (int64_t)R;
-}
+bool attention_many_candidates(int32_t n, int32_t R) { return (int64_t)n >= 16 * (int64_t)R; }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
   if (p.n <= 0 || p.S <= 0) return hipSuccess;
-  if (attention_many_candidates(p.n, p.R)) {
+  if (p.mq) {
     const int64_t tasks = (int64_t)((p.n + 31) / 32) * p.S;
     launch_k(attention_mq_kernel, dim3((unsigned)tasks), dim3(256), 0, st, p);
   } else {

@@ -55,6 +55,8 @@ static cvr_status check_spec(const cvr_spec* s, const cvr_table* tables, int32_t
     for (int i = 0; i < s->n_hidden; ++i)
       if (s->hidden[i] <= 0 || s->hidden[i] % 32) { why = "hidden widths must be positive multiples of 32"; return CVR_ERR_UNSUPPORTED; }
   } else {
+    // the sequence, attention and token-mixer kernels compute in bf16 (CVR article section 3.4.3)
+    if (s->lowp != CVR_LOWP_BF16) { why = "the CVR model runs in bf16 only"; return CVR_ERR_UNSUPPORTED; }
     if (s->d != 128) { why = "token width d must be 128"; return CVR_ERR_UNSUPPORTED; }
     if (s->n_tokens <= 0 || s->n_layers <= 0 || s->n_seq <= 0 || s->n_seq > 4) { why = "bad token/layer/sequence counts"; return CVR_ERR_SPEC; }
     if (s->n_seq_cols <= 0 || !s->seq_tables || s->n_seq_cols > 8) { why = "bad sequence columns"; return CVR_ERR_SPEC; }
@@ -329,7 +331,6 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
   }
   hipError_t he = hipStreamSynchronize(s);
   if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("create sync: ") + hipGetErrorString(he)); }
-  if (const char* pr = getenv("CVR_DLRM_PASS_ROWS")) m->pass_rows = std::max(0ll, atoll(pr));  // tuning override
   *out = m;
   return CVR_OK;
 }
@@ -487,6 +488,9 @@ static cvr_status check_batch(cvr_model* m, const cvr_batch* b, void* ws, size_t
   if (!b->cand_offsets || !b->bag_offsets || (b->n_ids > 0 && !b->ids)) return fail(m, CVR_ERR_ARG, "null CSR array");
   if (m->spec.model == CVR_MODEL_HYFORMER && (!b->seq_offsets || (b->n_positions > 0 && !b->seq_ids)))
     return fail(m, CVR_ERR_ARG, "CVR model needs seq_offsets and seq_ids");
+  // chunk descriptors carry the (sequence, request) segment in 23 bits
+  if (m->spec.model == CVR_MODEL_HYFORMER && (int64_t)m->spec.n_seq * b->n_requests >= (1 << 23))
+    return fail(m, CVR_ERR_ARG, "n_seq * n_requests must be below 2^23");
   plan = plan_workspace(m, b->n_requests, b->n_candidates, m->spec.model == CVR_MODEL_DLRM ? 0 : b->n_positions);
   if (ws_bytes < plan.total) return fail(m, CVR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.total) + " bytes");
   return CVR_OK;
@@ -742,6 +746,10 @@ extern "C" cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* b, void* wo
     g.out = out_scores;
     g.stream = s;
     g.debug = h->debug;
+    g.last_tok = h->last_tok;
+    g.last_attn_tok = h->last_attn_tok;
+    g.last_hidden_buf = h->last_hidden_buf;
+    g.last_tok_bf16 = h->last_tok_bf16;
   }
   const hipError_t e = hipGraphLaunch(g.exec, s);
   if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
@@ -750,7 +758,11 @@ extern "C" cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* b, void* wo
   h->last_R = b->n_requests;
   h->last_n = b->n_candidates;
   h->last_P = b->n_positions;
-  h->last_debug = h->debug;
+  h->last_debug = g.debug;
+  h->last_tok = g.last_tok;
+  h->last_attn_tok = g.last_attn_tok;
+  h->last_hidden_buf = g.last_hidden_buf;
+  h->last_tok_bf16 = g.last_tok_bf16;
   return CVR_OK;
 }
 
@@ -776,6 +788,27 @@ extern "C" cvr_status cvr_sync_status(cvr_handle h, void* hip_stream) {
 }
 
 // ------------------------------------------------------------------ debug export
+
+extern "C" cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value) {
+  if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
+  switch (option) {
+    case CVR_OPT_DLRM_PASS_ROWS:
+      if (value < -1 || value > INT32_MAX) return fail(h, CVR_ERR_ARG, "pass rows must be -1, 0 or a count");
+      h->pass_rows = value;
+      break;
+    case CVR_OPT_TOK_SHARE:
+      if (value < -1 || value > 1) return fail(h, CVR_ERR_ARG, "tokenizer sharing must be -1, 0 or 1");
+      h->opt_tok_share = (int)value;
+      break;
+    case CVR_OPT_ATTN_MQ:
+      if (value < -1 || value > 1) return fail(h, CVR_ERR_ARG, "attention form must be -1, 0 or 1");
+      h->opt_attn_mq = (int)value;
+      break;
+    default: return fail(h, CVR_ERR_ARG, "unknown option");
+  }
+  h->graph.reset();  // a captured graph baked in the previous choice
+  return CVR_OK;
+}
 
 extern "C" cvr_status cvr_set_debug(cvr_handle h, int32_t debug) {
   if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");

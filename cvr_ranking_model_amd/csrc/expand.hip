@@ -41,10 +41,13 @@ __global__ void expand_kernel(ExpandParams p) {
     if (i < p.total_bags && (int64_t)p.bag_offsets[i + 1] < v) bad |= ERRF_BAG_OFFSETS;
   }
   if (p.seq_offsets != nullptr && i < (int64_t)p.S * (p.R + 1)) {
-    const int64_t r = i % (p.R + 1);
+    // The [S][R+1] array read as one list must be non-decreasing: each sequence's segments in
+    // request order, and sequence s ending at or before sequence s+1 begins.  Segments are
+    // then disjoint inside [0, n_positions], so every position is encoded by one sequence's
+    // weights and the chunk count stays within n_positions / 32 + S * R.
     const int64_t v = p.seq_offsets[i];
     if (v < 0 || v > p.n_positions) bad |= ERRF_SEQ_OFFSETS;
-    if (r < p.R && (int64_t)p.seq_offsets[i + 1] < v) bad |= ERRF_SEQ_OFFSETS;
+    if (i + 1 < (int64_t)p.S * (p.R + 1) && (int64_t)p.seq_offsets[i + 1] < v) bad |= ERRF_SEQ_OFFSETS;
   }
   if (bad) raise_flag(p.flag, bad);
 }

@@ -718,18 +718,14 @@ static int big_grid(int tiles, int per_cu) {
 // per-candidate GEMMs of the CVR model at small batch).
 static int choose_tile(const GemmParams& p, bool af32) {
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
-  const char* env = getenv("CVR_GEMM_TILE");
-  int tile = env ? atoi(env) : 0;
+  int tile = 0;
   const bool big_ok = !af32 && !p.out_f32 && p.N % 128 == 0 && p.N <= kBigMaxN && p.c_nstride8 == 8 && !p.R &&
                       p.relu_end == 0 &&
                       (p.ldc & 7) == 0 && (p.c_gstride & 7) == 0;
-  if (tile == 256 && !big_ok) tile = 0;
-  if (!tile) {
-    if (big_ok && (int64_t)tiles(256, 128) * p.groups >= 256) tile = 256;
-    else if ((int64_t)tiles(128, 128) * p.groups >= 192) tile = 128;  // 3/4 of the CUs busy beats 4x the tiles
-    else if (p.full_n && p.N <= 128) tile = 96;                        // 64 x 128
-    else tile = 64;
-  }
+  if (big_ok && (int64_t)tiles(256, 128) * p.groups >= 256) tile = 256;
+  else if ((int64_t)tiles(128, 128) * p.groups >= 192) tile = 128;  // 3/4 of the CUs busy beats 4x the tiles
+  else if (p.full_n && p.N <= 128) tile = 96;                        // 64 x 128
+  else tile = 64;
   return tile;
 }
 

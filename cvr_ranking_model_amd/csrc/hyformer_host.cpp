@@ -15,8 +15,6 @@
 //   expert GEMM, gates + mixture, head fc1 GEMM, head output + sigmoid                  (B10-B11)
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-
 #include <string>
 
 #include "kernels.h"
@@ -52,8 +50,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   // ---- B2: tokenization, X = E W_tok^T + b into token rows 0..N-1.  When requests carry several
   // candidates, the request-side columns are multiplied once per request (U = E_req W_req^T)
   // and every candidate adds its request's row of U to its item-side product.
-  bool share = m->tok_split && (int64_t)n >= 4 * (int64_t)R;
-  if (const char* ev = getenv("CVR_TOK_SHARE")) share = m->tok_split && atoi(ev) != 0;
+  bool share = m->tok_split && (m->opt_tok_share < 0 ? (int64_t)n >= 4 * (int64_t)R : m->opt_tok_share != 0);
   if (!share) {
     GemmParams g{};
     g.M = n;
@@ -110,6 +107,8 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
 
   // ---- B3-B5: sequence encoding and mean pools (per request)
   int32_t* chunk_off = (int32_t*)(ws + w.chunk_off);
+  // every segment adds at most one partial chunk; the workspace holds this many
+  const int max_chunks = (int)(P / kSeqChunk) + S * R;
   int2* chunk_desc = (int2*)(ws + w.chunk_desc);
   e = L(STAGE_SEQ_CHUNKS, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, chunk_desc, s); });
   if (e != hipSuccess) return e;
@@ -132,6 +131,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     }
     p.chunk_off = chunk_off;
     p.desc = chunk_desc;
+    p.max_chunks = max_chunks;
     p.Wgu = (const __bf16*)m->wptr("seq.0.gate.weight");
     p.wgu_gstride = group_stride(m, [](int i) { return "seq." + S_(i) + ".gate.weight"; }, S, 2);
     p.bgu = (const float*)m->wptr("seq.0.gate.bias");
@@ -145,12 +145,11 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     p.H = (__bf16*)(ws + w.hseq);
     p.part = (float*)(ws + w.pool_part);
     p.flag = flag;
-    const int max_chunks = (int)(P / kSeqChunk) + S * R;
     e = L(STAGE_SWIGLU, [&] { return launch_swiglu(p, max_chunks, s); });
     if (e != hipSuccess) return e;
   }
   e = L(STAGE_SEQ_POOL, [&] {
-    return launch_seq_pool((const float*)(ws + w.pool_part), chunk_off, b->seq_offsets, R, S, P,
+    return launch_seq_pool((const float*)(ws + w.pool_part), chunk_off, b->seq_offsets, R, S, P, max_chunks,
                            (float*)(ws + w.seq_pool), s);
   });
   if (e != hipSuccess) return e;
@@ -199,6 +198,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       a.Y = (float*)tok[cur];
       a.T = T;
       a.N = N;
+      a.mq = m->opt_attn_mq < 0 ? attention_many_candidates(n, R) : m->opt_attn_mq != 0;
       e = L(STAGE_ATTENTION, [&] { return launch_attention(a, s); });
       if (e != hipSuccess) return e;
     }

@@ -211,6 +211,7 @@ struct SwigluParams {
   const float* col_table[kMaxSeqCols];
   const int32_t* chunk_off;     // [S*R+1]
   const int2* desc;             // [chunks]
+  int32_t max_chunks;           // chunks the workspace holds: n_positions / 32 + S * R
   const __bf16* Wgu;            // per sequence [2*256][128]: gate rows then up rows
   int64_t wgu_gstride;
   const float* bgu;             // per sequence [2*256]
@@ -226,7 +227,7 @@ struct SwigluParams {
 };
 hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st);
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
-                           int64_t n_positions, float* pool, hipStream_t st);
+                           int64_t n_positions, int32_t max_chunks, float* pool, hipStream_t st);
 
 // ---------------------------------------------------------------- attention (B7)
 struct AttnParams {
@@ -240,10 +241,10 @@ struct AttnParams {
   float inv_tau;
   float* Y;                     // [n][T][128]: writes token N+s
   int32_t T, N;
+  int32_t mq;                   // 1: MFMA products per request (attention_mq_kernel), 0: per candidate
 };
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
-// The MFMA form is used when requests carry 16 or more candidates on average (CVR_ATTN_MQ=0/1
-// overrides).
+// Default choice of the MFMA form: requests carry 16 or more candidates on average.
 bool attention_many_candidates(int32_t n, int32_t R);
 
 // ---------------------------------------------------------------- fused token mixer (B8)

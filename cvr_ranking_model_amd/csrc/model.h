@@ -68,6 +68,8 @@ struct GraphCache {
   float* out = nullptr;
   hipStream_t stream = nullptr;
   int debug = 0;
+  // buffer choices the captured launches made, restored on every replay for cvr_debug_export
+  int last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0, last_tok_bf16 = 0;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   void reset();
@@ -108,6 +110,8 @@ struct cvr_model {
   // state
   int debug = 0;
   int64_t pass_rows = -1;  // DLRM candidates per MLP pass: -1 derived from the layer width, 0 one pass
+  int opt_tok_share = -1;  // CVR_OPT_TOK_SHARE: -1 auto, 0 off, 1 on
+  int opt_attn_mq = -1;    // CVR_OPT_ATTN_MQ: -1 auto, 0 per candidate, 1 MFMA per request
   std::string err;
   char* last_ws = nullptr;
   cvr::WsPlan last_plan;

@@ -35,46 +35,50 @@ __device__ __forceinline__ void segment_range(const int32_t* __restrict__ seq_of
 
 // Exclusive scan of ceil(len / kSeqChunk) over the S*R segments (one block of 1024 threads):
 // thread t owns a run of consecutive segments; the run totals are scanned within each wave by
-// shuffles, then across the 16 waves.
+// shuffles, then across the 16 waves.  Sums are 64-bit and every offset written is capped at
+// max_chunks (what the workspace holds): with offsets that keep the layout contract the cap never
+// binds; with offsets that break it (flagged by the expand kernel) the table stays monotone and
+// every chunk it lists lies inside its own segment, so no later kernel leaves its arrays.
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* __restrict__ seq_offsets, int R, int S,
-                                                           int64_t n_positions, int32_t* __restrict__ chunk_off) {
-  __shared__ int32_t wsum[16];
+                                                           int64_t n_positions, int32_t max_chunks,
+                                                           int32_t* __restrict__ chunk_off) {
+  __shared__ long long wsum[16];
   const int SR = S * R;
   const int per = (SR + 1023) / 1024;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g0 = t * per;
-  int32_t local = 0;
+  long long local = 0;
   for (int g = g0; g < g0 + per && g < SR; ++g) {
     int64_t a, e;
     segment_range(seq_offsets, R, g, n_positions, a, e);
-    local += (int32_t)((e - a + kSeqChunk - 1) / kSeqChunk);
+    local += (e - a + kSeqChunk - 1) / kSeqChunk;
   }
-  int32_t incl = local;  // inclusive scan within the wave
+  long long incl = local;  // inclusive scan within the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int32_t v = __shfl_up(incl, off);
+    const long long v = __shfl_up(incl, off);
     if (lane >= off) incl += v;
   }
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   if (w == 0) {
-    int32_t x = lane < 16 ? wsum[lane] : 0;
+    long long x = lane < 16 ? wsum[lane] : 0;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
-      const int32_t v = __shfl_up(x, off);
+      const long long v = __shfl_up(x, off);
       if (lane >= off) x += v;
     }
     if (lane < 16) wsum[lane] = x;  // inclusive totals of waves 0..lane
   }
   __syncthreads();
-  int32_t run = (w > 0 ? wsum[w - 1] : 0) + incl - local;  // exclusive prefix of this thread's run
+  long long run = (w > 0 ? wsum[w - 1] : 0) + incl - local;  // exclusive prefix of this thread's run
   for (int g = g0; g < g0 + per && g < SR; ++g) {
-    chunk_off[g] = run;
+    chunk_off[g] = (int32_t)(run < max_chunks ? run : max_chunks);
     int64_t a, e;
     segment_range(seq_offsets, R, g, n_positions, a, e);
-    run += (int32_t)((e - a + kSeqChunk - 1) / kSeqChunk);
+    run += (e - a + kSeqChunk - 1) / kSeqChunk;
   }
-  if (t == 1023) chunk_off[SR] = wsum[15];
+  if (t == 1023) chunk_off[SR] = (int32_t)(wsum[15] < max_chunks ? wsum[15] : max_chunks);
 }
 
 // One descriptor per chunk: x = first position, y = (segment << 8) | positions in the chunk.
@@ -101,10 +105,13 @@ __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restri
 
 hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
                               int2* desc, hipStream_t st) {
-  launch_k(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, chunk_off);
+  // every segment adds at most one partial chunk; the workspace holds this many
+  const int64_t max_chunks = n_positions / kSeqChunk + (int64_t)S * R;
+  if (max_chunks > INT32_MAX) return hipErrorInvalidValue;
+  launch_k(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, (int32_t)max_chunks,
+           chunk_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S * R == 0) return e;
-  const int64_t max_chunks = n_positions / kSeqChunk + (int64_t)S * R;  // every segment adds at most one partial chunk
   launch_k(chunk_desc_kernel, dim3((unsigned)((max_chunks + 255) / 256)), dim3(256), 0, st, seq_offsets, R, S,
            n_positions, chunk_off, desc);
   return hipGetLastError();
@@ -146,7 +153,9 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   const int rw = wave & 3;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int SR = p.S * p.R;
-  const int total = p.chunk_off[SR];
+  // Offsets that break the layout contract (segments overlapping or out of order; flagged by the
+  // expand kernel) can count more chunks than the workspace holds: never walk past that bound.
+  const int total = p.chunk_off[SR] < p.max_chunks ? p.chunk_off[SR] : p.max_chunks;
   const int per = (total + gridDim.x - 1) / gridDim.x;
   const int c_begin = blockIdx.x * per;
   const int c_end = c_begin + per < total ? c_begin + per : total;
@@ -441,7 +450,8 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) 
 // rest of the batch.  Lane t reads four columns of every eighth chunk (16-byte loads).
 __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ seq_offsets, int R, int S,
-                                                       int64_t n_positions, float* __restrict__ pool) {
+                                                       int64_t n_positions, int32_t max_chunks,
+                                                       float* __restrict__ pool) {
   constexpr int kChains = 8;
   __shared__ float4 sm[kChains][kD / 4];
   const int g = blockIdx.x;
@@ -451,7 +461,9 @@ __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__
   a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
   e = e < a ? a : (e > n_positions ? n_positions : e);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = chunk_off[g] + chain; c < chunk_off[g + 1]; c += kChains) {
+  // chunk offsets past the workspace's chunk count come only from offsets the expand kernel flags
+  const int c_hi = chunk_off[g + 1] < max_chunks ? chunk_off[g + 1] : max_chunks;
+  for (int c = chunk_off[g] + chain; c < c_hi; c += kChains) {
     const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)c * kD + 4 * q);
     acc.x += v.x;
     acc.y += v.y;
@@ -476,9 +488,10 @@ __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__
 }
 
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
-                           int64_t n_positions, float* pool, hipStream_t st) {
+                           int64_t n_positions, int32_t max_chunks, float* pool, hipStream_t st) {
   if (R * S <= 0) return hipSuccess;
-  launch_k(seq_pool_kernel, dim3(R * S), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, pool);
+  launch_k(seq_pool_kernel, dim3(R * S), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, max_chunks,
+           pool);
   return hipGetLastError();
 }
 

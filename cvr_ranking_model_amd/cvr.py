@@ -24,6 +24,7 @@ CVR_SIDE_USER, CVR_SIDE_ITEM, CVR_SIDE_CONTEXT = 0, 1, 2
 CVR_LOWP_FP16, CVR_LOWP_BF16 = 0, 1
 (CVR_DBG_CAND_REQ, CVR_DBG_POOLED, CVR_DBG_INPUT_REQ, CVR_DBG_INPUT_ITEM, CVR_DBG_LOGITS, CVR_DBG_HSEQ,
  CVR_DBG_SEQ_POOL, CVR_DBG_TOKENS, CVR_DBG_QUERY, CVR_DBG_ATTN, CVR_DBG_HIDDEN) = range(11)
+CVR_OPT_DLRM_PASS_ROWS, CVR_OPT_TOK_SHARE, CVR_OPT_ATTN_MQ = range(3)
 SIDES = {"user": CVR_SIDE_USER, "item": CVR_SIDE_ITEM, "context": CVR_SIDE_CONTEXT}
 
 
@@ -65,6 +66,7 @@ _PROTOS = {
     "cvr_score_graph": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "cvr_sync_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "cvr_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
+    "cvr_set_option": (C.c_int, [C.c_void_p, C.c_int32, C.c_int64]),
     "cvr_debug_export": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t), C.c_void_p]),
     "cvr_timing_begin": (C.c_int, [C.c_void_p, C.c_int32, C.c_uint32]),
     "cvr_timing_end": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int32), C.c_int32,
@@ -147,6 +149,10 @@ def cvr_sync_status(h, stream):
 
 def cvr_set_debug(h, debug):
     _check(lib().cvr_set_debug(h, int(debug)), h)
+
+
+def cvr_set_option(h, option, value):
+    _check(lib().cvr_set_option(h, int(option), int(value)), h)
 
 
 def cvr_debug_export(h, what, dst_ptr, dst_bytes, stream):
@@ -413,6 +419,9 @@ class Model:
 
     def set_debug(self, on=True):
         cvr_set_debug(self.h, 1 if on else 0)
+
+    def set_option(self, option, value):
+        cvr_set_option(self.h, option, value)
 
     def export(self, what, dtype, shape):
         torch = _torch()

@@ -91,7 +91,8 @@ typedef struct {
  * of each feature's pooled bag.  Fields marked (CVR) are ignored for DLRM. */
 typedef struct {
   int32_t model;            /* CVR_MODEL_DLRM or CVR_MODEL_HYFORMER */
-  int32_t lowp;             /* CVR_LOWP_FP16 (DLRM) or CVR_LOWP_BF16 (CVR) */
+  int32_t lowp;             /* DLRM: CVR_LOWP_FP16 or CVR_LOWP_BF16; CVR: CVR_LOWP_BF16 only
+                               (CVR_ERR_UNSUPPORTED otherwise) */
   float clamp;              /* clamp bound after pooling (CTR article section 三: 10) */
   int32_t n_features;
   const cvr_feature* features;   /* host array [n_features] */
@@ -144,7 +145,10 @@ typedef struct {
  *     non-decreasing, bag_offsets[total_bags] = n_ids; ids are table rows.
  *   (CVR) seq_offsets [n_seq][n_requests+1]: positions of sequence s of
  *     request r are rows seq_offsets[s][r] .. seq_offsets[s][r+1]-1 of
- *     seq_ids; non-decreasing within each s; all inside [0, n_positions].
+ *     seq_ids; all inside [0, n_positions], and the whole array read as one
+ *     list is non-decreasing (within each s, and seq_offsets[s][n_requests] <=
+ *     seq_offsets[s+1][0]), so no position belongs to two sequences.
+ *     n_seq * n_requests < 2^23.
  *   (CVR) seq_ids [n_positions][n_seq_cols]: table rows of each column.
  * Offsets are per-request metadata passed as tensors (CVR article section
  * 3.3); the caller packs them on the host and copies them in one transfer
@@ -188,9 +192,8 @@ cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_c
  * Enqueued on hip_stream; returns without synchronising.
  * DLRM specs run the hidden layers over slices of the candidates, each slice
  * through every layer before the next (at most 128 MB per activation buffer:
- * 65536 candidates at width 1024; the environment variable
- * CVR_DLRM_PASS_ROWS, read by cvr_create, sets another slice size, 0 meaning
- * one slice).  Scores do not depend on the slicing.  With debug on, one slice
+ * 65536 candidates at width 1024; CVR_OPT_DLRM_PASS_ROWS sets another slice
+ * size).  Scores do not depend on the slicing.  With debug on, one slice
  * covers the batch so that the last hidden layer can be exported whole.  With
  * debug off, a last hidden layer that runs on the wide GEMM kernel also forms
  * the output layer's per-row partial sums over 64-column groups and stores
@@ -214,6 +217,22 @@ cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size
  * released by cvr_destroy. */
 cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
                            float* out_scores, void* hip_stream);
+
+/* Kernel-selection options of a model.  Each has a default that scoring uses unless the option
+ * is set; scores do not depend on them beyond the order of fp32 additions (DLRM_PASS_ROWS: not
+ * at all).  Setting an option discards a graph captured by cvr_score_graph.  Values:
+ *   CVR_OPT_DLRM_PASS_ROWS  DLRM: candidates per MLP pass (each pass through every layer before
+ *                           the next).  -1 (default): as many as fill 128 MB per activation
+ *                           buffer (65536 at width 1024); 0: one pass; k > 0: k candidates.
+ *   CVR_OPT_TOK_SHARE       CVR: tokenizer request-side columns multiplied once per request and
+ *                           added to every candidate of the request.  -1 (default): when requests
+ *                           average 4 or more candidates; 0: never; 1: whenever the spec allows.
+ *   CVR_OPT_ATTN_MQ         CVR: attention of a request's candidates as MFMA products over its
+ *                           shared states.  -1 (default): when requests average 16 or more
+ *                           candidates; 0: never (one block per candidate); 1: always.
+ * Unknown options and values outside these ranges return CVR_ERR_ARG. */
+enum { CVR_OPT_DLRM_PASS_ROWS = 0, CVR_OPT_TOK_SHARE = 1, CVR_OPT_ATTN_MQ = 2 };
+cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value);
 
 /* Wait for the stream and report the device error flag of the last
  * cvr_score on that workspace: CVR_ERR_RANGE if an id was outside its table

@@ -34,12 +34,14 @@ from .dlrm import dlrm_forward
 from .hyformer import hyformer_forward, token_mix, token_revert
 
 
-def score(spec, tables, weights, batch, requests=None, exact=False, trace=False):
-    """Score a batch (or a subset of its requests) with the model the spec names."""
+def score(spec, tables, weights, batch, requests=None, exact=False, trace=False, accumulate="fp64"):
+    """Score a batch (or a subset of its requests) with the model the spec names.
+    ``accumulate`` (CVR model only): "fp64" (default) or "fp32" sums in every Linear."""
     if spec["model"] == "dlrm":
         return dlrm_forward(spec, tables, weights, batch, requests=requests, exact=exact)
     if spec["model"] == "hyformer":
-        return hyformer_forward(spec, tables, weights, batch, requests=requests, exact=exact, trace=trace)
+        return hyformer_forward(spec, tables, weights, batch, requests=requests, exact=exact, trace=trace,
+                                accumulate=accumulate)
     raise OracleInputError(f"unknown model {spec['model']!r}")
 
 

@@ -74,6 +74,10 @@ def expand(spec, batch):
             raise OracleInputError(f"seq_ids must be [positions, {ncol}]")
         if np.any(np.diff(so, axis=1) < 0) or so.min() < 0 or so.max() > sid.shape[0]:
             raise OracleInputError("seq_offsets must be non-decreasing and inside seq_ids")
+        # the batch layout keeps sequences apart: sequence s ends before sequence s+1 begins,
+        # so no position belongs to two sequences
+        if np.any(np.diff(so.reshape(-1)) < 0):
+            raise OracleInputError("sequences must not overlap: seq_offsets read as one list must be non-decreasing")
         for ci, col in enumerate(spec["seq"]["columns"]):
             rows = spec["tables"][col["table"]]["rows"]
             c = sid[:, ci]

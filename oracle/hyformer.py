@@ -22,6 +22,19 @@ from .common import expand, candidate_inputs, clamp, sigmoid, requests_to_candid
 from .lowp import rounder
 
 
+def matmul64(a, b):
+    """A Linear's products summed in fp64 (the oracle's default)."""
+    return np.asarray(a, dtype=np.float64) @ np.asarray(b, dtype=np.float64)
+
+
+def matmul32(a, b):
+    """The same products summed in fp32.  The operands are low-precision values, so every
+    product is exact in fp32 and only the summation is rounded: this is what a device that
+    accumulates in fp32 computes, up to the order of its additions.  Used to measure how far
+    two valid evaluations of the precision plan can sit apart."""
+    return (np.asarray(a, dtype=np.float32) @ np.asarray(b, dtype=np.float32)).astype(np.float64)
+
+
 def _w(weights, name, rnd):
     return rnd(np.asarray(weights[name], dtype=np.float32).astype(np.float64))
 
@@ -44,7 +57,7 @@ def softmax(x, axis=-1):
     return e / np.sum(e, axis=axis, keepdims=True)
 
 
-def tokenize(spec, weights, e, rnd):
+def tokenize(spec, weights, e, rnd, mm=matmul64):
     """Step B2: non-sequence tokens.
 
     The CVR article (sections 3.2.2-3.2.3) splits the concatenated user, item
@@ -55,7 +68,7 @@ def tokenize(spec, weights, e, rnd):
     cannot work: 1280 input columns do not divide into 13 tokens of 128.
     """
     N, d = spec["n_tokens"], spec["d"]
-    y = e @ _w(weights, "tok.weight", rnd).T + _b(weights, "tok.bias")
+    y = mm(e, _w(weights, "tok.weight", rnd).T) + _b(weights, "tok.bias")
     return y.reshape(e.shape[0], N, d)
 
 
@@ -77,7 +90,7 @@ def sequence_rows(spec, tables, ex, s, requests):
     return np.concatenate(cols, axis=1), lens
 
 
-def swiglu(weights, s, E, rnd):
+def swiglu(weights, s, E, rnd, mm=matmul64):
     """Step B4: the per-position SwiGLU encoder of sequence ``s``.
 
     The CVR article (sections 3.2.2-3.2.3) maps each of the three sequences
@@ -86,10 +99,10 @@ def swiglu(weights, s, E, rnd):
     + b_down, no residual and no normalisation.  The product is the input of
     the down projection, so it is rounded to the low-precision type.
     """
-    g = E @ _w(weights, f"seq.{s}.gate.weight", rnd).T + _b(weights, f"seq.{s}.gate.bias")
-    u = E @ _w(weights, f"seq.{s}.up.weight", rnd).T + _b(weights, f"seq.{s}.up.bias")
+    g = mm(E, _w(weights, f"seq.{s}.gate.weight", rnd).T) + _b(weights, f"seq.{s}.gate.bias")
+    u = mm(E, _w(weights, f"seq.{s}.up.weight", rnd).T) + _b(weights, f"seq.{s}.up.bias")
     a = rnd(silu(g) * u)
-    return rnd(a @ _w(weights, f"seq.{s}.down.weight", rnd).T + _b(weights, f"seq.{s}.down.bias"))
+    return rnd(mm(a, _w(weights, f"seq.{s}.down.weight", rnd).T) + _b(weights, f"seq.{s}.down.bias"))
 
 
 def mean_pool(H):
@@ -99,7 +112,7 @@ def mean_pool(H):
     return H.sum(axis=0) / H.shape[0]
 
 
-def query(weights, l, s, X, p, rnd):
+def query(weights, l, s, X, p, rnd, mm=matmul64):
     """Step B6: one global query per sequence.
 
     The CVR article (section 3.2.3, Query Decoding) concatenates the N
@@ -110,10 +123,10 @@ def query(weights, l, s, X, p, rnd):
     ``X`` is [c, N, d], ``p`` is [c, d].
     """
     inp = rnd(np.concatenate([X.reshape(X.shape[0], -1), p], axis=1))
-    return inp @ _w(weights, f"layer.{l}.query.{s}.weight", rnd).T + _b(weights, f"layer.{l}.query.{s}.bias")
+    return mm(inp, _w(weights, f"layer.{l}.query.{s}.weight", rnd).T) + _b(weights, f"layer.{l}.query.{s}.bias")
 
 
-def cross_attention(H, q, tau, rnd):
+def cross_attention(H, q, tau, rnd, mm=matmul64):
     """Step B7: one query attending over one sequence's hidden states.
 
     The CVR article (section 3.2.3) takes the SwiGLU-encoded states directly
@@ -125,8 +138,8 @@ def cross_attention(H, q, tau, rnd):
     """
     if H.shape[0] == 0:
         return np.zeros(H.shape[1]), np.zeros(0)
-    a = softmax((H @ q) / tau)
-    return a @ H, a
+    a = softmax(mm(H, q) / tau)
+    return mm(a, H), a
 
 
 def token_mix(Y, heads):
@@ -155,7 +168,7 @@ def token_revert(F, tokens):
     return F.reshape(lead + (Hh, tokens, w)).swapaxes(-3, -2).reshape(lead + (tokens, Hh * w))
 
 
-def mixer(spec, weights, l, Y, rnd):
+def mixer(spec, weights, l, Y, rnd, mm=matmul64):
     """Step B8: Z = Y + Revert(FFN_h(Mix(Y)_h)) for one stacked layer.
 
     Reading: one FFN per mixed token (Linear -> ReLU -> Linear with biases,
@@ -166,9 +179,9 @@ def mixer(spec, weights, l, Y, rnd):
     M = rnd(token_mix(Y, H))
     F = np.empty_like(M)
     for h in range(H):
-        hid = rnd(np.maximum(M[:, h, :] @ _w(weights, f"layer.{l}.mix.{h}.fc1.weight", rnd).T
+        hid = rnd(np.maximum(mm(M[:, h, :], _w(weights, f"layer.{l}.mix.{h}.fc1.weight", rnd).T)
                              + _b(weights, f"layer.{l}.mix.{h}.fc1.bias"), 0.0))
-        F[:, h, :] = hid @ _w(weights, f"layer.{l}.mix.{h}.fc2.weight", rnd).T + _b(weights, f"layer.{l}.mix.{h}.fc2.bias")
+        F[:, h, :] = mm(hid, _w(weights, f"layer.{l}.mix.{h}.fc2.weight", rnd).T) + _b(weights, f"layer.{l}.mix.{h}.fc2.bias")
     return Y + token_revert(F, Y.shape[1])
 
 
@@ -181,7 +194,7 @@ def task_experts(spec):
     return [sorted(int(e) for e in lst) for lst in lists]
 
 
-def ple_heads(spec, weights, z, rnd):
+def ple_heads(spec, weights, z, rnd, mm=matmul64):
     """Steps B10-B11: PLE experts, per-task gates and two-layer heads.
 
     The CVR article (section 3.2.4) predicts each scenario's pCVR with
@@ -200,20 +213,20 @@ def ple_heads(spec, weights, z, rnd):
     """
     E = spec["n_experts"]
     z = rnd(z)
-    experts = [np.maximum(z @ _w(weights, f"ple.expert.{e}.weight", rnd).T + _b(weights, f"ple.expert.{e}.bias"), 0.0)
+    experts = [np.maximum(mm(z, _w(weights, f"ple.expert.{e}.weight", rnd).T) + _b(weights, f"ple.expert.{e}.bias"), 0.0)
                for e in range(E)]
     logits, tin = [], []
     for k, mixed in enumerate(task_experts(spec)):
-        g = softmax(z @ _w(weights, f"ple.gate.{k}.weight", rnd).T + _b(weights, f"ple.gate.{k}.bias"))
+        g = softmax(mm(z, _w(weights, f"ple.gate.{k}.weight", rnd).T) + _b(weights, f"ple.gate.{k}.bias"))
         t = rnd(sum(g[:, i:i + 1] * experts[e] for i, e in enumerate(mixed)))
-        u = rnd(np.maximum(t @ _w(weights, f"head.{k}.fc1.weight", rnd).T + _b(weights, f"head.{k}.fc1.bias"), 0.0))
-        y = u @ _w(weights, f"head.{k}.fc2.weight", rnd).T + _b(weights, f"head.{k}.fc2.bias")
+        u = rnd(np.maximum(mm(t, _w(weights, f"head.{k}.fc1.weight", rnd).T) + _b(weights, f"head.{k}.fc1.bias"), 0.0))
+        y = mm(u, _w(weights, f"head.{k}.fc2.weight", rnd).T) + _b(weights, f"head.{k}.fc2.bias")
         logits.append(y[:, 0])
         tin.append(t)
     return np.stack(logits, axis=1), tin
 
 
-def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, trace=False):
+def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, trace=False, accumulate="fp64"):
     """Steps B0-B11 for all candidates (or those of the listed requests).
 
     Sequences belong to the request (the user's behaviour); every candidate of
@@ -223,6 +236,9 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
     sequences and their pooled vectors are shared by all layers, and the
     prediction level reads the last layer's full token matrix.
 
+    ``accumulate="fp32"`` sums every Linear's (and the attention's) products in fp32 instead
+    of fp64 (see :func:`matmul32`); the default is fp64.
+
     Returns ``scores`` fp32 [c, tasks], ``logits`` fp64 [c, tasks], ``cand``;
     with ``trace`` also the intermediates (``e``, ``X0``, ``H``, ``p``,
     ``q``, ``o``, ``Z``, ``attn``).
@@ -230,6 +246,9 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
     if spec["model"] != "hyformer":
         raise OracleInputError("not a CVR spec")
     rnd = rounder(spec["lowp"], exact)
+    if accumulate not in ("fp64", "fp32"):
+        raise OracleInputError("accumulate must be fp64 or fp32")
+    mm = matmul32 if accumulate == "fp32" else matmul64
     ex = expand(spec, batch)
     R = ex["R"]
     reqs = list(range(R)) if requests is None else [int(r) for r in requests]
@@ -241,14 +260,14 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
 
     # B1-B2: non-sequence input and tokens, per candidate.
     e, pooled = candidate_inputs(spec, tables, ex, cands, rnd)
-    X = tokenize(spec, weights, e, rnd)
+    X = tokenize(spec, weights, e, rnd, mm)
 
     # B3-B5: per request and sequence.
     Hs, ps = {}, {}
     for s in range(S):
         rows, lens = sequence_rows(spec, tables, ex, s, reqs)
         Eseq = rnd(clamp(rows, spec["clamp"]).astype(np.float64))
-        Hall = swiglu(weights, s, Eseq, rnd) if rows.shape[0] else np.zeros((0, d))
+        Hall = swiglu(weights, s, Eseq, rnd, mm) if rows.shape[0] else np.zeros((0, d))
         off = np.concatenate([[0], np.cumsum(lens)])
         for i, r in enumerate(reqs):
             Hs[(s, r)] = Hall[off[i]:off[i + 1]]
@@ -262,23 +281,23 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
         ql, al = [], []
         for s in range(S):
             p = np.stack([ps[(s, int(r))] for r in cand_req]) if nc else np.zeros((0, d))
-            q = query(weights, l, s, X, p, rnd)
+            q = query(weights, l, s, X, p, rnd, mm)
             o = np.zeros((nc, d))
             att = []
             for i in range(nc):
-                o[i], a = cross_attention(Hs[(s, int(cand_req[i]))], q[i], tau, rnd)
+                o[i], a = cross_attention(Hs[(s, int(cand_req[i]))], q[i], tau, rnd, mm)
                 att.append(a)
             outs.append(o)
             ql.append(q)
             al.append(att)
         Y = np.concatenate([X, np.stack(outs, axis=1)], axis=1)
-        Z = mixer(spec, weights, l, Y, rnd)
+        Z = mixer(spec, weights, l, Y, rnd, mm)
         X = Z[:, :N, :]
         tr["q"].append(ql)
         tr["o"].append(outs)
         tr["Z"].append(Z)
         tr["attn"].append(al)
-    logits, tin = ple_heads(spec, weights, Z.reshape(nc, -1), rnd)
+    logits, tin = ple_heads(spec, weights, Z.reshape(nc, -1), rnd, mm)
     tr["task_in"] = tin
     out = {"scores": sigmoid(logits).astype(np.float32), "logits": logits, "cand": cands, "ex": ex}
     if trace:

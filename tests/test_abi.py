@@ -102,6 +102,24 @@ def test_bad_specs_are_rejected_on_the_host():
     assert e.value.status == cv.CVR_ERR_UNSUPPORTED
 
 
+def test_cvr_spec_in_fp16_is_rejected():
+    """The CVR kernels compute in bf16 (the CVR article's BF16 inference): a CVR spec asking for
+    fp16 is refused rather than scored with fp16 bit patterns read as bf16."""
+    cvr = synth.load_spec("c3")
+    s, tabs, keep = _spec_c(dict(cvr, lowp="fp16"))
+    with pytest.raises(cv.CvrError, match="bf16") as e:
+        cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"]))
+    assert e.value.status == cv.CVR_ERR_UNSUPPORTED
+    s, tabs, keep = _spec_c(cvr)
+    assert cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"])) > 0
+
+
+def test_set_option_needs_a_handle_and_known_values():
+    L = cv.lib()
+    assert L.cvr_set_option(None, cv.CVR_OPT_ATTN_MQ, 1) == cv.CVR_ERR_ARG
+    assert "null handle" in L.cvr_last_error(None).decode()
+
+
 def test_fill_and_create_argument_checks():
     with pytest.raises(cv.CvrError) as e:
         cv.cvr_fill_table(None, 10, 4, 1, 0.05, None)

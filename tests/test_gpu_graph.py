@@ -95,3 +95,28 @@ def test_graph_needs_created_stream():
     import ctypes as C
     with pytest.raises(cv.CvrError):
         cv.cvr_score_graph(m.h, db.c, C.c_void_p(ws.data_ptr()), ws.numel(), C.c_void_p(out.data_ptr()), C.c_void_p(0))
+
+
+def test_graph_replay_restores_export_state():
+    """A replay leaves the handle describing the replayed call: after a debug-off graph (last
+    layer's tokens written as bf16) is replayed following an eager debug-on call, the fp32 token
+    export is refused instead of returning bf16 bytes read as fp32."""
+    spec = synth.load_spec("c3")
+    banner("graph replay c3: export state after replay")
+    m, _ = build_model(spec, "stress", debug=False)
+    db = cv.DeviceBatch(synth.make_batch(spec, requests=8, seed_offset=6))
+    out = torch.empty(db.n_candidates * spec["n_tasks"], dtype=torch.float32, device="cuda")
+    shape = (db.n_candidates, spec["n_tokens"] + 3, spec["d"])
+    m.score_graph(db, out)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    m.set_debug(True)
+    m.score(db)
+    assert m.sync_status() == cv.CVR_OK
+    m.export(cv.CVR_DBG_TOKENS, torch.float32, shape)          # fp32 tokens after the debug call
+    m.set_debug(False)
+    m.score_graph(db, out)                                     # replays the debug-off capture
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    with pytest.raises(cv.CvrError, match="bf16"):
+        m.export(cv.CVR_DBG_TOKENS, torch.float32, shape)

@@ -279,14 +279,34 @@ def test_empty_sequence_gives_zero_pool_and_output(rng):
     assert np.all(np.isfinite(out["scores"]))
 
 
-def _brute_force(spec, tables, w, b):
-    """Whole model, one candidate at a time, with explicit index loops (exact arithmetic)."""
+def scalar_bf16(x):
+    """Round one Python float to the nearest bfloat16 value, ties to even: keep 8 significant
+    bits of the binary significand (Python's round() breaks exact halves to even)."""
+    if x == 0.0 or math.isinf(x) or math.isnan(x):
+        return x
+    if abs(x) < 2.0 ** -126:                      # below fp32's normal range: fixed quantum 2^-133
+        return round(x * 2.0 ** 133) * 2.0 ** -133
+    m, e = math.frexp(x)
+    return math.ldexp(round(math.ldexp(m, 8)), e - 8)
+
+
+def _brute_force(spec, tables, w, b, rb=None):
+    """Whole model, one candidate at a time, with explicit index loops.
+
+    ``rb`` None: exact arithmetic.  Otherwise ``rb`` rounds one scalar and is applied where
+    the precision plan of the CVR article's BF16 inference (section 3.4.3) rounds: every
+    Linear weight, every Linear input (the pooled inputs, each sequence position, the SwiGLU
+    product, the query input, the mixed tokens and the mixer hidden layer, the flattened token
+    matrix, the gated task input, the head hidden layer) and the stored sequence states."""
     ex = oracle.expand(spec, b)
     d, N, S, Hh = spec["d"], spec["n_tokens"], 3, spec["mixer_heads"]
     T = N + S
     wd = d // Hh
-    lin = lambda W, x, bias: [sum(float(W[i][k]) * x[k] for k in range(len(x))) + float(bias[i]) for i in range(len(bias))]
+    rnd = (lambda v: [rb(float(a)) for a in v]) if rb else (lambda v: [float(a) for a in v])
+    W = {k: [rnd(row) for row in np.atleast_2d(v)] if k.endswith(".weight") else [float(a) for a in v] for k, v in w.items()}
+    lin = lambda Wm, x, bias: [sum(Wm[i][k] * x[k] for k in range(len(x))) + bias[i] for i in range(len(bias))]
     relu = lambda v: [max(a, 0.0) for a in v]
+    w = W
     out = []
     for c in range(ex["n"]):
         r = int(ex["cand_req"][c])
@@ -301,6 +321,7 @@ def _brute_force(spec, tables, w, b):
                     acc = np.float32(acc + tables[f["table"]][ex["ids"][k], j])
                 v = float(acc / np.float32(hi - lo)) if hi > lo else 0.0
                 e.append(min(max(v, -10.0), 10.0))
+        e = rnd(e)
         y = lin(w["tok.weight"], e, w["tok.bias"])
         X = [[y[i * d + j] for j in range(d)] for i in range(N)]
         Hs, ps = [], []
@@ -310,16 +331,17 @@ def _brute_force(spec, tables, w, b):
                 row = []
                 for ci, col in enumerate(spec["seq"]["columns"]):
                     row += [min(max(float(v), -10.0), 10.0) for v in tables[col["table"]][ex["seq_ids"][pidx, ci]]]
+                row = rnd(row)
                 g = lin(w[f"seq.{s}.gate.weight"], row, w[f"seq.{s}.gate.bias"])
                 u = lin(w[f"seq.{s}.up.weight"], row, w[f"seq.{s}.up.bias"])
-                a = [gi / (1 + math.exp(-gi)) * ui for gi, ui in zip(g, u)]
-                Hrows.append(lin(w[f"seq.{s}.down.weight"], a, w[f"seq.{s}.down.bias"]))
+                a = rnd([gi / (1 + math.exp(-gi)) * ui for gi, ui in zip(g, u)])
+                Hrows.append(rnd(lin(w[f"seq.{s}.down.weight"], a, w[f"seq.{s}.down.bias"])))
             Hs.append(Hrows)
             ps.append([sum(h[j] for h in Hrows) / len(Hrows) if Hrows else 0.0 for j in range(d)])
         for l in range(spec["n_layers"]):
             Y = [list(x) for x in X]
             for s in range(S):
-                q = lin(w[f"layer.{l}.query.{s}.weight"], [v for x in X for v in x] + ps[s], w[f"layer.{l}.query.{s}.bias"])
+                q = lin(w[f"layer.{l}.query.{s}.weight"], rnd([v for x in X for v in x] + ps[s]), w[f"layer.{l}.query.{s}.bias"])
                 if Hs[s]:
                     sc = [sum(h[j] * q[j] for j in range(d)) / spec["tau"] for h in Hs[s]]
                     m = max(sc)
@@ -330,14 +352,14 @@ def _brute_force(spec, tables, w, b):
                     Y.append([0.0] * d)
             Zt = [list(y) for y in Y]
             for h in range(Hh):
-                m_h = [Y[t][h * wd + j] for t in range(T) for j in range(wd)]
-                hid = relu(lin(w[f"layer.{l}.mix.{h}.fc1.weight"], m_h, w[f"layer.{l}.mix.{h}.fc1.bias"]))
+                m_h = rnd([Y[t][h * wd + j] for t in range(T) for j in range(wd)])
+                hid = rnd(relu(lin(w[f"layer.{l}.mix.{h}.fc1.weight"], m_h, w[f"layer.{l}.mix.{h}.fc1.bias"])))
                 F = lin(w[f"layer.{l}.mix.{h}.fc2.weight"], hid, w[f"layer.{l}.mix.{h}.fc2.bias"])
                 for t in range(T):
                     for j in range(wd):
                         Zt[t][h * wd + j] += F[t * wd + j]
             X = Zt[:N]
-        z = [v for tok in Zt for v in tok]
+        z = rnd([v for tok in Zt for v in tok])
         experts = [relu(lin(w[f"ple.expert.{e_}.weight"], z, w[f"ple.expert.{e_}.bias"])) for e_ in range(spec["n_experts"])]
         logits = []
         lists = spec.get("ple_task_experts") or [list(range(spec["n_experts"]))] * spec["n_tasks"]
@@ -347,8 +369,8 @@ def _brute_force(spec, tables, w, b):
             ge = [math.exp(v - m) for v in gl]
             ge = [v / sum(ge) for v in ge]
             mixed = sorted(lists[k])
-            t_in = [sum(ge[i] * experts[e_][j] for i, e_ in enumerate(mixed)) for j in range(spec["expert_dim"])]
-            u = relu(lin(w[f"head.{k}.fc1.weight"], t_in, w[f"head.{k}.fc1.bias"]))
+            t_in = rnd([sum(ge[i] * experts[e_][j] for i, e_ in enumerate(mixed)) for j in range(spec["expert_dim"])])
+            u = rnd(relu(lin(w[f"head.{k}.fc1.weight"], t_in, w[f"head.{k}.fc1.bias"])))
             logits.append(lin(w[f"head.{k}.fc2.weight"], u, w[f"head.{k}.fc2.bias"])[0])
         out.append(logits)
     return np.array(out)
@@ -363,11 +385,26 @@ def test_whole_model_brute_force_exact(layers, task_experts):
     assert np.allclose(got, want, rtol=1e-11, atol=1e-11)
 
 
-def test_bf16_plan_stays_near_exact():
-    spec, tables, w, b = _tiny_model(C=2)
-    lo = oracle.score(spec, tables, w, b)["scores"]
-    hi = oracle.score(spec, tables, w, b, exact=True)["scores"]
-    assert 0 < np.abs(lo - hi).max() < 0.05
+@pytest.mark.parametrize("layers,task_experts", [(1, None), (2, None), (1, [[0, 2], [1, 2]])])
+def test_whole_model_brute_force_bf16_plan(layers, task_experts):
+    """The default (bf16) oracle equals the scalar brute force that rounds at exactly the
+    precision plan's points, with a rounding function of its own."""
+    spec, tables, w, b = _tiny_model(layers=layers, C=2, lens=[[3, 0, 2], [1, 4, 2], [2, 2, 1]],
+                                     ple_task_experts=task_experts)
+    got = oracle.score(spec, tables, w, b)["logits"]
+    want = _brute_force(spec, tables, w, b, rb=scalar_bf16)
+    assert np.allclose(got, want, rtol=1e-11, atol=1e-11)
+    # and the rounding is visible: the plan differs from exact arithmetic
+    assert not np.allclose(got, _brute_force(spec, tables, w, b), rtol=1e-6, atol=1e-6)
+
+
+def test_scalar_bf16_by_hand():
+    assert scalar_bf16(1.0 + 2.0 ** -8) == 1.0                        # tie -> even
+    assert scalar_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6        # tie -> even (up)
+    assert scalar_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert scalar_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -20)) == -(1.0 + 2.0 ** -7)
+    assert scalar_bf16(3.0 * 2.0 ** -130) == 3.0 * 2.0 ** -130       # fp32 subnormal range, exact
+    assert scalar_bf16(0.1) == 0.10009765625
 
 
 def test_c3_shapes():
