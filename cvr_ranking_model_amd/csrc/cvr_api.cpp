@@ -20,7 +20,7 @@ using namespace cvr;
 
 static thread_local std::string g_last_error;
 
-static cvr_status fail(cvr_model* m, cvr_status s, const std::string& msg) {
+cvr_status cvr::fail(cvr_model* m, cvr_status s, const std::string& msg) {
   if (m) m->err = msg;
   g_last_error = msg;
   return s;
@@ -668,6 +668,12 @@ static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsP
 
 extern "C" cvr_status cvr_score(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes, float* out_scores,
                                 void* hip_stream) {
+  return cvr::score_call(h, b, workspace, ws_bytes, out_scores, hip_stream);
+}
+
+// The scoring call behind cvr_score and the entry points that bring their own workspace.
+cvr_status cvr::score_call(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes, float* out_scores,
+                           void* hip_stream) {
   if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
   WsPlan plan;
   cvr_status st = check_batch(h, b, workspace, ws_bytes, out_scores, plan);

@@ -133,6 +133,11 @@ struct cvr_model {
 
 namespace cvr {
 WsPlan plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P);
+// Records msg as the handle's (and the thread's) last error and returns s.
+cvr_status fail(cvr_model* m, cvr_status s, const std::string& msg);
+// cvr_score's work: checks, then the launches into the given workspace.
+cvr_status score_call(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes, float* out_scores,
+                      void* hip_stream);
 // Candidates per DLRM MLP pass for a batch of n (all of them in debug mode).
 int64_t dlrm_pass_rows(const cvr_model* m, int64_t n);
 

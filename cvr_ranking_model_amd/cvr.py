@@ -64,6 +64,7 @@ _PROTOS = {
     "cvr_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int64, C.c_int64, C.POINTER(C.c_size_t)]),
     "cvr_score": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "cvr_score_graph": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
+    "cvr_score_noalloc": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_void_p]),
     "cvr_sync_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "cvr_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
     "cvr_set_option": (C.c_int, [C.c_void_p, C.c_int32, C.c_int64]),
@@ -137,6 +138,13 @@ def cvr_score(h, batch_c, ws_ptr, ws_bytes, out_ptr, stream):
 
 def cvr_score_graph(h, batch_c, ws_ptr, ws_bytes, out_ptr, stream):
     _check(lib().cvr_score_graph(h, C.byref(batch_c), ws_ptr, ws_bytes, out_ptr, stream), h)
+
+
+def cvr_score_noalloc(h, batch_c, out_ptr, stream):
+    _check(lib().cvr_score_noalloc(h, C.byref(batch_c), out_ptr, stream), h)
+
+
+CVR_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def cvr_sync_status(h, stream):
@@ -393,6 +401,14 @@ class Model:
             out = torch.empty(max(1, dbatch.n_candidates * self.n_tasks), dtype=torch.float32, device=self.device)
         cvr_score(self.h, dbatch.c, C.c_void_p(ws.data_ptr()), ws.numel(), C.c_void_p(out.data_ptr()),
                   _stream_ptr(self.stream))
+        return out
+
+    def score_noalloc(self, dbatch: DeviceBatch, out=None):
+        """cvr_score_noalloc on the model's stream: the library's own scratch array as workspace."""
+        torch = _torch()
+        if out is None:
+            out = torch.empty(max(1, dbatch.n_candidates * self.n_tasks), dtype=torch.float32, device=self.device)
+        cvr_score_noalloc(self.h, dbatch.c, C.c_void_p(out.data_ptr()), _stream_ptr(self.stream))
         return out
 
     def score_graph(self, dbatch: DeviceBatch, out=None):

@@ -203,6 +203,19 @@ cvr_status cvr_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_c
 cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
                      float* out_scores, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): cvr_score without a workspace argument.  The
+ * workspace is a fixed array of CVR_NOALLOC_SCRATCH_BYTES in the library's own device memory,
+ * one per device, held until the process ends; the call itself allocates nothing.  Batches
+ * whose cvr_workspace_bytes exceed it return CVR_ERR_WORKSPACE (64 MiB holds, e.g., a request
+ * of 1 user + 500 candidates of either model, or a few thousand DLRM candidates).  Every call
+ * on a device shares that device's array: calls that overlap on one device (several streams,
+ * threads or models) race and must be serialised by the caller.  cvr_sync_status and
+ * cvr_debug_export read the array as they read a workspace, until the next call on the
+ * device.  Same results as cvr_score (the same kernels). */
+#define CVR_NOALLOC_SCRATCH_BYTES (64u << 20)
+cvr_status cvr_score_noalloc(cvr_handle h, const cvr_batch* batch, float* out_scores, void* hip_stream);
+
 /* cvr_score through graph replay (CVR article section 3.4.4: the serving
  * path captures the scoring launches once per batch shape and replays them).
  * Same arguments and result as cvr_score.  The first call for a given key --
