@@ -231,16 +231,27 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     dom = max(stages, key=lambda k: stages[k][0])
     stats0 = {t: model.cache_stats(t) for t in cached}
     graph_dt = None
+    graph_info = None
     if args.graph:
-        for _ in range(max(1, warmup)):
-            model.score_graph(db, out)
+        # replays rotate over four batches of the workload (other ids, other id counts): one
+        # graph per batch bucket, captured on first use
+        gb = [synth.make_batch(spec, requests=batch, candidates=candidates, uniform_ids=uniform_ids,
+                               seed_offset=100 + i) for i in range(4)]
+        gdbs = [cv.DeviceBatch(b) for b in gb]
+        big = tuple(max(x) for x in zip(*[(d.n_requests, d.n_candidates, d.n_ids, d.n_positions) for d in gdbs]))
+        gout = torch.empty(max(d.n_candidates for d in gdbs) * model.n_tasks, dtype=torch.float32, device="cuda")
+        for i in range(max(4, warmup)):
+            model.score_graph(gdbs[i % 4], gout, ws_sizes=big)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
-            model.score_graph(db, out)
+        for i in range(steps):
+            model.score_graph(gdbs[i % 4], gout, ws_sizes=big)
         torch.cuda.synchronize()
         graph_dt = time.perf_counter() - t0
         assert model.sync_status() == cv.CVR_OK
+        held, caps = model.graph_info()
+        graph_info = {"batches": 4, "graphs_held": held, "captures": caps,
+                      "candidates_per_step": sum(d.n_candidates for d in gdbs) / 4}
     print(f"[bench] {workload}: timed region, {steps} steps", file=sys.stderr, flush=True)
     model.timing_begin(steps, [dom])
     torch.cuda.synchronize()
@@ -264,7 +275,7 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     for i in range(steps):
         ev[i][0].record(model.stream)
         if args.graph:
-            model.score_graph(db, out)
+            model.score_graph(gdbs[i % 4], gout, ws_sizes=big)
         else:
             model.score(dbs[i % nb], out)
         ev[i][1].record(model.stream)
@@ -292,7 +303,7 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
         torch.cuda.synchronize()
         del src, dst
     ms_step = dt * 1e3 / steps
-    value = n * steps / dt
+    value = (graph_info["candidates_per_step"] if graph_info else n) * steps / dt
 
     # per-stage rooflines from the live event timings; the dominant stage gives "roofline"
     works = [stage_work(spec, b) for b in batches]
@@ -368,6 +379,7 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     if args.graph:
         res["eager_ms_per_step"] = round(eager_dt * 1e3 / steps, 4)
         res["roofline_pass"] = "eager steps timed right after the graph replays (events on the roofline kernel)"
+        res["graph"] = graph_info
     if gather_control and not uniform_ids and not cached and "gather_pool" in table:
         # cold control: the same workload with uniform ids (no hot rows for the caches to hold)
         ub = synth.make_batch(spec, requests=batch, candidates=candidates, uniform_ids=True, seed_offset=7)

@@ -479,7 +479,7 @@ extern "C" const char* cvr_stage_name(cvr_handle, int32_t stage) {
 // ------------------------------------------------------------------ scoring
 
 
-static cvr_status check_batch(cvr_model* m, const cvr_batch* b, void* ws, size_t ws_bytes, float* out, WsPlan& plan) {
+static cvr_status check_batch_args(cvr_model* m, const cvr_batch* b, void* ws, float* out) {
   if (!b || !ws || !out) return fail(m, CVR_ERR_ARG, "null batch, workspace or output");
   if ((uintptr_t)ws & 255) return fail(m, CVR_ERR_ARG, "workspace must be 256-byte aligned");
   if (b->n_requests <= 0) return fail(m, CVR_ERR_ARG, "n_requests must be >= 1");
@@ -491,6 +491,12 @@ static cvr_status check_batch(cvr_model* m, const cvr_batch* b, void* ws, size_t
   // chunk descriptors carry the (sequence, request) segment in 23 bits
   if (m->spec.model == CVR_MODEL_HYFORMER && (int64_t)m->spec.n_seq * b->n_requests >= (1 << 23))
     return fail(m, CVR_ERR_ARG, "n_seq * n_requests must be below 2^23");
+  return CVR_OK;
+}
+
+static cvr_status check_batch(cvr_model* m, const cvr_batch* b, void* ws, size_t ws_bytes, float* out, WsPlan& plan) {
+  cvr_status st = check_batch_args(m, b, ws, out);
+  if (st != CVR_OK) return st;
   plan = plan_workspace(m, b->n_requests, b->n_candidates, m->spec.model == CVR_MODEL_DLRM ? 0 : b->n_positions);
   if (ws_bytes < plan.total) return fail(m, CVR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.total) + " bytes");
   return CVR_OK;
@@ -511,7 +517,10 @@ static GatherCache gather_cache(const cvr_model::Cache& c, int32_t dim) {
 }
 
 // Shared front of both models: flag clear, expand, gather-pool into the two input matrices.
-static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan& w, Launcher& L, hipStream_t s) {
+// bucket: the batch is a graph bucket's padded staging copy, whose n_ids is a capacity (its last
+// bag may end before it).
+static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan& w, Launcher& L, hipStream_t s,
+                            bool bucket = false) {
   const cvr_spec& sp = m->spec;
   int32_t* flag = (int32_t*)(ws + w.flag);
   int64_t total_bags = 0;
@@ -530,6 +539,7 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
   ep.n_positions = b->n_positions;
   ep.cand_req = (int32_t*)(ws + w.cand_req);
   ep.flag = flag;
+  ep.ids_capacity = bucket ? 1 : 0;
   e = L(STAGE_EXPAND, [&] { return launch_expand(ep, s); });
   if (e != hipSuccess) return e;
 
@@ -697,78 +707,228 @@ cvr_status cvr::score_call(cvr_handle h, const cvr_batch* b, void* workspace, si
   return CVR_OK;
 }
 
-// ------------------------------------------------------------------ graph replay
+// ------------------------------------------------------------------ graph replay per batch bucket
 void GraphCache::reset() {
-  if (exec) (void)hipGraphExecDestroy(exec);
-  if (graph) (void)hipGraphDestroy(graph);
-  exec = nullptr;
-  graph = nullptr;
-  valid = false;
+  for (GraphEntry& g : entries) {
+    for (hipGraphExec_t x : g.exec)
+      if (x) (void)hipGraphExecDestroy(x);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+  }
+  entries.clear();
 }
 
-static bool same_key(const GraphCache& g, const cvr_batch* b, void* ws, size_t ws_bytes, float* out, hipStream_t s,
-                     int debug) {
-  return g.valid && g.ws == ws && g.ws_bytes == ws_bytes && g.out == out && g.stream == s && g.debug == debug &&
-         g.batch.n_requests == b->n_requests && g.batch.n_candidates == b->n_candidates && g.batch.n_ids == b->n_ids &&
-         g.batch.n_positions == b->n_positions && g.batch.cand_offsets == b->cand_offsets &&
-         g.batch.bag_offsets == b->bag_offsets && g.batch.ids == b->ids && g.batch.seq_offsets == b->seq_offsets &&
-         g.batch.seq_ids == b->seq_ids;
+static int64_t round_bucket(int64_t x) {
+  if (x < 16) return x;
+  int k = 0;
+  while ((x >> k) >= 16) ++k;
+  return ((x + (int64_t{1} << k) - 1) >> k) << k;  // m * 2^k, 8 <= m <= 16
+}
+
+void cvr::bucket_sizes(const cvr_model* m, int64_t R, int64_t n, int64_t ids, int64_t P, int64_t& Rb, int64_t& nb,
+                       int64_t& idsb, int64_t& Pb) {
+  Rb = round_bucket(R + 1);
+  nb = round_bucket(n + 1);
+  idsb = round_bucket(ids);
+  Pb = m->spec.model == CVR_MODEL_HYFORMER ? round_bucket(P) : 0;
+}
+
+GraphPlan cvr::plan_graph(const cvr_model* m, int64_t Rb, int64_t nb, int64_t idsb, int64_t Pb) {
+  GraphPlan g;
+  g.plan = plan_workspace(m, Rb, nb, Pb);
+  size_t off = g.plan.total;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  int64_t bags = 0;
+  for (int f = 0; f < m->spec.n_features; ++f) bags += m->feats[f].side == CVR_SIDE_ITEM ? nb : Rb;
+  const bool cvrm = m->spec.model == CVR_MODEL_HYFORMER;
+  const int tasks = cvrm ? m->spec.n_tasks : 1;
+  g.co = take((size_t)(Rb + 1) * 4);
+  g.bo = take((size_t)(bags + 1) * 4);
+  g.ids = take((size_t)idsb * 4);
+  g.so = take(cvrm ? (size_t)m->spec.n_seq * (Rb + 1) * 4 : 0);
+  g.scores = take((size_t)nb * tasks * 4);
+  g.hdr = take(sizeof(BucketHeader));
+  g.total = align256(off);
+  return g;
+}
+
+static bool bucket_fits(const cvr_model* m, int64_t Rb, int64_t nb, int64_t idsb, int64_t Pb) {
+  if (Rb > INT32_MAX || nb > INT32_MAX || idsb > INT32_MAX || Pb > INT32_MAX) return false;
+  if (m->spec.model == CVR_MODEL_HYFORMER && (int64_t)m->spec.n_seq * Rb >= (1 << 23)) return false;
+  int64_t bags = 0;
+  for (int f = 0; f < m->spec.n_features; ++f) bags += m->feats[f].side == CVR_SIDE_ITEM ? nb : Rb;
+  return bags < INT32_MAX;
+}
+
+extern "C" cvr_status cvr_graph_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_candidates,
+                                                int64_t max_ids, int64_t max_positions, size_t* bytes) {
+  if (!h || !bytes) return fail(h, CVR_ERR_ARG, "null argument");
+  if (max_requests < 1 || max_candidates < 0 || max_ids < 0 || max_positions < 0) return fail(h, CVR_ERR_ARG, "bad size");
+  int64_t Rb, nb, idsb, Pb;
+  bucket_sizes(h, max_requests, max_candidates, max_ids, max_positions, Rb, nb, idsb, Pb);
+  if (!bucket_fits(h, Rb, nb, idsb, Pb)) return fail(h, CVR_ERR_ARG, "sizes beyond the int32 limits of the batch layout");
+  *bytes = plan_graph(h, Rb, nb, idsb, Pb).total;
+  return CVR_OK;
+}
+
+extern "C" cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures) {
+  if (!h || !graphs_held || !captures) return fail(h, CVR_ERR_ARG, "null argument");
+  *graphs_held = (int64_t)h->graph.entries.size();
+  *captures = h->graph.captures;
+  return CVR_OK;
+}
+
+// Capture one scoring call on the bucket's staging arrays into a graph.
+static cvr_status capture_bucket(cvr_model* h, const GraphPlan& gp, const GraphKey& key, const BucketPadParams& pad,
+                                 hipStream_t s, GraphEntry& out) {
+  char* ws = (char*)key.ws;
+  cvr_batch sb{};
+  sb.n_requests = key.R;
+  sb.n_candidates = key.n;
+  sb.n_ids = key.ids;
+  sb.n_positions = key.P;
+  sb.cand_offsets = (const int32_t*)(ws + gp.co);
+  sb.bag_offsets = (const int32_t*)(ws + gp.bo);
+  sb.ids = (const int32_t*)(ws + gp.ids);
+  if (h->spec.model == CVR_MODEL_HYFORMER) {
+    sb.seq_offsets = (const int32_t*)(ws + gp.so);
+    sb.seq_ids = pad.sid;  // replaced at run time by the header's pointer (capture_seq_ids_ref)
+    h->capture_seq_ids_ref = &((const BucketHeader*)(ws + gp.hdr))->seq_ids;
+  }
+  float* scores = (float*)(ws + gp.scores);
+  const int tasks = h->spec.model == CVR_MODEL_HYFORMER ? h->spec.n_tasks : 1;
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("begin capture: ") + hipGetErrorString(e));
+  Launcher L(h, s, false);
+  e = run_front(h, &sb, ws, gp.plan, L, s, true);
+  if (e == hipSuccess) {
+    if (h->spec.model == CVR_MODEL_DLRM) e = run_dlrm(h, &sb, ws, gp.plan, scores, L, s);
+    else e = run_hyformer(h, &sb, ws, gp.plan, scores, L, s);
+  }
+  if (e == hipSuccess)
+    e = launch_bucket_copy_out((const BucketHeader*)(ws + gp.hdr), scores, (int64_t)key.n * tasks, s);
+  h->capture_seq_ids_ref = nullptr;
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(s, &graph);
+  if (e == hipSuccess) e = ec;
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipGraphInstantiate(&exec[k], graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    for (hipGraphExec_t x : exec)
+      if (x) (void)hipGraphExecDestroy(x);
+    if (graph) (void)hipGraphDestroy(graph);
+    return fail(h, CVR_ERR_HIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+  }
+  out.key = key;
+  out.graph = graph;
+  out.exec[0] = exec[0];
+  out.exec[1] = exec[1];
+  out.last_tok = h->last_tok;
+  out.last_attn_tok = h->last_attn_tok;
+  out.last_hidden_buf = h->last_hidden_buf;
+  out.last_tok_bf16 = h->last_tok_bf16;
+  h->graph.captures++;
+  return CVR_OK;
 }
 
 extern "C" cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* b, void* workspace, size_t ws_bytes,
                                       float* out_scores, void* hip_stream) {
   if (!h) return fail(nullptr, CVR_ERR_ARG, "null handle");
   if (!hip_stream) return fail(h, CVR_ERR_ARG, "graph replay needs a created stream (the null stream cannot be captured)");
-  WsPlan plan;
-  cvr_status st = check_batch(h, b, workspace, ws_bytes, out_scores, plan);
+  cvr_status st = check_batch_args(h, b, workspace, out_scores);
   if (st != CVR_OK) return st;
   if (h->spec.model == CVR_MODEL_DLRM && h->spec.n_hidden == 0) return fail(h, CVR_ERR_UNSUPPORTED, "DLRM without hidden layers");
+  int64_t Rb, nb, idsb, Pb;
+  bucket_sizes(h, b->n_requests, b->n_candidates, b->n_ids, b->n_positions, Rb, nb, idsb, Pb);
+  if (!bucket_fits(h, Rb, nb, idsb, Pb)) return fail(h, CVR_ERR_ARG, "batch bucket beyond the int32 limits of the batch layout");
+  const GraphPlan gp = plan_graph(h, Rb, nb, idsb, Pb);
+  if (ws_bytes < gp.total)
+    return fail(h, CVR_ERR_WORKSPACE, "workspace too small for this batch's bucket: need " + std::to_string(gp.total) +
+                                          " bytes (cvr_graph_workspace_bytes)");
   hipStream_t s = (hipStream_t)hip_stream;
   char* ws = (char*)workspace;
-  GraphCache& g = h->graph;
-  if (!same_key(g, b, workspace, ws_bytes, out_scores, s, h->debug)) {
-    g.reset();
-    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("begin capture: ") + hipGetErrorString(e));
-    Launcher L(h, s, false);
-    e = run_front(h, b, ws, plan, L, s);
-    if (e == hipSuccess && b->n_candidates > 0) {
-      if (h->spec.model == CVR_MODEL_DLRM) e = run_dlrm(h, b, ws, plan, out_scores, L, s);
-      else e = run_hyformer(h, b, ws, plan, out_scores, L, s);
-    }
-    hipGraph_t graph = nullptr;
-    const hipError_t ec = hipStreamEndCapture(s, &graph);
-    if (e == hipSuccess) e = ec;
-    if (e == hipSuccess) e = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
-    g.graph = graph;
-    if (e != hipSuccess) {
-      g.reset();
-      return fail(h, CVR_ERR_HIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    }
-    g.valid = true;
-    g.batch = *b;
-    g.ws = workspace;
-    g.ws_bytes = ws_bytes;
-    g.out = out_scores;
-    g.stream = s;
-    g.debug = h->debug;
-    g.last_tok = h->last_tok;
-    g.last_attn_tok = h->last_attn_tok;
-    g.last_hidden_buf = h->last_hidden_buf;
-    g.last_tok_bf16 = h->last_tok_bf16;
+  GraphKey key;
+  key.R = (int32_t)Rb;
+  key.n = (int32_t)nb;
+  key.ids = idsb;
+  key.P = Pb;
+  key.ws = workspace;
+  key.ws_bytes = ws_bytes;
+  key.stream = s;
+  key.debug = h->debug;
+  // the padding kernel's arguments for this call: the caller's batch into the bucket's staging arrays
+  BucketPadParams p{};
+  p.co = b->cand_offsets;
+  p.bo = b->bag_offsets;
+  p.ids = b->ids;
+  p.so = h->spec.model == CVR_MODEL_HYFORMER ? b->seq_offsets : nullptr;
+  p.sid = h->spec.model == CVR_MODEL_HYFORMER ? b->seq_ids : nullptr;
+  p.R = b->n_requests;
+  p.n = b->n_candidates;
+  p.n_ids = b->n_ids;
+  p.P = h->spec.model == CVR_MODEL_HYFORMER ? b->n_positions : 0;
+  p.S = h->spec.model == CVR_MODEL_HYFORMER ? h->spec.n_seq : 0;
+  p.ncols = h->spec.model == CVR_MODEL_HYFORMER ? h->spec.n_seq_cols : 0;
+  p.Rb = (int32_t)Rb;
+  p.nb = (int32_t)nb;
+  p.ids_b = idsb;
+  p.Pb = Pb;
+  p.nf = h->spec.n_features;
+  p.base[0] = p.base_b[0] = 0;
+  for (int f = 0; f < p.nf; ++f) {
+    const bool item = h->feats[f].side == CVR_SIDE_ITEM;
+    p.base[f + 1] = p.base[f] + (item ? b->n_candidates : b->n_requests);
+    p.base_b[f + 1] = p.base_b[f] + (item ? nb : Rb);
   }
-  const hipError_t e = hipGraphLaunch(g.exec, s);
+  p.total_bags = p.base[p.nf];
+  p.total_bags_b = p.base_b[p.nf];
+  p.co_b = (int32_t*)(ws + gp.co);
+  p.bo_b = (int32_t*)(ws + gp.bo);
+  p.ids_bk = (int32_t*)(ws + gp.ids);
+  p.so_b = (int32_t*)(ws + gp.so);
+  p.hdr = (BucketHeader*)(ws + gp.hdr);
+  p.out = out_scores;
+  p.tasks = h->spec.model == CVR_MODEL_HYFORMER ? h->spec.n_tasks : 1;
+  GraphCache& gc = h->graph;
+  gc.calls++;
+  GraphEntry* g = nullptr;
+  for (GraphEntry& e : gc.entries)
+    if (e.key == key) g = &e;
+  if (!g) {
+    if ((int)gc.entries.size() >= GraphCache::kMaxGraphs) {  // release the least recently used
+      size_t lru = 0;
+      for (size_t i = 1; i < gc.entries.size(); ++i)
+        if (gc.entries[i].used < gc.entries[lru].used) lru = i;
+      for (hipGraphExec_t x : gc.entries[lru].exec)
+        if (x) (void)hipGraphExecDestroy(x);
+      if (gc.entries[lru].graph) (void)hipGraphDestroy(gc.entries[lru].graph);
+      gc.entries.erase(gc.entries.begin() + (long)lru);
+    }
+    GraphEntry fresh;
+    st = capture_bucket(h, gp, key, p, s, fresh);
+    if (st != CVR_OK) return st;
+    gc.entries.push_back(fresh);
+    g = &gc.entries.back();
+  }
+  g->used = gc.calls;
+  // an ordinary launch ahead of the replay (updating a node of the executable graph instead was
+  // measured to hold the host until the device had caught up)
+  hipError_t e = launch_bucket_pad(p, s);
+  if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("bucket padding: ") + hipGetErrorString(e));
+  e = hipGraphLaunch(g->exec[g->next], s);
+  g->next ^= 1;
   if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
+
+  // the handle now describes the replayed call: the bucket's padded batch
   h->last_ws = ws;
-  h->last_plan = plan;
-  h->last_R = b->n_requests;
-  h->last_n = b->n_candidates;
-  h->last_P = b->n_positions;
-  h->last_debug = g.debug;
-  h->last_tok = g.last_tok;
-  h->last_attn_tok = g.last_attn_tok;
-  h->last_hidden_buf = g.last_hidden_buf;
-  h->last_tok_bf16 = g.last_tok_bf16;
+  h->last_plan = gp.plan;
+  h->last_R = Rb;
+  h->last_n = nb;
+  h->last_P = Pb;
+  h->last_debug = g->key.debug;
+  h->last_tok = g->last_tok;
+  h->last_attn_tok = g->last_attn_tok;
+  h->last_hidden_buf = g->last_hidden_buf;
+  h->last_tok_bf16 = g->last_tok_bf16;
   return CVR_OK;
 }
 

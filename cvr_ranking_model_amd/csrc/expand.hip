@@ -37,7 +37,7 @@ __global__ void expand_kernel(ExpandParams p) {
   if (i <= p.total_bags) {
     const int64_t v = p.bag_offsets[i];
     if ((i == 0 && v != 0) || v < 0 || v > p.n_ids) bad |= ERRF_BAG_OFFSETS;
-    if (i == p.total_bags && v != p.n_ids) bad |= ERRF_BAG_OFFSETS;
+    if (i == p.total_bags && (p.ids_capacity ? v > p.n_ids : v != p.n_ids)) bad |= ERRF_BAG_OFFSETS;
     if (i < p.total_bags && (int64_t)p.bag_offsets[i + 1] < v) bad |= ERRF_BAG_OFFSETS;
   }
   if (p.seq_offsets != nullptr && i < (int64_t)p.S * (p.R + 1)) {

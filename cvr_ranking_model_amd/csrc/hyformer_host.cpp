@@ -119,6 +119,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     p.S = S;
     p.n_positions = P;
     p.seq_ids = b->seq_ids;
+    p.seq_ids_ref = m->capture_seq_ids_ref;  // bucket replay: the caller's array, named per call
     p.ncols = sp.n_seq_cols;
     int col = 0;
     for (int c = 0; c < sp.n_seq_cols; ++c) {

@@ -53,9 +53,45 @@ struct ExpandParams {
   int64_t n_positions;
   int32_t* cand_req;            // [n] out
   int32_t* flag;                // status word (cleared by this launch's first block before use)
+  int32_t ids_capacity;         // 1: n_ids is a capacity, the last bag may end before it (bucket replay)
 };
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t st);
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
+
+// ---------------------------------------------------------------- graph replay per batch bucket
+// Written by bucket_pad_kernel before each replay, read by the replayed graph's last kernel.
+struct BucketHeader {
+  int64_t count;           // scores to copy out: n_candidates * n_tasks of the caller's batch
+  float* out;              // the caller's out_scores
+  const int32_t* seq_ids;  // the caller's seq_ids, read in place by the sequence encoder
+};
+struct BucketPadParams {
+  // the caller's batch
+  const int32_t* co;            // cand_offsets [R+1]
+  const int32_t* bo;            // bag_offsets [total_bags+1]
+  const int32_t* ids;           // [n_ids]
+  const int32_t* so;            // seq_offsets [S][R+1] (CVR) or null
+  const int32_t* sid;           // seq_ids [P][ncols] (CVR) or null
+  int32_t R, n;
+  int64_t total_bags, n_ids, P;
+  int32_t S, ncols;
+  // the bucket
+  int32_t Rb, nb;
+  int64_t total_bags_b, ids_b, Pb;
+  int32_t nf;
+  int64_t base[kMaxGatherFeatures + 1];         // first bag of each feature, caller's layout
+  int64_t base_b[kMaxGatherFeatures + 1];       // first bag of each feature, bucket layout
+  // staging arrays of the bucket (workspace)
+  int32_t* co_b;
+  int32_t* bo_b;
+  int32_t* ids_bk;
+  int32_t* so_b;
+  BucketHeader* hdr;
+  float* out;
+  int32_t tasks;
+};
+hipError_t launch_bucket_pad(const BucketPadParams& p, hipStream_t st);
+hipError_t launch_bucket_copy_out(const BucketHeader* hdr, const float* src, int64_t cap, hipStream_t st);
 
 // ---------------------------------------------------------------- HBM hot-row cache
 // Directory of one table's cache, in caller-owned device memory (see cache_layout):
@@ -204,6 +240,7 @@ struct SwigluParams {
   int32_t R, S;
   int64_t n_positions;
   const int32_t* seq_ids;       // [n_positions][ncols]
+  const int32_t* const* seq_ids_ref;  // if set, seq_ids is read from here at run time (bucket replay)
   int32_t ncols;
   int32_t col_off[kMaxSeqCols]; // first column of each sequence column in the 128-wide token
   int32_t col_dim[kMaxSeqCols];

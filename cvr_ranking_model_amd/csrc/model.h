@@ -59,20 +59,44 @@ struct WsPlan {
   size_t total = 0;
 };
 
-// One captured scoring call: replayed while every launch parameter it baked in is unchanged.
-struct GraphCache {
-  bool valid = false;
-  cvr_batch batch{};
+// Graph replay per batch bucket.  A bucket is the batch's four sizes rounded up (bucket_sizes);
+// one graph per (bucket, workspace, stream, debug setting) scores the bucket's staging arrays.
+struct GraphKey {
+  int32_t R = 0, n = 0;
+  int64_t ids = 0, P = 0;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  float* out = nullptr;
   hipStream_t stream = nullptr;
   int debug = 0;
+  bool operator==(const GraphKey& o) const {
+    return R == o.R && n == o.n && ids == o.ids && P == o.P && ws == o.ws && ws_bytes == o.ws_bytes &&
+           stream == o.stream && debug == o.debug;
+  }
+};
+struct GraphEntry {
+  GraphKey key;
+  hipGraph_t graph = nullptr;
+  // two instances of the graph, launched in turn: a replay then never waits for the previous
+  // replay of the same instance
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  int next = 0;
+  uint64_t used = 0;  // call counter of the last use (least recently used goes first)
   // buffer choices the captured launches made, restored on every replay for cvr_debug_export
   int last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0, last_tok_bf16 = 0;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-  void reset();
+};
+struct GraphCache {
+  static constexpr int kMaxGraphs = 8;
+  std::vector<GraphEntry> entries;
+  uint64_t calls = 0;
+  int64_t captures = 0;
+  void reset();  // releases every graph
+};
+
+// Workspace of a graph-replayed call: the scoring plan at the bucket's sizes, then the bucket's
+// staging arrays, score buffer and header.
+struct GraphPlan {
+  WsPlan plan;
+  size_t co = 0, bo = 0, ids = 0, so = 0, scores = 0, hdr = 0, total = 0;
 };
 
 struct Timing {
@@ -118,6 +142,8 @@ struct cvr_model {
   int64_t last_R = 0, last_n = 0, last_P = 0;
   int last_debug = 0, last_tok = 0, last_attn_tok = 0, last_hidden_buf = 0;
   int last_tok_bf16 = 0;  // the last layer's token matrix was written as bf16 (debug off)
+  // while a bucket graph is captured: where its sequence encoder finds the caller's seq_ids
+  const int32_t* const* capture_seq_ids_ref = nullptr;
   cvr::Timing timing;
   cvr::GraphCache graph;
   // HBM hot-row caches attached to host-resident tables (cvr_cache_attach)
@@ -133,6 +159,11 @@ struct cvr_model {
 
 namespace cvr {
 WsPlan plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P);
+// The bucket of a batch: each size rounded up to the next m * 2^k with 8 <= m <= 16 (sizes
+// below 16 exact), one spare request and one spare candidate included.
+void bucket_sizes(const cvr_model* m, int64_t R, int64_t n, int64_t ids, int64_t P, int64_t& Rb, int64_t& nb,
+                  int64_t& idsb, int64_t& Pb);
+GraphPlan plan_graph(const cvr_model* m, int64_t Rb, int64_t nb, int64_t idsb, int64_t Pb);
 // Records msg as the handle's (and the thread's) last error and returns s.
 cvr_status fail(cvr_model* m, cvr_status s, const std::string& msg);
 // cvr_score's work: checks, then the launches into the given workspace.

@@ -278,6 +278,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
 
   // ---------------------------------------------------------------- consumers
   const int bt = tid - 256;  // 0..255
+  const int32_t* seq_ids = p.seq_ids_ref ? *p.seq_ids_ref : p.seq_ids;
   // Granule i of a consumer thread covers position (bt + 256 i) / 32 and columns
   // 4 * (bt % 32) .. +3, which sit in one sequence column (table, rows and width fixed).
   const float* gtab;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   bool bad = false;
   auto load_ids = [&](int2 d, int32_t (&id)[4]) {
     const int np = d.y & 255;
-    const int32_t* chunk_ids = p.seq_ids + (int64_t)d.x * p.ncols;  // the same for every lane
+    const int32_t* chunk_ids = seq_ids + (int64_t)d.x * p.ncols;  // the same for every lane
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pos = gpos0 + 8 * i;

@@ -65,6 +65,9 @@ _PROTOS = {
     "cvr_score": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "cvr_score_graph": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "cvr_score_noalloc": (C.c_int, [C.c_void_p, C.POINTER(cvr_batch), C.c_void_p, C.c_void_p]),
+    "cvr_graph_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int64, C.c_int64,
+                                            C.POINTER(C.c_size_t)]),
+    "cvr_graph_info": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
     "cvr_sync_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "cvr_set_debug": (C.c_int, [C.c_void_p, C.c_int32]),
     "cvr_set_option": (C.c_int, [C.c_void_p, C.c_int32, C.c_int64]),
@@ -138,6 +141,18 @@ def cvr_score(h, batch_c, ws_ptr, ws_bytes, out_ptr, stream):
 
 def cvr_score_graph(h, batch_c, ws_ptr, ws_bytes, out_ptr, stream):
     _check(lib().cvr_score_graph(h, C.byref(batch_c), ws_ptr, ws_bytes, out_ptr, stream), h)
+
+
+def cvr_graph_workspace_bytes(h, max_requests, max_candidates, max_ids, max_positions):
+    out = C.c_size_t(0)
+    _check(lib().cvr_graph_workspace_bytes(h, max_requests, max_candidates, max_ids, max_positions, C.byref(out)), h)
+    return out.value
+
+
+def cvr_graph_info(h):
+    held, caps = C.c_int64(0), C.c_int64(0)
+    _check(lib().cvr_graph_info(h, C.byref(held), C.byref(caps)), h)
+    return held.value, caps.value
 
 
 def cvr_score_noalloc(h, batch_c, out_ptr, stream):
@@ -411,11 +426,24 @@ class Model:
         cvr_score_noalloc(self.h, dbatch.c, C.c_void_p(out.data_ptr()), _stream_ptr(self.stream))
         return out
 
-    def score_graph(self, dbatch: DeviceBatch, out=None):
-        """cvr_score_graph on the model's stream (or a private one ordered after the current
-        stream: graph capture needs a created stream)."""
+    def graph_workspace(self, R, n, n_ids, P):
         torch = _torch()
-        ws = self.workspace(dbatch.n_requests, dbatch.n_candidates, dbatch.n_ids, dbatch.n_positions)
+        need = cvr_graph_workspace_bytes(self.h, R, n, n_ids, P)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    def graph_info(self):
+        """(graphs held, graphs captured since creation)."""
+        return cvr_graph_info(self.h)
+
+    def score_graph(self, dbatch: DeviceBatch, out=None, ws_sizes=None):
+        """cvr_score_graph on the model's stream (or a private one ordered after the current
+        stream: graph capture needs a created stream).  ws_sizes: (R, n, ids, P) to size the
+        workspace for (default: this batch's own)."""
+        torch = _torch()
+        sizes = ws_sizes or (dbatch.n_requests, dbatch.n_candidates, dbatch.n_ids, dbatch.n_positions)
+        ws = self.graph_workspace(*sizes)
         if out is None:
             out = torch.empty(max(1, dbatch.n_candidates * self.n_tasks), dtype=torch.float32, device=self.device)
         s = self.stream

@@ -216,20 +216,44 @@ cvr_status cvr_score(cvr_handle h, const cvr_batch* batch, void* workspace, size
 #define CVR_NOALLOC_SCRATCH_BYTES (64u << 20)
 cvr_status cvr_score_noalloc(cvr_handle h, const cvr_batch* batch, float* out_scores, void* hip_stream);
 
-/* cvr_score through graph replay (CVR article section 3.4.4: the serving
- * path captures the scoring launches once per batch shape and replays them).
- * Same arguments and result as cvr_score.  The first call for a given key --
- * the batch's four sizes and five array pointers, workspace, ws_bytes,
- * out_scores, hip_stream and the debug setting -- captures the call's kernel
- * launches on hip_stream into a HIP graph and launches it; later calls with
- * the same key replay that graph, which reads the batch arrays' contents at
- * replay time.  A call with a different key replaces the graph.  hip_stream
- * must be a created stream (CVR_ERR_ARG for the null stream); cvr_timing does
- * not record graph launches.  Host-side checks run on every call; device-side
- * checks are reported by cvr_sync_status as for cvr_score.  The graph is
- * released by cvr_destroy. */
+/* cvr_score through graph replay per batch bucket (CVR article section 3.4.4:
+ * the serving path captures the scoring launches once per batch size bucket
+ * and replays them, reusing the same buffers).  Same arguments and result as
+ * cvr_score.  The batch's bucket is its four sizes rounded up -- requests + 1
+ * and candidates + 1 (one spare of each), ids and positions as they are -- each
+ * to the next m * 2^k with 8 <= m <= 16 (sizes below 16 stay exact), so a
+ * bucket holds at most 12.5% more than the batch in each size plus the spares.
+ * The first call for a bucket (with this workspace, ws_bytes, stream and debug
+ * setting) captures one scoring call at the bucket's sizes into a HIP graph;
+ * later calls in the bucket replay it without capturing.  Every call first
+ * launches one kernel that copies the batch into the bucket's staging arrays
+ * in the workspace and pads it with requests, candidates, bags and positions
+ * that belong to no caller request (their scores are computed and dropped:
+ * the padding costs up to the bucket's extra size in work); the graph ends by
+ * copying the caller's scores to out_scores.  Scores equal cvr_score's on the
+ * same batch when the bucket's sizes select the same kernels (the kernel
+ * choices depend on sizes: CVR_OPT_TOK_SHARE and CVR_OPT_ATTN_MQ fix two of
+ * them), else up to the order of fp32 additions.  At most 8 graphs are held
+ * per model (least recently used released first); cvr_set_option and
+ * cvr_cache_attach release them all.  workspace: at least
+ * cvr_graph_workspace_bytes for the batch's sizes (more than cvr_score
+ * needs).  hip_stream must be a created stream (CVR_ERR_ARG for the null
+ * stream); cvr_timing does not record graph launches.  Host-side checks run on
+ * every call; device-side checks are reported by cvr_sync_status as for
+ * cvr_score, malformed offsets included (the padding keeps them malformed).
+ * After a replay, cvr_debug_export describes the padded batch: per-request
+ * and per-candidate rows of the caller's batch first, padding after them.
+ * Graphs are released by cvr_destroy. */
 cvr_status cvr_score_graph(cvr_handle h, const cvr_batch* batch, void* workspace, size_t ws_bytes,
                            float* out_scores, void* hip_stream);
+
+/* Device bytes of workspace cvr_score_graph needs for batches up to the given
+ * sizes (those of their bucket; max_positions is ignored for DLRM). */
+cvr_status cvr_graph_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t max_candidates, int64_t max_ids,
+                                     int64_t max_positions, size_t* bytes);
+
+/* Graphs held by the model and graphs captured since cvr_create (host values). */
+cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures);
 
 /* Kernel-selection options of a model.  Each has a default that scoring uses unless the option
  * is set; scores do not depend on them beyond the order of fp32 additions (DLRM_PASS_ROWS: not
