@@ -314,6 +314,12 @@ def weight_shapes(spec: dict) -> dict:
     T = N + S
     H = spec["mixer_heads"]
     mh = spec["mixer_hidden"]
+    if spec.get("epnet_hidden"):
+        d_dom = sum(spec["tables"][f["table"]]["dim"] for f in spec["features"] if f["side"] == "context")
+        shapes["epnet.fc1.weight"] = (spec["epnet_hidden"], d_dom + e_dim)
+        shapes["epnet.fc1.bias"] = (spec["epnet_hidden"],)
+        shapes["epnet.fc2.weight"] = (e_dim, spec["epnet_hidden"])
+        shapes["epnet.fc2.bias"] = (e_dim,)
     shapes["tok.weight"] = (N * d, e_dim)
     shapes["tok.bias"] = (N * d,)
     for s in range(S):

@@ -57,6 +57,38 @@ def softmax(x, axis=-1):
     return e / np.sum(e, axis=axis, keepdims=True)
 
 
+def domain_columns(spec):
+    """Columns of the model input that hold the scenario (domain) features: the context-side
+    features, in spec order."""
+    cols, c = [], 0
+    for f in spec["features"]:
+        dim = spec["tables"][f["table"]]["dim"]
+        if f["side"] == "context":
+            cols.extend(range(c, c + dim))
+        c += dim
+    return np.array(cols, dtype=np.int64)
+
+
+def epnet(spec, weights, e, rnd, mm=matmul64):
+    """Optional step before B2: EPNet, the scenario-aware non-sequence embedding.
+
+    The CVR article (section 3.2.1) obtains the non-sequence embedding through EPNet, which
+    models several scenarios, but prints no formula.  Reading: EPNet as PEPNet defines it
+    (Chang et al., KDD 2023): a gate unit turns the scenario features' embedding, concatenated
+    with the general embedding, into a per-element scale delta = gamma * sigmoid(W2 ReLU(W1
+    [e_domain, e] + b1) + b2) with gamma = 2, and the general embedding is multiplied by it
+    element by element.  The scenario features are the spec's context-side features; the gate's
+    hidden width is the spec's ``epnet_hidden``.  Both gate Linears take low-precision inputs,
+    and the scaled embedding, the tokenizer's input, is rounded again.  ``e`` is [c, D].
+    """
+    x = rnd(np.concatenate([e[:, domain_columns(spec)], e], axis=1))
+    h = rnd(np.maximum(mm(x, _w(weights, "epnet.fc1.weight", rnd).T) + _b(weights, "epnet.fc1.bias"), 0.0))
+    g = mm(h, _w(weights, "epnet.fc2.weight", rnd).T) + _b(weights, "epnet.fc2.bias")
+    with np.errstate(over="ignore"):             # exp(-g) = inf for g << 0 gives delta = 0
+        delta = 2.0 / (1.0 + np.exp(-g))
+    return rnd(delta * e)
+
+
 def tokenize(spec, weights, e, rnd, mm=matmul64):
     """Step B2: non-sequence tokens.
 
@@ -240,8 +272,9 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
     of fp64 (see :func:`matmul32`); the default is fp64.
 
     Returns ``scores`` fp32 [c, tasks], ``logits`` fp64 [c, tasks], ``cand``;
-    with ``trace`` also the intermediates (``e``, ``X0``, ``H``, ``p``,
-    ``q``, ``o``, ``Z``, ``attn``).
+    with ``trace`` also the intermediates (``e_in`` the pooled inputs, ``e`` the tokenizer's
+    input (``e_in`` scaled by EPNet when the spec has it), ``X0``, ``H``, ``p``, ``q``, ``o``,
+    ``Z``, ``attn``).
     """
     if spec["model"] != "hyformer":
         raise OracleInputError("not a CVR spec")
@@ -259,7 +292,8 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
     tau = float(spec["tau"])
 
     # B1-B2: non-sequence input and tokens, per candidate.
-    e, pooled = candidate_inputs(spec, tables, ex, cands, rnd)
+    e_in, pooled = candidate_inputs(spec, tables, ex, cands, rnd)
+    e = epnet(spec, weights, e_in, rnd, mm) if spec.get("epnet_hidden") else e_in
     X = tokenize(spec, weights, e, rnd, mm)
 
     # B3-B5: per request and sequence.
@@ -273,7 +307,7 @@ def hyformer_forward(spec, tables, weights, batch, requests=None, exact=False, t
             Hs[(s, r)] = Hall[off[i]:off[i + 1]]
             ps[(s, r)] = mean_pool(Hs[(s, r)])
 
-    tr = {"e": e, "X0": X.copy(), "H": Hs, "p": ps, "q": [], "o": [], "Z": [], "attn": [], "pooled": pooled}
+    tr = {"e_in": e_in, "e": e, "X0": X.copy(), "H": Hs, "p": ps, "q": [], "o": [], "Z": [], "attn": [], "pooled": pooled}
     nc = cands.size
     Z = None
     for l in range(spec["n_layers"]):

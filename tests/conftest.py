@@ -35,7 +35,7 @@ def tiny_dlrm_spec(dims=(4, 4, 2, 2), sides=("user", "user", "item", "item"), hi
 
 def tiny_cvr_spec(d=16, n_tokens=13, heads=16, layers=1, lens=(3, 5, 4), rows=16, e_dims=(8, 8, 8, 8),
                   sides=("user", "item", "item", "context"), seq_dims=(8, 4, 2, 2), hidden=8, mixer_hidden=8,
-                  experts=3, expert_dim=8, tasks=2, head_hidden=4, lowp="bf16", tau=None):
+                  experts=3, expert_dim=8, tasks=2, head_hidden=4, lowp="bf16", tau=None, epnet_hidden=0):
     assert sum(seq_dims) == d
     nf = len(e_dims)
     tables = [{"name": f"ns{i}", "rows": rows, "dim": e} for i, e in enumerate(e_dims)]
@@ -48,7 +48,7 @@ def tiny_cvr_spec(d=16, n_tokens=13, heads=16, layers=1, lens=(3, 5, 4), rows=16
             "d": d, "n_tokens": n_tokens, "n_layers": layers, "swiglu_hidden": hidden,
             "tau": float(tau if tau is not None else 2.0 * math.sqrt(d)), "mixer_heads": heads,
             "mixer_hidden": mixer_hidden, "n_experts": experts, "expert_dim": expert_dim, "n_tasks": tasks,
-            "head_hidden": head_hidden,
+            "head_hidden": head_hidden, "epnet_hidden": epnet_hidden,
             "workload": {"requests": 3, "candidates": 2, "seed": 11, "zipf_a": 1.05, "cold_frac": 0.0}}
 
 

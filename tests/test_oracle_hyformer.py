@@ -322,6 +322,16 @@ def _brute_force(spec, tables, w, b, rb=None):
                 v = float(acc / np.float32(hi - lo)) if hi > lo else 0.0
                 e.append(min(max(v, -10.0), 10.0))
         e = rnd(e)
+        if spec.get("epnet_hidden"):
+            dom, col = [], 0
+            for f in spec["features"]:
+                dim = spec["tables"][f["table"]]["dim"]
+                if f["side"] == "context":
+                    dom += e[col:col + dim]
+                col += dim
+            hh = rnd(relu(lin(w["epnet.fc1.weight"], rnd(dom + e), w["epnet.fc1.bias"])))
+            gg = lin(w["epnet.fc2.weight"], hh, w["epnet.fc2.bias"])
+            e = rnd([2.0 / (1.0 + math.exp(-g_)) * v for g_, v in zip(gg, e)])
         y = lin(w["tok.weight"], e, w["tok.bias"])
         X = [[y[i * d + j] for j in range(d)] for i in range(N)]
         Hs, ps = [], []
@@ -396,6 +406,38 @@ def test_whole_model_brute_force_bf16_plan(layers, task_experts):
     assert np.allclose(got, want, rtol=1e-11, atol=1e-11)
     # and the rounding is visible: the plan differs from exact arithmetic
     assert not np.allclose(got, _brute_force(spec, tables, w, b), rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("layers", [1, 2])
+def test_epnet_brute_force(layers):
+    """EPNet (PEPNet's gate unit on the scenario features, CVR article section 3.2.1 reading):
+    the oracle against the scalar brute force, exact and in the bf16 plan."""
+    spec, tables, w, b = _tiny_model(layers=layers, C=2, lens=[[3, 0, 2], [1, 4, 2], [2, 2, 1]], epnet_hidden=6)
+    assert spec["features"][3]["side"] == "context" and w["epnet.fc1.weight"].shape == (6, 8 + 32)
+    got = oracle.score(spec, tables, w, b, exact=True)["logits"]
+    assert np.allclose(got, _brute_force(spec, tables, w, b), rtol=1e-11, atol=1e-11)
+    got = oracle.score(spec, tables, w, b)["logits"]
+    assert np.allclose(got, _brute_force(spec, tables, w, b, rb=scalar_bf16), rtol=1e-11, atol=1e-11)
+
+
+def test_epnet_gate_limits():
+    """delta = 2 sigmoid(.): a zero second layer gives delta = 1 (the model without EPNet, bit for
+    bit); a very negative bias closes the gate (tokens = tokenizer bias); a very positive one
+    doubles the embedding (exact in bf16)."""
+    spec, tables, w, b = _tiny_model(C=2, epnet_hidden=6)
+    plain_spec = dict(spec, epnet_hidden=0)
+    plain_w = {k: v for k, v in w.items() if not k.startswith("epnet.")}
+    ref = oracle.score(plain_spec, tables, plain_w, b, trace=True)
+    w1 = dict(w, **{"epnet.fc2.weight": np.zeros_like(w["epnet.fc2.weight"]),
+                    "epnet.fc2.bias": np.zeros_like(w["epnet.fc2.bias"])})
+    assert np.array_equal(oracle.score(spec, tables, w1, b)["scores"], ref["scores"])
+    w0 = dict(w1, **{"epnet.fc2.bias": np.full_like(w["epnet.fc2.bias"], -1e4)})
+    out = oracle.score(spec, tables, w0, b, trace=True)["trace"]
+    assert np.array_equal(out["e"], np.zeros_like(out["e"]))
+    assert np.array_equal(out["X0"], np.broadcast_to(w["tok.bias"].astype(np.float64).reshape(13, -1), out["X0"].shape))
+    w2 = dict(w1, **{"epnet.fc2.bias": np.full_like(w["epnet.fc2.bias"], 1e4)})
+    out = oracle.score(spec, tables, w2, b, trace=True)["trace"]
+    assert np.array_equal(out["e"], 2.0 * ref["trace"]["e"]) and np.array_equal(out["e_in"], ref["trace"]["e"])
 
 
 def test_scalar_bf16_by_hand():
