@@ -81,6 +81,8 @@ def stage_work(spec, batch):
     d = spec["d"]
     per_pos = sum(lin(f"seq.0.{x}.weight") for x in ["gate", "up", "down"])
     work["tokenize_gemm"] = ("flop", n * lin("tok.weight"))
+    if spec.get("epnet_hidden"):
+        work["epnet"] = ("flop", n * (lin("epnet.fc1.weight") + lin("epnet.fc2.weight")))
     work["swiglu"] = ("flop", P * per_pos)
     work["swiglu_bytes"] = ("byte", P * (sum(spec["tables"][c["table"]]["dim"] for c in spec["seq"]["columns"]) * 4
                                          + 4 * len(spec["seq"]["columns"]) + d * 2))
@@ -178,6 +180,8 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     spec = synth.load_spec(workload)
     if args.ple_task_experts:
         spec["ple_task_experts"] = [[int(e) for e in t.split(",")] for t in args.ple_task_experts.split("/")]
+    if args.epnet and spec["model"] == "hyformer":
+        spec["epnet_hidden"] = args.epnet
     print(f"[bench] workload {workload}: filling tables", file=sys.stderr, flush=True)
     tables = cv.device_tables(spec, args.variant)
     cached = []
@@ -367,6 +371,7 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
         "config": dict({"workload": WORKLOAD_TEXT[workload], "candidates_per_step": n,
                         "requests_per_step": db.n_requests},
                        **({"ple_task_experts": spec["ple_task_experts"]} if args.ple_task_experts else {}),
+                       **({"epnet_hidden": spec["epnet_hidden"]} if spec.get("epnet_hidden") else {}),
                        **({"hot_row_cache": cache_cfg, "distinct_batches": nb} if cached else {})),
         "roofline": roof,
         "stages": table,
@@ -429,6 +434,9 @@ def main():
     ap.add_argument("--ple-task-experts", default=None,
                     help="CVR: experts each task's gate mixes, tasks separated by '/', e.g. 0,2/1,2 "
                          "(PLE with one task-specific expert per task and a shared one)")
+    ap.add_argument("--epnet", type=int, default=0,
+                    help="CVR: EPNet gate hidden width (0: off), scaling the non-sequence embedding by the "
+                         "context-side scenario features (CVR article section 3.2.1)")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",

@@ -86,6 +86,13 @@ static cvr_status check_spec(const cvr_spec* s, const cvr_table* tables, int32_t
       }
     }
     if (!(s->tau > 0.f) || !std::isfinite(s->tau)) { why = "tau must be positive"; return CVR_ERR_SPEC; }
+    if (s->epnet_hidden < 0) { why = "epnet_hidden must be 0 (off) or positive"; return CVR_ERR_SPEC; }
+    if (s->epnet_hidden > 0) {
+      if (s->epnet_hidden % 32) { why = "epnet_hidden must be a multiple of 32"; return CVR_ERR_UNSUPPORTED; }
+      bool ctx = false;
+      for (int f = 0; f < s->n_features; ++f) ctx |= s->features[f].side == CVR_SIDE_CONTEXT;
+      if (!ctx) { why = "EPNet needs at least one context-side (scenario) feature"; return CVR_ERR_SPEC; }
+    }
   }
   return CVR_OK;
 }
@@ -115,7 +122,26 @@ static void derive(cvr_model* m) {
     else m->segs.push_back({item, k + dim, m->fcol[f]});
     k += dim;
   }
-  m->tok_split = s.model == CVR_MODEL_HYFORMER && m->D_req > 0 && m->D_item > 0;
+  // EPNet's scenario columns: runs of consecutive context-side features in the request-side matrix
+  m->dom_segs.clear();
+  m->D_dom = 0;
+  if (s.model == CVR_MODEL_HYFORMER && s.epnet_hidden > 0) {
+    int run_k0 = 0;  // first gate-input column of the current run
+    for (int f = 0; f < s.n_features; ++f) {
+      if (m->feats[f].side != CVR_SIDE_CONTEXT) continue;
+      const int dim = m->tables[m->feats[f].table].dim;
+      const bool extends = !m->dom_segs.empty() && m->dom_segs.back().col0 + (m->D_dom - run_k0) == m->fcol[f];
+      if (extends) {
+        m->dom_segs.back().k_end += dim;
+      } else {
+        run_k0 = m->D_dom;
+        m->dom_segs.push_back({false, m->D_dom + dim, m->fcol[f]});
+      }
+      m->D_dom += dim;
+    }
+  }
+  // the tokenizer's request-side block once per request: not with EPNet, whose scale is per candidate
+  m->tok_split = s.model == CVR_MODEL_HYFORMER && m->D_req > 0 && m->D_item > 0 && s.epnet_hidden == 0;
   int kb = 0;
   for (const InputSeg& sg : m->segs) {
     if ((sg.k_end - kb) % 32) m->tok_split = false;
@@ -147,6 +173,12 @@ static void plan_weights(cvr_model* m) {
   } else {
     const int d = s.d, N = s.n_tokens, S = s.n_seq, T = N + S, hs = s.swiglu_hidden;
     const int mw = T * d / s.mixer_heads;
+    if (s.epnet_hidden > 0) {
+      add("epnet.fc1.weight", s.epnet_hidden, (int64_t)m->D_dom + m->e_dim, true);
+      add("epnet.fc1.bias", s.epnet_hidden, 1, false);
+      add("epnet.fc2.weight", m->e_dim, s.epnet_hidden, true);
+      add("epnet.fc2.bias", m->e_dim, 1, false);
+    }
     add("tok.weight", (int64_t)N * d, m->e_dim, true);
     add("tok.bias", (int64_t)N * d, 1, false);
     if (m->tok_split) {
@@ -225,6 +257,12 @@ static cvr_status check_segments(const cvr_model* m, std::string& why) {
   for (const auto& sg : m->segs)
     if (sg.k_end % 32 || sg.col0 % 8) { why = "each run of same-side features must end on a multiple of 32 columns"; return CVR_ERR_UNSUPPORTED; }
   if (m->e_dim % 32) { why = "model input width must be a multiple of 32"; return CVR_ERR_UNSUPPORTED; }
+  if (!m->dom_segs.empty()) {
+    if (m->dom_segs.size() + m->segs.size() > (size_t)kMaxASegments)
+      { why = "EPNet: scenario runs plus input runs exceed 4 segments"; return CVR_ERR_UNSUPPORTED; }
+    for (const auto& sg : m->dom_segs)
+      if (sg.k_end % 32 || sg.col0 % 8) { why = "EPNet: each run of scenario features must be a multiple of 32 wide"; return CVR_ERR_UNSUPPORTED; }
+  }
   return CVR_OK;
 }
 
@@ -397,6 +435,11 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     w.gates = take((size_t)n * s.n_tasks * s.n_experts * 4);
     w.task_in = take((size_t)s.n_tasks * n * s.expert_dim * lp);
     w.head_hid = take((size_t)s.n_tasks * n * s.head_hidden * lp);
+    if (s.epnet_hidden > 0) {
+      w.ep_h = take((size_t)n * s.epnet_hidden * lp);
+      w.ep_g = take((size_t)n * m->e_dim * 4);
+      w.x_ep = take((size_t)n * m->e_dim * lp);
+    }
   }
   w.total = align256(off);
   return w;
@@ -472,7 +515,8 @@ extern "C" cvr_status cvr_timing_end(cvr_handle h, double* stage_ms, int32_t* st
 extern "C" const char* cvr_stage_name(cvr_handle, int32_t stage) {
   static const char* names[kNumStages] = {"expand", "gather_pool", "mlp_gemm", "dlrm_output", "tokenize_gemm",
                                           "swiglu", "seq_pool", "query_gemm", "attention", "mixer_gemm",
-                                          "ple_gemm", "ple_gate", "head_gemm", "head_out", "cache", "seq_chunks"};
+                                          "ple_gemm", "ple_gate", "head_gemm", "head_out", "cache", "seq_chunks",
+                                          "epnet"};
   return (stage >= 0 && stage < kNumStages) ? names[stage] : "";
 }
 
@@ -1016,6 +1060,9 @@ extern "C" cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, si
         return fail(h, CVR_ERR_ARG, "hidden activations need cvr_set_debug(1) before scoring (otherwise the last "
                                     "hidden layer may be fused into the output layer)");
       off = w.h[h->last_hidden_buf]; bytes = n * h->hidden[sp.n_hidden - 1] * 2; break;
+    case CVR_DBG_EPNET:
+      if (!cvr || sp.epnet_hidden == 0) return fail(h, CVR_ERR_ARG, "CVR model with EPNet only");
+      off = w.x_ep; bytes = n * h->e_dim * 2; break;
     default: return fail(h, CVR_ERR_ARG, "unknown export");
   }
   if (dst_bytes < bytes) return fail(h, CVR_ERR_ARG, "destination too small: need " + std::to_string(bytes));

@@ -47,6 +47,66 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   int32_t* flag = (int32_t*)(ws + w.flag);
   hipError_t e;
 
+  // ---- EPNet (optional): e' = e * 2 sigmoid(W2 ReLU(W1 [e_domain, e] + b1) + b2), written as the
+  // tokenizer's bf16 input.  Gate input: the scenario columns, then every input run, all read in
+  // place (request-side runs through the candidate -> request map).
+  const bool ep = sp.epnet_hidden > 0;
+  if (ep) {
+    GemmParams g{};
+    g.M = n;
+    g.N = sp.epnet_hidden;
+    g.K = m->D_dom + m->e_dim;
+    g.groups = 1;
+    for (const InputSeg& sg : m->dom_segs)
+      g.seg[g.nseg++] = ASeg{ws + w.x_req, cand_req, (int64_t)m->ld_req, 0, sg.k_end, 8, sg.col0, 0};
+    for (const InputSeg& sg : m->segs)
+      g.seg[g.nseg++] = ASeg{ws + (sg.item ? w.x_item : w.x_req), sg.item ? nullptr : cand_req,
+                             (int64_t)(sg.item ? m->ld_item : m->ld_req), 0, m->D_dom + sg.k_end, 8, sg.col0, 0};
+    g.W = m->wptr("epnet.fc1.weight");
+    g.bias = (const float*)m->wptr("epnet.fc1.bias");
+    g.C = ws + w.ep_h;
+    g.ldc = sp.epnet_hidden;
+    g.c_nstride8 = 8;
+    g.relu = 1;
+    e = L(STAGE_EPNET, [&] { return launch_gemm(g, lowp, s); });
+    if (e != hipSuccess) return e;
+    GemmParams g2{};
+    g2.M = n;
+    g2.N = m->e_dim;
+    g2.K = sp.epnet_hidden;
+    g2.groups = 1;
+    g2.nseg = 1;
+    g2.seg[0] = ASeg{ws + w.ep_h, nullptr, (int64_t)sp.epnet_hidden, 0, sp.epnet_hidden, 8, 0, 0};
+    g2.W = m->wptr("epnet.fc2.weight");
+    g2.bias = (const float*)m->wptr("epnet.fc2.bias");
+    g2.C = ws + w.ep_g;
+    g2.ldc = m->e_dim;
+    g2.c_nstride8 = 8;
+    g2.out_f32 = 1;
+    e = L(STAGE_EPNET, [&] { return launch_gemm(g2, lowp, s); });
+    if (e != hipSuccess) return e;
+    EpnetParams ap{};
+    ap.n = n;
+    ap.D = m->e_dim;
+    ap.g = (const float*)(ws + w.ep_g);
+    ap.x_req = (const __bf16*)(ws + w.x_req);
+    ap.x_item = (const __bf16*)(ws + w.x_item);
+    ap.ld_req = m->ld_req;
+    ap.ld_item = m->ld_item;
+    ap.cand_req = cand_req;
+    int kb = 0;
+    for (const InputSeg& sg : m->segs) {
+      ap.run_k0[ap.nruns] = kb;
+      ap.run_col0[ap.nruns] = sg.col0;
+      ap.run_item[ap.nruns] = sg.item ? 1 : 0;
+      ap.nruns++;
+      kb = sg.k_end;
+    }
+    ap.out = (__bf16*)(ws + w.x_ep);
+    e = L(STAGE_EPNET, [&] { return launch_epnet_apply(ap, s); });
+    if (e != hipSuccess) return e;
+  }
+
   // ---- B2: tokenization, X = E W_tok^T + b into token rows 0..N-1.  When requests carry several
   // candidates, the request-side columns are multiplied once per request (U = E_req W_req^T)
   // and every candidate adds its request's row of U to its item-side product.
@@ -57,11 +117,16 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     g.N = N * d;
     g.K = m->e_dim;
     g.groups = 1;
-    g.nseg = (int)m->segs.size();
-    for (size_t i = 0; i < m->segs.size(); ++i) {
-      const InputSeg& sg = m->segs[i];
-      g.seg[i] = ASeg{ws + (sg.item ? w.x_item : w.x_req), sg.item ? nullptr : cand_req,
-                      (int64_t)(sg.item ? m->ld_item : m->ld_req), 0, sg.k_end, 8, sg.col0, 0};
+    if (ep) {
+      g.nseg = 1;
+      g.seg[0] = ASeg{ws + w.x_ep, nullptr, (int64_t)m->e_dim, 0, m->e_dim, 8, 0, 0};
+    } else {
+      g.nseg = (int)m->segs.size();
+      for (size_t i = 0; i < m->segs.size(); ++i) {
+        const InputSeg& sg = m->segs[i];
+        g.seg[i] = ASeg{ws + (sg.item ? w.x_item : w.x_req), sg.item ? nullptr : cand_req,
+                        (int64_t)(sg.item ? m->ld_item : m->ld_req), 0, sg.k_end, 8, sg.col0, 0};
+      }
     }
     g.W = m->wptr("tok.weight");
     g.bias = (const float*)m->wptr("tok.bias");

@@ -308,6 +308,24 @@ hipError_t launch_token_mix(const TokenMixParams& p, hipStream_t st);
 // MFMA operands: every 16-byte piece a lane loads sits next to its neighbours' pieces.
 hipError_t launch_mix_pack(const float* src, void* dst, int which, hipStream_t st);
 
+// ---------------------------------------------------------------- EPNet (before B2)
+// e' = bf16(2 sigmoid(g) * e) over the D model-input columns of n candidates; e is read in place
+// from the request-side matrix (through cand_req) or the item-side matrix, run by run.
+struct EpnetParams {
+  int32_t n, D;
+  const float* g;               // [n][D] gate pre-activations
+  const __bf16* x_req;
+  const __bf16* x_item;
+  int64_t ld_req, ld_item;
+  const int32_t* cand_req;
+  int32_t nruns;
+  int32_t run_k0[kMaxASegments];    // first model-input column of each run of same-side features
+  int32_t run_col0[kMaxASegments];  // its first column in its side's matrix
+  int32_t run_item[kMaxASegments];  // 1: item-side run
+  __bf16* out;                  // [n][D]
+};
+hipError_t launch_epnet_apply(const EpnetParams& p, hipStream_t st);
+
 // ---------------------------------------------------------------- PLE gates and heads (B10-B11)
 struct PleGateParams {
   // Row c of the expert GEMM output (row stride ld): the E expert outputs [E][edim] (after

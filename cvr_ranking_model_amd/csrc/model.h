@@ -27,6 +27,7 @@ enum Stage {
   STAGE_HEAD_OUT,
   STAGE_CACHE,
   STAGE_SEQ_CHUNKS,
+  STAGE_EPNET,
   kNumStages
 };
 constexpr int kMaxLaunchesPerCall = 64;
@@ -56,6 +57,7 @@ struct WsPlan {
   size_t opart = 0;  // DLRM: output-layer partials of a fused last hidden layer
   size_t tok[2] = {0, 0}, hseq = 0, chunk_off = 0, chunk_desc = 0, pool_part = 0, seq_pool = 0, query = 0,
          mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0, tok_req = 0;
+  size_t ep_h = 0, ep_g = 0, x_ep = 0;  // CVR with EPNet: gate hidden, gate pre-activations, scaled input
   size_t total = 0;
 };
 
@@ -125,6 +127,10 @@ struct cvr_model {
   // CVR: the tokenizer split into its request-side and item-side columns (both present and every
   // run a multiple of 32 wide), so requests with many candidates tokenize their own columns once
   bool tok_split = false;
+  // CVR with EPNet: runs of context-side (scenario) features in the request-side matrix, their
+  // total width
+  std::vector<cvr::InputSeg> dom_segs;
+  int D_dom = 0;
   // weights
   std::vector<cvr::WEntry> w;
   std::map<std::string, int> widx;

@@ -23,7 +23,7 @@ CVR_MODEL_DLRM, CVR_MODEL_HYFORMER = 0, 1
 CVR_SIDE_USER, CVR_SIDE_ITEM, CVR_SIDE_CONTEXT = 0, 1, 2
 CVR_LOWP_FP16, CVR_LOWP_BF16 = 0, 1
 (CVR_DBG_CAND_REQ, CVR_DBG_POOLED, CVR_DBG_INPUT_REQ, CVR_DBG_INPUT_ITEM, CVR_DBG_LOGITS, CVR_DBG_HSEQ,
- CVR_DBG_SEQ_POOL, CVR_DBG_TOKENS, CVR_DBG_QUERY, CVR_DBG_ATTN, CVR_DBG_HIDDEN) = range(11)
+ CVR_DBG_SEQ_POOL, CVR_DBG_TOKENS, CVR_DBG_QUERY, CVR_DBG_ATTN, CVR_DBG_HIDDEN, CVR_DBG_EPNET) = range(12)
 CVR_OPT_DLRM_PASS_ROWS, CVR_OPT_TOK_SHARE, CVR_OPT_ATTN_MQ = range(3)
 SIDES = {"user": CVR_SIDE_USER, "item": CVR_SIDE_ITEM, "context": CVR_SIDE_CONTEXT}
 
@@ -44,7 +44,8 @@ class cvr_spec(C.Structure):
                 ("n_seq_cols", C.c_int32), ("seq_tables", C.POINTER(C.c_int32)),
                 ("swiglu_hidden", C.c_int32), ("tau", C.c_float), ("mixer_heads", C.c_int32),
                 ("mixer_hidden", C.c_int32), ("n_experts", C.c_int32), ("expert_dim", C.c_int32),
-                ("n_tasks", C.c_int32), ("head_hidden", C.c_int32), ("task_experts", C.POINTER(C.c_int32))]
+                ("n_tasks", C.c_int32), ("head_hidden", C.c_int32), ("task_experts", C.POINTER(C.c_int32)),
+                ("epnet_hidden", C.c_int32)]
 
 
 class cvr_weight(C.Structure):
@@ -272,6 +273,7 @@ def spec_to_c(spec, tables):
         s.mixer_heads, s.mixer_hidden = spec["mixer_heads"], spec["mixer_hidden"]
         s.n_experts, s.expert_dim = spec["n_experts"], spec["expert_dim"]
         s.n_tasks, s.head_hidden = spec["n_tasks"], spec["head_hidden"]
+        s.epnet_hidden = int(spec.get("epnet_hidden") or 0)
         if spec.get("ple_task_experts") is not None:
             E = spec["n_experts"]
             mask = [0] * (spec["n_tasks"] * E)

@@ -120,6 +120,12 @@ typedef struct {
    * expert per task plus one shared expert (CVR article section 3.2.4).  Gate
    * k's Linear has one output per expert it mixes, in expert order. */
   const int32_t* task_experts;
+  /* (CVR) EPNet: 0 (off), or the hidden width (a multiple of 32) of the gate unit that scales
+   * the non-sequence embedding before tokenization (CVR article section 3.2.1; read as
+   * PEPNet's gate: e' = e * 2 sigmoid(W2 ReLU(W1 [e_domain, e] + b1) + b2), e_domain the
+   * context-side features' columns).  Weights epnet.fc1.{weight,bias} [hidden][D_domain + D],
+   * epnet.fc2.{weight,bias} [D][hidden].  Needs at least one context-side feature. */
+  int32_t epnet_hidden;
 } cvr_spec;
 
 /* One dense parameter, fp32, device memory, read only during cvr_create.
@@ -128,7 +134,7 @@ typedef struct {
  *   CVR:  tok.{weight,bias}; seq.<s>.{gate,up,down}.{weight,bias};
  *         layer.<l>.query.<s>.{weight,bias}; layer.<l>.mix.<h>.{fc1,fc2}.{weight,bias};
  *         ple.expert.<e>.{weight,bias}; ple.gate.<k>.{weight,bias};
- *         head.<k>.{fc1,fc2}.{weight,bias}. */
+ *         head.<k>.{fc1,fc2}.{weight,bias}; with EPNet also epnet.{fc1,fc2}.{weight,bias}. */
 typedef struct {
   const char* name;         /* host string */
   const float* data;        /* device */
@@ -292,9 +298,10 @@ enum {
                                scoring when the fused token mixer runs: it then writes Z as bf16) */
   CVR_DBG_QUERY = 8,        /* (CVR) fp32 [n_seq][n][d]: last layer's queries */
   CVR_DBG_ATTN = 9,         /* (CVR) fp32 [n][N+n_seq][d]: last layer's token matrix before mixing (attention outputs in rows N..) */
-  CVR_DBG_HIDDEN = 10       /* (DLRM, debug mode) lowp [n][width]: activations of the last hidden
+  CVR_DBG_HIDDEN = 10,      /* (DLRM, debug mode) lowp [n][width]: activations of the last hidden
                                layer (outside debug mode that layer may hand per-row partials of
                                the output layer to it instead of storing its activations) */
+  CVR_DBG_EPNET = 11        /* (CVR with EPNet) bf16 [n][D]: the scaled model input (tokenizer input) */
 };
 cvr_status cvr_set_debug(cvr_handle h, int32_t debug);
 cvr_status cvr_debug_export(cvr_handle h, int32_t what, void* dst, size_t dst_bytes, size_t* written,

@@ -114,6 +114,29 @@ def test_cvr_spec_in_fp16_is_rejected():
     assert cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"])) > 0
 
 
+def test_epnet_spec_checks():
+    cvr = synth.load_spec("c3")
+    s, tabs, keep = _spec_c(dict(cvr, epnet_hidden=100))
+    with pytest.raises(cv.CvrError) as e:
+        cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"]))
+    assert e.value.status == cv.CVR_ERR_UNSUPPORTED
+    no_ctx = dict(cvr, epnet_hidden=128, features=[dict(f, side="user") if f["side"] == "context" else f
+                                                   for f in cvr["features"]])
+    s, tabs, keep = _spec_c(no_ctx)
+    with pytest.raises(cv.CvrError, match="context"):
+        cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"]))
+    # the arena gains the two gate Linears (bf16) and their biases (fp32), and loses the
+    # tokenizer's request-side and item-side copies (the scaled input is per candidate, so the
+    # request-side block is no longer shared)
+    base = cv.cvr_weight_arena_bytes(*_spec_c(cvr)[:2], len(cvr["tables"]))
+    s, tabs, keep = _spec_c(dict(cvr, epnet_hidden=128))
+    grown = cv.cvr_weight_arena_bytes(s, tabs, len(cvr["tables"]))
+    r = lambda x: (x + 255) // 256 * 256
+    gate = r(128 * (256 + 1280) * 2) + r(128 * 4) + r(1280 * 128 * 2) + r(1280 * 4)
+    split = r(13 * 128 * 768 * 2) + r(13 * 128 * 512 * 2)
+    assert grown - base == gate - split
+
+
 def test_set_option_needs_a_handle_and_known_values():
     L = cv.lib()
     assert L.cvr_set_option(None, cv.CVR_OPT_ATTN_MQ, 1) == cv.CVR_ERR_ARG

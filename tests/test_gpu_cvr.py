@@ -60,7 +60,16 @@ def check_cvr(spec, m, batch, variant, requests=None, tables_host=None):
         bags = cands if f["side"] == "item" else np.unique(ex["cand_req"][cands])
         assert np.array_equal(pooled[fi][bags], oracle_pooled(spec, tables_host, ex, fi, bags)), fi
     xr, xi = export_inputs(m, spec, db)
-    assert np.array_equal(assemble_inputs(spec, xr, xi, cand_req, cands), tr["e"])
+    assert np.array_equal(assemble_inputs(spec, xr, xi, cand_req, cands), tr["e_in"])
+    if spec.get("epnet_hidden"):
+        # EPNet's scaled input: one rounding past the gate (fp32 sums and exp on the GPU), so an
+        # element equals the oracle's or sits one bf16 step away
+        D = tr["e"].shape[1]
+        xe = bf16_np(m.export(cv.CVR_DBG_EPNET, torch.bfloat16, (max(n, 1), D)))[cands]
+        steps = np.abs(xe - tr["e"]) / np.maximum(np.ldexp(1.0, np.frexp(np.maximum(np.abs(xe), np.abs(tr["e"])))[1] - 8),
+                                                  2.0 ** -133)
+        banner(f"  EPNet input: max bf16 steps {steps.max():.2f}, share differing {np.mean(xe != tr['e']):.2e}")
+        assert steps.max() <= 1.0 and np.mean(xe != tr["e"]) < 1e-2
     # B3-B5: encoded sequences (one rounding step after the bf16 gate/up input, one after the down projection)
     so = ex["seq_offsets"]
     Hg = bf16_np(m.export(cv.CVR_DBG_HSEQ, torch.bfloat16, (max(db.n_positions, 1), d)))
@@ -83,7 +92,7 @@ def check_cvr(spec, m, batch, variant, requests=None, tables_host=None):
     assert pool_err <= U_BF16
     # B2 + B7 of the last layer: tokens before mixing (rows 0..N-1 are the layer input, N.. the attention outputs)
     Yg = m.export(cv.CVR_DBG_ATTN, torch.float32, (max(n, 1), T, d)).cpu().numpy().astype(np.float64)[cands]
-    if spec["n_layers"] == 1:
+    if spec["n_layers"] == 1 and not spec.get("epnet_hidden"):
         # tokens are an fp32 GEMM output over bit-exact bf16 inputs: fp32 vs fp64 accumulation only
         x0 = tr["X0"]
         banner(f"  tokens: max |d| / rms {np.abs(Yg[:, :N] - x0).max() / rms(x0):.2e}")
@@ -186,6 +195,26 @@ def test_c3_task_specific_experts(task_experts):
     banner(f"c3 stress, PLE task experts {task_experts}: 16 samples")
     m, _ = build_model(spec, "stress")
     check_cvr(spec, m, synth.make_batch(spec, requests=16), "stress")
+
+
+@pytest.mark.parametrize("variant", ["bench", "stress"])
+def test_epnet(variant):
+    """EPNet (PEPNet's gate on the context-side scenario features, CVR article section 3.2.1
+    reading) ahead of the tokenizer: the scaled input and every later stage against the oracle,
+    one candidate per request and several (the tokenizer then reads the scaled rows whole)."""
+    spec = dict(synth.load_spec("c3"), epnet_hidden=128)
+    for kw in [dict(requests=16), dict(cand_counts=[7, 0, 40, 1, 3])]:
+        banner(f"c3 {variant} with EPNet (hidden 128): {kw}")
+        m, _ = build_model(spec, variant)
+        check_cvr(spec, m, synth.make_batch(spec, **kw), variant)
+        m.close()
+
+
+def test_epnet_two_layers_full_debug_off():
+    spec = dict(synth.load_spec("c4"), epnet_hidden=256)
+    banner("c4 stress with EPNet (hidden 256), 4096 samples, debug off: oracle on samples 0, 2047, 4095")
+    m, _ = build_model(spec, "stress", debug=False)
+    check_scores_debug_off(spec, m, synth.make_batch(spec), "stress", requests=[0, 2047, 4095])
 
 
 def test_mixer_gemm_path():
