@@ -48,7 +48,7 @@ def dlrm_output_bytes(spec, n):
     return total
 
 
-def stage_work(spec, batch):
+def stage_work(spec, batch, user_block=False):
     """Algorithmic work per step, per stage: ("flop"|"byte", amount).
 
     FLOPs count 2*M*N*K per Linear as performed.  Bytes count what the stage
@@ -73,6 +73,11 @@ def stage_work(spec, batch):
     if spec["model"] == "dlrm":
         work["mlp_gemm"] = ("flop", n * sum(lin(k) for k in shapes if k.startswith("mlp.") and k.endswith(".weight")
                                           and shapes[k][0] > 1))
+        if user_block:
+            # performed: the first layer's request-side columns once per request, not per candidate
+            d_req = sum(spec["tables"][f["table"]]["dim"] for f in spec["features"] if f["side"] != "item")
+            w0 = spec["mlp_hidden"][0]
+            work["mlp_gemm"] = ("flop", work["mlp_gemm"][1] - 2 * (n - R) * w0 * d_req)
         work["dlrm_output"] = ("byte", dlrm_output_bytes(spec, n))
         return work
     S = len(spec["seq"]["lengths"])
@@ -201,6 +206,8 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     # created stream, and eager calls then run on the same one)
     torch.cuda.synchronize()
     model = cv.Model(spec, tables, weights, stream=torch.cuda.Stream())
+    if args.user_block and spec["model"] == "dlrm":
+        model.set_option(cv.CVR_OPT_DLRM_USER_BLOCK, 1)
     cache_cfg = {}
     if cached:
         total = sum(spec["tables"][t]["rows"] * spec["tables"][t]["dim"] * 4 for t in cached)
@@ -310,7 +317,8 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     value = (graph_info["candidates_per_step"] if graph_info else n) * steps / dt
 
     # per-stage rooflines from the live event timings; the dominant stage gives "roofline"
-    works = [stage_work(spec, b) for b in batches]
+    user_blk = bool(args.user_block and spec["model"] == "dlrm")
+    works = [stage_work(spec, b, user_blk) for b in batches]
     work = {k: (v[0], sum(w[k][1] for w in works) / len(works)) for k, v in works[0].items()}
     peak_f = MFMA_PEAK_TFLOPS[spec["lowp"]]
     default_shape = batch is None and candidates is None and not uniform_ids and not args.cache
@@ -372,6 +380,8 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
                         "requests_per_step": db.n_requests},
                        **({"ple_task_experts": spec["ple_task_experts"]} if args.ple_task_experts else {}),
                        **({"epnet_hidden": spec["epnet_hidden"]} if spec.get("epnet_hidden") else {}),
+                       **({"user_block": "first-layer request-side columns once per request"}
+                          if args.user_block and spec["model"] == "dlrm" else {}),
                        **({"hot_row_cache": cache_cfg, "distinct_batches": nb} if cached else {})),
         "roofline": roof,
         "stages": table,
@@ -437,6 +447,8 @@ def main():
     ap.add_argument("--epnet", type=int, default=0,
                     help="CVR: EPNet gate hidden width (0: off), scaling the non-sequence embedding by the "
                          "context-side scenario features (CVR article section 3.2.1)")
+    ap.add_argument("--user-block", action="store_true",
+                    help="DLRM: the first Linear's request-side columns once per request (CVR_OPT_DLRM_USER_BLOCK)")
     ap.add_argument("--uniform-ids", action="store_true", help="cold control: uniform ids instead of Zipf")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",

@@ -142,9 +142,10 @@ static void derive(cvr_model* m) {
   }
   // the tokenizer's request-side block once per request: not with EPNet, whose scale is per candidate
   m->tok_split = s.model == CVR_MODEL_HYFORMER && m->D_req > 0 && m->D_item > 0 && s.epnet_hidden == 0;
+  m->dlrm_split = s.model == CVR_MODEL_DLRM && m->D_req > 0 && m->D_item > 0 && s.n_hidden > 0;
   int kb = 0;
   for (const InputSeg& sg : m->segs) {
-    if ((sg.k_end - kb) % 32) m->tok_split = false;
+    if ((sg.k_end - kb) % 32) m->tok_split = m->dlrm_split = false;
     kb = sg.k_end;
   }
 }
@@ -168,6 +169,11 @@ static void plan_weights(cvr_model* m) {
       const int out = i < s.n_hidden ? m->hidden[i] : 1;
       add("mlp." + std::to_string(i) + ".weight", out, in, true);
       add("mlp." + std::to_string(i) + ".bias", out, 1, false);
+      if (i == 0 && m->dlrm_split) {
+        // the first Linear's request-side and item-side columns as matrices of their own
+        add("_mlp0.req.weight", out, m->D_req, true);
+        add("_mlp0.item.weight", out, m->D_item, true);
+      }
       in = out;
     }
   } else {
@@ -336,11 +342,14 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
   }
   for (size_t i = 0; i < seen.size(); ++i)
     if (!seen[i] && m->w[i].name[0] != '_') { std::string n = m->w[i].name; delete m; return fail(nullptr, CVR_ERR_SPEC, "missing weight " + n); }
-  if (m->tok_split) {
-    // column runs of the packed tokenizer weight into its request-side and item-side halves
-    const WEntry& wt = m->w[m->widx.at("tok.weight")];
-    const WEntry& wr = m->w[m->widx.at("_tok.req.weight")];
-    const WEntry& wi = m->w[m->widx.at("_tok.item.weight")];
+  // column runs of a packed input-side weight (the tokenizer's, or the first MLP layer's) into its
+  // request-side and item-side matrices
+  const char* split_src = m->tok_split ? "tok.weight" : (m->dlrm_split ? "mlp.0.weight" : nullptr);
+  if (split_src) {
+    const std::string pre = m->tok_split ? "_tok" : "_mlp0";
+    const WEntry& wt = m->w[m->widx.at(split_src)];
+    const WEntry& wr = m->w[m->widx.at(pre + ".req.weight")];
+    const WEntry& wi = m->w[m->widx.at(pre + ".item.weight")];
     int kb = 0, creq = 0, citem = 0;
     for (const InputSeg& sg : m->segs) {
       const int width = sg.k_end - kb;
@@ -349,7 +358,7 @@ extern "C" cvr_status cvr_create(const cvr_spec* spec, const cvr_table* tables, 
       hipError_t he = hipMemcpy2DAsync(m->arena + dst.off + (size_t)c * 2, (size_t)dst.cols * 2,
                                        m->arena + wt.off + (size_t)kb * 2, (size_t)wt.cols * 2, (size_t)width * 2,
                                        (size_t)wt.rows, hipMemcpyDeviceToDevice, s);
-      if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("splitting tokenizer: ") + hipGetErrorString(he)); }
+      if (he != hipSuccess) { delete m; return fail(nullptr, CVR_ERR_HIP, std::string("splitting input weight: ") + hipGetErrorString(he)); }
       c += width;
       kb = sg.k_end;
     }
@@ -419,6 +428,7 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     w.h[1] = take((size_t)hr * maxw * lp);
     const int wl = s.n_hidden > 0 ? m->hidden[s.n_hidden - 1] : 0;
     w.opart = take((size_t)((wl + kOutGroup - 1) / kOutGroup) * hr * 4);
+    if (m->dlrm_split) w.u_req = take((size_t)R * m->hidden[0] * 4);
   } else {
     const int64_t d = s.d, S = s.n_seq, T = s.n_tokens + s.n_seq;
     w.tok[0] = take((size_t)n * T * d * 4);
@@ -669,6 +679,32 @@ static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsP
   const int L_ = sp.n_hidden;
   const void* w_out = m->wptr("mlp." + std::to_string(L_) + ".weight");
   const float* b_out = (const float*)m->wptr("mlp." + std::to_string(L_) + ".bias");
+  // The user block (CTR article section 四; CVR article section 3.4.5, taken to the first layer):
+  // the request-side columns of the first Linear multiplied once per request, U = X_req W_req^T
+  // in fp32; every candidate's first layer adds its request's row of U to its item-side product.
+  const bool user_block = m->dlrm_split && m->opt_user_block == 1;
+  if (user_block) {
+    GemmParams g{};
+    g.M = b->n_requests;
+    g.N = m->hidden[0];
+    g.K = m->D_req;
+    g.groups = 1;
+    int kb = 0, k = 0;
+    for (const InputSeg& sg : m->segs) {
+      if (!sg.item) {
+        k += sg.k_end - kb;
+        g.seg[g.nseg++] = ASeg{ws + w.x_req, nullptr, (int64_t)m->ld_req, 0, k, 8, sg.col0, 0};
+      }
+      kb = sg.k_end;
+    }
+    g.W = m->wptr("_mlp0.req.weight");
+    g.C = ws + w.u_req;
+    g.ldc = m->hidden[0];
+    g.c_nstride8 = 8;
+    g.out_f32 = 1;
+    e = L(STAGE_MLP_GEMM, [&] { return launch_gemm(g, sp.lowp, s); });
+    if (e != hipSuccess) return e;
+  }
   for (int64_t r0 = 0; r0 < n; r0 += pr) {
     const int mc = (int)std::min(pr, n - r0);
     int in = m->e_dim;
@@ -681,12 +717,30 @@ static hipError_t run_dlrm(cvr_model* m, const cvr_batch* b, char* ws, const WsP
       g.N = width;
       g.K = in;
       g.groups = 1;
-      if (i == 0) input_segments(m, ws, w, g, r0);
-      else {
+      g.W = m->wptr("mlp." + std::to_string(i) + ".weight");
+      if (i == 0 && user_block) {
+        // item-side columns only, plus the request's row of U
+        g.K = m->D_item;
+        int kb = 0, k = 0;
+        for (const InputSeg& sg : m->segs) {
+          if (sg.item) {
+            k += sg.k_end - kb;
+            g.seg[g.nseg++] = ASeg{ws + w.x_item + (size_t)r0 * m->ld_item * 2, nullptr, (int64_t)m->ld_item, 0, k, 8,
+                                   sg.col0, 0};
+          }
+          kb = sg.k_end;
+        }
+        g.W = m->wptr("_mlp0.item.weight");
+        g.R = ws + w.u_req;
+        g.r_f32 = 1;
+        g.r_rowmap = (const int32_t*)(ws + w.cand_req) + r0;
+        g.r_ld = m->hidden[0];
+      } else if (i == 0) {
+        input_segments(m, ws, w, g, r0);
+      } else {
         g.nseg = 1;
         g.seg[0] = ASeg{ws + w.h[cur], nullptr, (int64_t)in, 0, in, 8, 0, 0};
       }
-      g.W = m->wptr("mlp." + std::to_string(i) + ".weight");
       g.bias = (const float*)m->wptr("mlp." + std::to_string(i) + ".bias");
       const int nxt = cur == 0 ? 1 : 0;
       g.C = ws + w.h[nxt];
@@ -1013,6 +1067,12 @@ extern "C" cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value
     case CVR_OPT_ATTN_MQ:
       if (value < -1 || value > 1) return fail(h, CVR_ERR_ARG, "attention form must be -1, 0 or 1");
       h->opt_attn_mq = (int)value;
+      break;
+    case CVR_OPT_DLRM_USER_BLOCK:
+      if (value < -1 || value > 1) return fail(h, CVR_ERR_ARG, "user block must be -1, 0 or 1");
+      if (value == 1 && !h->dlrm_split)
+        return fail(h, CVR_ERR_UNSUPPORTED, "the user block needs a DLRM spec with both sides, runs of 32 columns");
+      h->opt_user_block = (int)value;
       break;
     default: return fail(h, CVR_ERR_ARG, "unknown option");
   }

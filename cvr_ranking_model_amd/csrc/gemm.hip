@@ -219,8 +219,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   const float* bias = p.bias ? p.bias + (int64_t)g * p.bias_gstride : nullptr;
   constexpr bool kCanStageF32 = 4 * 32 * (WTN + 8) * 4 <= kSmemElems * (int)sizeof(T);
   constexpr bool kCanStageLp = 4 * 32 * (WTN + 8) * (int)sizeof(T) <= kSmemElems * (int)sizeof(T);
-  // an fp32 residual (no ReLU to follow it) is added on the way out of the staging area
-  const bool stage_r = !p.R || (p.out_f32 && p.r_f32 && !p.relu && (!p.r_rowmap || (p.r_ld & 3) == 0));
+  // An fp32 residual is added on the way out of the staging area for fp32 outputs (no ReLU may
+  // follow it there), and before the ReLU on the way in for low-precision outputs.
+  const bool stage_r = !p.R || (p.r_f32 && (p.out_f32 ? (!p.relu && (!p.r_rowmap || (p.r_ld & 3) == 0)) : true));
   if ((p.out_f32 ? kCanStageF32 : kCanStageLp) && p.c_nstride8 == 8 && stage_r && (p.ldc & 7) == 0) {
     // Contiguous output rows: stage each wave's tile 32 rows at a time through LDS (free after
     // the K loop) and write it back as 16-byte row segments.  Every thread runs the same number
@@ -283,6 +284,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             float x = acc[i][j][v] + bn;
+            if (p.R) {
+              const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+              if (m < p.M && n < p.N)
+                x += reinterpret_cast<const float*>(p.R)[p.r_rowmap ? (int64_t)p.r_rowmap[m] * p.r_ld + n
+                                                                    : (int64_t)g * p.c_gstride + (int64_t)m * p.ldc + n];
+            }
             if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = relu_f32(x);
             st[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * OP + nl] = Lowp<T>::from_f32(x);
           }

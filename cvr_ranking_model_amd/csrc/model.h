@@ -55,6 +55,7 @@ struct WsPlan {
   size_t flag = 0, cand_req = 0, x_req = 0, x_item = 0, logits = 0, pooled = 0, pooled_bytes = 0;
   size_t h[2] = {0, 0};
   size_t opart = 0;  // DLRM: output-layer partials of a fused last hidden layer
+  size_t u_req = 0;  // DLRM with the user block once per request: [R][width 0] fp32
   size_t tok[2] = {0, 0}, hseq = 0, chunk_off = 0, chunk_desc = 0, pool_part = 0, seq_pool = 0, query = 0,
          mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0, tok_req = 0;
   size_t ep_h = 0, ep_g = 0, x_ep = 0;  // CVR with EPNet: gate hidden, gate pre-activations, scaled input
@@ -131,6 +132,9 @@ struct cvr_model {
   // total width
   std::vector<cvr::InputSeg> dom_segs;
   int D_dom = 0;
+  // DLRM: the first Linear split into its request-side and item-side columns (both present and
+  // every run a multiple of 32 wide), so the request-side product can run once per request
+  bool dlrm_split = false;
   // weights
   std::vector<cvr::WEntry> w;
   std::map<std::string, int> widx;
@@ -142,6 +146,7 @@ struct cvr_model {
   int64_t pass_rows = -1;  // DLRM candidates per MLP pass: -1 derived from the layer width, 0 one pass
   int opt_tok_share = -1;  // CVR_OPT_TOK_SHARE: -1 auto, 0 off, 1 on
   int opt_attn_mq = -1;    // CVR_OPT_ATTN_MQ: -1 auto, 0 per candidate, 1 MFMA per request
+  int opt_user_block = -1; // CVR_OPT_DLRM_USER_BLOCK: -1 auto (off), 0 off, 1 on
   std::string err;
   char* last_ws = nullptr;
   cvr::WsPlan last_plan;

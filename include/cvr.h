@@ -273,8 +273,14 @@ cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures)
  *   CVR_OPT_ATTN_MQ         CVR: attention of a request's candidates as MFMA products over its
  *                           shared states.  -1 (default): when requests average 16 or more
  *                           candidates; 0: never (one block per candidate); 1: always.
+ *   CVR_OPT_DLRM_USER_BLOCK DLRM: the first Linear's request-side columns multiplied once per
+ *                           request (U = X_req W_req^T in fp32) and U's row added to every
+ *                           candidate's item-side product (CTR article section 四, CVR article
+ *                           section 3.4.5).  -1 (default) and 0: off; 1: on (CVR_ERR_UNSUPPORTED
+ *                           unless the spec has request-side and item-side features in runs of
+ *                           multiples of 32 columns).
  * Unknown options and values outside these ranges return CVR_ERR_ARG. */
-enum { CVR_OPT_DLRM_PASS_ROWS = 0, CVR_OPT_TOK_SHARE = 1, CVR_OPT_ATTN_MQ = 2 };
+enum { CVR_OPT_DLRM_PASS_ROWS = 0, CVR_OPT_TOK_SHARE = 1, CVR_OPT_ATTN_MQ = 2, CVR_OPT_DLRM_USER_BLOCK = 3 };
 cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value);
 
 /* Wait for the stream and report the device error flag of the last

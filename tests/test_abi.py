@@ -57,6 +57,12 @@ def test_arena_size_matches_weight_shapes():
         for wname, shape in synth.weight_shapes(spec).items():
             n = int(np.prod(shape))
             want += ((n * (2 if wname.endswith(".weight") else 4)) + 255) // 256 * 256
+        if spec["model"] == "dlrm":
+            # the first Linear's request-side and item-side columns as two more matrices
+            dims = [spec["tables"][f["table"]]["dim"] for f in spec["features"]]
+            d_item = sum(dmn for dmn, f in zip(dims, spec["features"]) if f["side"] == "item")
+            w0 = spec["mlp_hidden"][0]
+            want += (w0 * (sum(dims) - d_item) * 2 + 255) // 256 * 256 + (w0 * d_item * 2 + 255) // 256 * 256
         if spec["model"] == "hyformer":
             # one internal fp32 bias vector for the expert GEMM: expert biases, then gate biases
             gates = spec["n_tasks"] * spec["n_experts"]

@@ -220,6 +220,33 @@ def test_mlp_slices_equal_one_pass():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,variant", [("c2", "stress"), ("c2", "bench"), ("c5", "stress"), ("c1", "clamp")])
+def test_user_block_once_per_request(name, variant):
+    """The first Linear's request-side columns multiplied once per request and added to every
+    candidate's item-side product (CVR_OPT_DLRM_USER_BLOCK): the bench's launch configuration
+    against the oracle (plan and exact arithmetic) on sampled requests, and against the same
+    model without the block (only the order of fp32 additions differs)."""
+    spec = synth.load_spec(name)
+    banner(f"{name} {variant}: first-layer user block once per request")
+    m, _ = build_model(spec, variant, debug=False)
+    b = synth.make_batch(spec)
+    R = len(b["cand_offsets"]) - 1
+    reqs = sorted({0, R // 2, R - 1})
+    _, ref, st = run(m, b)
+    assert st == cv.CVR_OK
+    ref = ref.cpu().numpy().copy()
+    m.set_option(cv.CVR_OPT_DLRM_USER_BLOCK, 1)
+    out = check_scores_debug_off(spec, m, b, variant, requests=reqs)
+    d = float(np.abs(out.cpu().numpy() - ref).max())
+    banner(f"  with vs without the block: max |d score| {d:.3e}")
+    assert d <= SCORE_TOL
+    m.set_option(cv.CVR_OPT_DLRM_USER_BLOCK, 0)
+    _, again, st = run(m, b)
+    assert np.array_equal(again.cpu().numpy(), ref)
+    del m
+    torch.cuda.empty_cache()
+
+
 def _tiny():
     return tiny_dlrm_spec(dims=(16, 16, 32, 32), hidden=(64, 32), rows=50, bag_max=5)
 
