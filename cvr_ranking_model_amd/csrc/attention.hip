@@ -5,9 +5,11 @@
 // temperature that keeps the softmax from collapsing to one-hot:
 //   o = sum_t softmax_t(H[t] . q / tau) H[t]      over the valid positions t.
 //
-// One block of 4 waves per (candidate, sequence).  Eight lanes share a position (16
-// columns each, two 16-byte loads of the bf16 row), a wave covers 8 positions and the
-// block 32 per step.  Each lane group keeps an online softmax state (running max, sum of
+// One block of 4 waves per (candidate, sequence).  Eight lanes share a position: lane `sub`
+// holds columns 8*sub .. 8*sub+7 and 64 + 8*sub .. 64 + 8*sub + 7, so each 16-byte load of a
+// wave reads one whole 128-byte half row for each of its 8 positions; a wave covers 8 positions
+// and the block 32 per step, and each lane group loads its next position before it works on
+// the current one.  Each lane group keeps an online softmax state (running max, sum of
 // exponentials, weighted sum) in fp32; states are merged in a fixed butterfly order across
 // lane groups and then wave by wave, so the result is bitwise reproducible.  The output is
 // written in fp32 as token N+s of the token matrix.  A single pass reads each encoded state
@@ -51,16 +53,22 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
   a = a < 0 ? 0 : (a > p.n_positions ? p.n_positions : a);
   e = e < a ? a : (e > p.n_positions ? p.n_positions : e);
 
+  // q[0..7] = columns 8*sub.., q[8..15] = columns 64 + 8*sub..
   float q[16];
   {
-    const float4* qp = reinterpret_cast<const float4*>(p.q + ((int64_t)s * p.n + c) * 128 + sub * 16);
+    const float* qrow = p.q + ((int64_t)s * p.n + c) * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = qp[j];
-      q[4 * j] = v.x;
-      q[4 * j + 1] = v.y;
-      q[4 * j + 2] = v.z;
-      q[4 * j + 3] = v.w;
+    for (int hf = 0; hf < 2; ++hf) {
+      const float4* qp = reinterpret_cast<const float4*>(qrow + 64 * hf + sub * 8);
+      const float4 v0 = qp[0], v1 = qp[1];
+      q[8 * hf + 0] = v0.x;
+      q[8 * hf + 1] = v0.y;
+      q[8 * hf + 2] = v0.z;
+      q[8 * hf + 3] = v0.w;
+      q[8 * hf + 4] = v1.x;
+      q[8 * hf + 5] = v1.y;
+      q[8 * hf + 6] = v1.z;
+      q[8 * hf + 7] = v1.w;
     }
   }
   SoftState st;
@@ -69,11 +77,19 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) st.o[j] = 0.f;
 
+  // the row of position t: columns 8*sub.. and 64 + 8*sub..
+  auto load_row = [&](int64_t t, bf16x8& h0, bf16x8& h1) {
+    const bf16* hp = p.H + t * 128 + sub * 8;
+    h0 = *reinterpret_cast<const bf16x8*>(hp);
+    h1 = *reinterpret_cast<const bf16x8*>(hp + 64);
+  };
+  int64_t t = a + wave * 8 + grp;
+  bf16x8 n0, n1;
+  if (t < e) load_row(t, n0, n1);
 #pragma unroll 1
-  for (int64_t t = a + wave * 8 + grp; t < e; t += 32) {
-    const bf16* hp = p.H + t * 128 + sub * 16;
-    const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(hp);
-    const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(hp + 8);
+  for (; t < e; t += 32) {
+    const bf16x8 h0 = n0, h1 = n1;
+    if (t + 32 < e) load_row(t + 32, n0, n1);
     float h[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -121,10 +137,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
       merge_state(st, o2);
     }
     const float inv = st.l == 0.f ? 0.f : 1.0f / st.l;  // an empty sequence gives 0; NaN passes
-    float4* out = reinterpret_cast<float4*>(p.Y + ((int64_t)c * p.T + p.N + s) * 128 + sub * 16);
+    float* orow = p.Y + ((int64_t)c * p.T + p.N + s) * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      out[j] = make_float4(st.o[4 * j] * inv, st.o[4 * j + 1] * inv, st.o[4 * j + 2] * inv, st.o[4 * j + 3] * inv);
+    for (int hf = 0; hf < 2; ++hf) {
+      float4* out = reinterpret_cast<float4*>(orow + 64 * hf + sub * 8);
+      out[0] = make_float4(st.o[8 * hf] * inv, st.o[8 * hf + 1] * inv, st.o[8 * hf + 2] * inv, st.o[8 * hf + 3] * inv);
+      out[1] = make_float4(st.o[8 * hf + 4] * inv, st.o[8 * hf + 5] * inv, st.o[8 * hf + 6] * inv, st.o[8 * hf + 7] * inv);
+    }
   }
 }
 

@@ -15,9 +15,9 @@
 //      64w..64w+63 and the matching up units, so SiLU(gate+b) * (up+b) is formed in
 //      registers and written to LDS as bf16 (the input of the down projection);
 //   3. H = A W_down^T + b (MFMA 32x32x16; the bias starts one of the two accumulators),
-//      rounded to bf16, staged through LDS and stored as
-//      rows; the rounded values are summed per column over the chunk's positions for the
-//      mean pool.
+//      rounded to bf16, staged through LDS and stored as rows; the rounded values are summed
+//      per column over the chunk's positions for the mean pool (for a full chunk on the matrix
+//      unit, as a product with a matrix of ones).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -248,23 +248,26 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
             for (int pg = 0; pg < 2; ++pg)
               acc[q][h][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[q][h][ks], e[pg][ks], acc[q][h][pg], 0, 0, 0);
         };
-        // The matrix phase runs at a raised wave priority, so the consumer on this SIMD fills the
-        // vector unit around it rather than the other way round.
-        __builtin_amdgcn_s_setprio(2);
         // Unit group q's SiLU (vector and transcendental instructions) is interleaved with the
-        // matrix instructions of group q+1; only the last group's SiLU runs on its own.
+        // 16 matrix instructions of group q+1, one matrix instruction to four vector ones, so
+        // that the vector work issues while the matrix unit is busy; only the last group's SiLU
+        // runs on its own.
 #pragma unroll
         for (int ks = 0; ks < kD / 32; ++ks) mfma_step(0, ks);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 1; q < 4; ++q)
+        for (int q = 1; q < 4; ++q) {
 #pragma unroll
-          for (int ks = 0; ks < kD / 32; ++ks) {
-            mfma_step(q, ks);
-            if (ks == 1) silu_put(q - 1, 0);
-            if (ks == 3) silu_put(q - 1, 1);
-            __builtin_amdgcn_sched_barrier(0);  // keep each step's MFMAs and SiLU together
+          for (int ks = 0; ks < kD / 32; ++ks) mfma_step(q, ks);
+          silu_put(q - 1, 0);
+          silu_put(q - 1, 1);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
           }
-        __builtin_amdgcn_s_setprio(0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         silu_put(3, 0);
         silu_put(3, 1);
       }
@@ -354,6 +357,48 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   if (bt == 0) Ds[0] = d0;
   __syncthreads();  // E(0) and Ds[0] complete (pairs with the producers' first wait)
 
+  // Chunk c's H (the two accumulator chains h2) rounded to bf16 and staged in Hs[buf] for the
+  // producers; its column sums over the chunk's positions go to Cs[buf].  Lane holds rows
+  // 8*(v/4) + 4*(lane/32) + v%4 of column ncol, converted two rows at a time.
+  auto epilogue = [&](const f32x16 (&h2)[2], int np, int buf) {
+    bf16* hdst = Hs[buf];
+    if (np == kM) {
+      // The column sums of a full chunk on the matrix unit: a 32 x 16 matrix of ones times the
+      // lane's rounded rows as the B operand (lanes l and l+32 hold the 32 rows of column l%32
+      // between them, each row in one k slot), so every entry of the product is the sum.
+      V8 hb[2];
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const bf16x2 h = __builtin_convertvector((float2_t){h2[0][v] + h2[1][v], h2[0][v + 1] + h2[1][v + 1]}, bf16x2);
+        hdst[m * kEPitch + ncol] = h[0];
+        hdst[(m + 1) * kEPitch + ncol] = h[1];
+        hb[v >> 3][v & 7] = h[0];
+        hb[v >> 3][(v & 7) + 1] = h[1];
+      }
+      V8 ones;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
+      f32x16 cs = Lowp<bf16>::mfma32(ones, hb[0], (f32x16){});
+      cs = Lowp<bf16>::mfma32(ones, hb[1], cs);
+      if (lane < 32) Cs[buf][ncol] = cs[0];
+    } else {
+      // a partial chunk: only rows below np are summed, in row order per lane, then the two lanes
+      float colsum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const bf16x2 h = __builtin_convertvector((float2_t){h2[0][v] + h2[1][v], h2[0][v + 1] + h2[1][v + 1]}, bf16x2);
+        hdst[m * kEPitch + ncol] = h[0];
+        hdst[(m + 1) * kEPitch + ncol] = h[1];
+        if (m < np) colsum += (float)h[0];
+        if (m + 1 < np) colsum += (float)h[1];
+      }
+      colsum += __shfl_xor(colsum, 32);
+      if (lane < 32) Cs[buf][ncol] = colsum;
+    }
+  };
+
   // One pipeline iteration; `cur` holds the rows of chunk i+1 and is refilled with i+3.
   auto step = [&](int i, float4 (&cur)[4]) {
     // E(i+1) and the gathers further ahead first: VALU work while the producer on this SIMD
@@ -366,9 +411,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       d5 = desc_of(i + 5);
       if (bt == 0) Ds[(i + 1) & 1] = d1;
     }
-    const bool down = i >= 1 && i <= n;
-    f32x16 hacc[2];
-    if (down) {
+    if (i >= 1 && i <= n) {
       // chunk i-1: down projection on the SiLU tile, while the producer runs its SiLU
       const int s = (dprev.y >> 8) / p.R;
       if (s != cur_s) {
@@ -379,46 +422,28 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         cur_s = s;
       }
       const bf16* A = As[(i - 1) & 1];
+      f32x16 hacc[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {  // even and odd k in two accumulators, the even one starts at the bias
         hacc[0][v] = bd;
         hacc[1][v] = 0.f;
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kHid / 16; ++k) {
         const V8 a = *reinterpret_cast<const V8*>(&A[lr * kAPitch + k * 16 + lk]);
         hacc[k & 1] = Lowp<bf16>::mfma32(a, wd[k], hacc[k & 1]);
       }
-    }
-    if (down) {
-      // bf16 H staged for the producers; lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of ncol,
-      // converted two rows at a time
-      const int np = dprev.y & 255;
-      bf16* hdst = Hs[(i - 1) & 1];
-      float colsum = 0.f;
-      if (np == kM) {
+      // the first eight tile reads go out together, then one read after each matrix
+      // instruction, so the chain does not wait on each read in turn
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bf16x2 h = __builtin_convertvector((float2_t){hacc[0][v] + hacc[1][v], hacc[0][v + 1] + hacc[1][v + 1]}, bf16x2);
-          hdst[m * kEPitch + ncol] = h[0];
-          hdst[(m + 1) * kEPitch + ncol] = h[1];
-          colsum += (float)h[0];
-          colsum += (float)h[1];
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const int m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bf16x2 h = __builtin_convertvector((float2_t){hacc[0][v] + hacc[1][v], hacc[0][v + 1] + hacc[1][v + 1]}, bf16x2);
-          hdst[m * kEPitch + ncol] = h[0];
-          hdst[(m + 1) * kEPitch + ncol] = h[1];
-          if (m < np) colsum += (float)h[0];
-          if (m + 1 < np) colsum += (float)h[1];
-        }
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      colsum += __shfl_xor(colsum, 32);
-      if (lane < 32) Cs[(i - 1) & 1][ncol] = colsum;
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue(hacc, dprev.y & 255, (i - 1) & 1);
     }
     dprev = d0;
     d0 = d1;
