@@ -425,6 +425,74 @@ def run_config(workload, args, steps, warmup, batch=None, candidates=None, unifo
     return res
 
 
+def read_ceilings(reps=10):
+    """Read-bandwidth ceilings of the chip for the two streaming access patterns of the path,
+    measured with the library's probe kernels (cvr_probe_stream_read, cvr_probe_row_read):
+      stream       one front-to-back read of 4 GiB (the cross-attention reads each encoded
+                   state once per layer: 3.49 GB at 4096 samples);
+      rows_<B>_<F> uniform random whole rows of B bytes from a table of F bytes (the embedding
+                   gather: fp32 rows of 32 or 64 columns, tables of 1.28 GB and 25.6 GB), 8M
+                   ids per launch for 128-byte rows and 4M for 256-byte rows.
+    Bytes counted: the buffer, or rows plus the 4-byte ids.  Each shape is timed over `reps`
+    launches (HIP events on the launching stream) at several grid sizes; the best is the ceiling."""
+    import torch
+    from cvr_ranking_model_amd import cvr as cv
+    C = cv.C
+    st = torch.cuda.current_stream()
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+
+    def timed(launch):
+        for _ in range(2):
+            launch()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(st)
+        for _ in range(reps):
+            launch()
+        ev[1].record(st)
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sweep = {}
+    for blocks in [4096, 16384, 65536, 262144]:
+        ms = timed(lambda: cv.cvr_probe_stream_read(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
+                                                    blocks, C.c_void_p(st.cuda_stream)))
+        sweep[blocks] = round(nbytes / ms / 1e6, 1)
+    best = max(sweep, key=sweep.get)
+    out["stream"] = {"GB/s": sweep[best], "frac": round(sweep[best] / HBM_PEAK_GBS, 4), "bytes": nbytes,
+                     "blocks": best, "sweep_GB/s": sweep}
+    del buf
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device="cuda")
+    for foot in [1.28e9, 25.6e9]:
+        for row_bytes in [128, 256]:
+            n_rows = int(foot // row_bytes)
+            n_ids = (8 << 20) if row_bytes == 128 else (4 << 20)
+            table = torch.empty(n_rows * row_bytes, dtype=torch.uint8, device="cuda")
+            table.fill_(1)
+            gen.manual_seed(1234 + row_bytes)
+            ids = torch.randint(0, n_rows, (n_ids,), generator=gen, device="cuda", dtype=torch.int32)
+            moved = n_ids * (row_bytes + 4)
+            sweep = {}
+            for blocks in [2048, 8192, 32768]:
+                ms = timed(lambda: cv.cvr_probe_row_read(C.c_void_p(table.data_ptr()), n_rows, row_bytes,
+                                                         C.c_void_p(ids.data_ptr()), n_ids,
+                                                         C.c_void_p(sink.data_ptr()), blocks,
+                                                         C.c_void_p(st.cuda_stream)))
+                sweep[blocks] = round(moved / ms / 1e6, 1)
+            best = max(sweep, key=sweep.get)
+            out[f"rows_{row_bytes}B_{foot / 1e9:g}GB"] = {
+                "GB/s": sweep[best], "frac": round(sweep[best] / HBM_PEAK_GBS, 4), "bytes": moved,
+                "n_ids": n_ids, "blocks": best, "sweep_GB/s": sweep}
+            del table, ids
+            torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +528,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 256 MiB fp32 copy kernel (torch.neg) so a "
                          "hardware-counter run can scale its byte counters against a known size")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure only the read-bandwidth ceilings (stream and random rows) and print them")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library scores on one GPU (requests would shard across GPUs "
@@ -467,6 +537,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.ceilings:
+        print(json.dumps({"read_ceilings": read_ceilings()}), flush=True)
+        return
     main_res = run_config(args.workload, args, args.steps, args.warmup, batch=args.batch,
                           candidates=args.candidates, uniform_ids=args.uniform_ids,
                           gather_control=not args.no_extra)
@@ -499,6 +572,16 @@ def main():
         for w in [x for x in args.extra.split(",") if x and x != args.workload]:
             configs[w] = run_config(w, args, min(args.steps, 20), min(args.warmup, 5), cpu_budget=10.0)
         line["configs"] = configs
+        line["read_ceilings"] = ceil = read_ceilings()
+        # the streaming kernels against the chip's measured read ceilings
+        att = line.get("stages", {}).get("attention", {}).get("achieved")
+        if att:
+            line["attention_of_stream_ceiling"] = round(att / ceil["stream"]["GB/s"], 4)
+        for w, r in [(args.workload, line)] + list(configs.items()):
+            g = r.get("gather_uniform_ids", {}).get("achieved")
+            if g:
+                r["gather_uniform_of_row_ceiling"] = {
+                    k: round(g / v["GB/s"], 4) for k, v in ceil.items() if k.startswith("rows_")}
     print(json.dumps(line), flush=True)
 
 

@@ -378,6 +378,26 @@ const char* cvr_stage_name(cvr_handle h, int32_t stage);
 cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed, double halfwidth,
                           void* hip_stream);
 
+/* Read-bandwidth probes: the ceilings the streaming kernels are measured
+ * against; not part of scoring.  Each block xors what it read into one
+ * uint32 of sink (device, >= blocks entries, caller-owned), so no load is
+ * dropped; the value means nothing else.  Both enqueue one kernel of
+ * `blocks` blocks of 256 threads (1 <= blocks <= 2^20) on hip_stream and
+ * return CVR_ERR_ARG on a null pointer or a size outside the stated range.
+ * cvr_probe_stream_read: reads `bytes` (a multiple of 16) of device memory
+ *   at src (16-byte aligned) once, front to back, 16 bytes per lane and
+ *   four loads in flight per lane -- the access pattern of the cross-
+ *   attention over encoded states (CVR article, section 3.2.3).
+ * cvr_probe_row_read: for each of the n_ids int32 ids (device), reads the
+ *   whole row of row_bytes (64, 128 or 256) of the device table at table
+ *   (16-byte aligned, n_rows rows), one 16-byte load per lane and eight rows
+ *   in flight per lane group -- the access pattern of the embedding gather
+ *   over HBM-resident rows (CTR article, section 二).  An id outside
+ *   [0, n_rows) reads row 0. */
+cvr_status cvr_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, void* hip_stream);
+cvr_status cvr_probe_row_read(const void* table, int64_t n_rows, int32_t row_bytes, const int32_t* ids,
+                              int64_t n_ids, uint32_t* sink, int32_t blocks, void* hip_stream);
+
 const char* cvr_last_error(cvr_handle h);
 const char* cvr_status_string(cvr_status s);
 void cvr_destroy(cvr_handle h);
