@@ -168,3 +168,27 @@ def test_cache_state_bytes_host_checks():
     for sets, ways, dim in [(0, 4, 32), (16, 0, 32), (16, 17, 64), (16, 4, 30), (1 << 30, 4, 32)]:
         with pytest.raises(cv.CvrError):
             cv.cvr_cache_state_bytes(sets, ways, dim)
+
+
+def test_probe_argument_checks():
+    """The bandwidth probes refuse null pointers, misaligned or ragged sizes, grids outside
+    [1, 2^20] and row widths other than 64/128/256 bytes before any device work."""
+    import ctypes as C
+    fake = C.c_void_p(1 << 20)    # aligned non-null stand-in; never dereferenced on these paths
+    cases = [
+        lambda: cv.cvr_probe_stream_read(None, 1024, fake, 64, None),
+        lambda: cv.cvr_probe_stream_read(fake, 1024, None, 64, None),
+        lambda: cv.cvr_probe_stream_read(C.c_void_p((1 << 20) + 4), 1024, fake, 64, None),
+        lambda: cv.cvr_probe_stream_read(fake, 1000, fake, 64, None),
+        lambda: cv.cvr_probe_stream_read(fake, 1024, fake, 0, None),
+        lambda: cv.cvr_probe_stream_read(fake, 1024, fake, (1 << 20) + 1, None),
+        lambda: cv.cvr_probe_row_read(fake, 100, 96, fake, 10, fake, 64, None),
+        lambda: cv.cvr_probe_row_read(fake, 0, 128, fake, 10, fake, 64, None),
+        lambda: cv.cvr_probe_row_read(None, 100, 128, fake, 10, fake, 64, None),
+        lambda: cv.cvr_probe_row_read(fake, 100, 128, fake, -1, fake, 64, None),
+        lambda: cv.cvr_probe_row_read(fake, 100, 128, fake, 10, fake, 0, None),
+    ]
+    for call in cases:
+        with pytest.raises(cv.CvrError) as e:
+            call()
+        assert e.value.status == cv.CVR_ERR_ARG
