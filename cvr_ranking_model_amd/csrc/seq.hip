@@ -118,6 +118,12 @@ hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t 
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Wait for every outstanding vector-memory operation of this wave (vmcnt(0); the other counters
+// left alone).  Used right after the rare weight reloads, so that the compiler knows the weights
+// have landed after the branch and puts no conservative full wait on the steady-state path,
+// where it would also wait for the gathers and stores still in flight.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 typedef float float2_t __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;        // token width
 constexpr int kHid = 256;      // SwiGLU hidden width
@@ -132,11 +138,13 @@ static_assert(kM == 32, "one 32-row MFMA tile per chunk");
 // Waves 4-7 (consumers) hold the down projection for 32 output columns each, turn chunk c-1
 // into bf16 H (staged in LDS) and pool partials, and gather and convert rows two chunks ahead.
 // Every SIMD runs one wave of each kind, so one's VALU work overlaps the other's matrix
-// instructions.  E, the SiLU tile, the H staging and the chunk descriptors are double-
-// buffered in LDS; one block barrier per iteration hands them over.
-// Loads and stores share one vector-memory counter: consumers only load (their waits count
-// loads alone, so rows two chunks ahead stay in flight) and producers only store (they take no
-// chunk data from global memory: descriptors come through LDS).
+// instructions.  E, the SiLU tile and the H staging are double-buffered in LDS, the chunk
+// descriptors sit in an eight-entry LDS ring; one block barrier per iteration hands them over.
+// Loads and stores share one vector-memory counter and its waits are in issue order (a wait
+// for one load also waits for every older one): consumers only load, in the same order on
+// every path (ids of chunk c+4, then rows of chunk c+3), so the wait for the ids never covers
+// the rows issued after them and the gathers keep two iterations to arrive; producers only
+// store (they take no chunk data from global memory: descriptors come through LDS).
 // Both roles pass the same n + 3 block barriers: one after the consumers' prologue and one at
 // the end of each of the n + 2 pipeline iterations.
 __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
@@ -146,7 +154,9 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   __shared__ __align__(16) float Bs[4][2 * 64];          // producer w: gate bias, up bias
   __shared__ __align__(16) bf16 Hs[2][kM * kEPitch];     // finished H tile of a chunk
   __shared__ __align__(16) float Cs[2][kD];              // its pool partials
-  __shared__ int2 Ds[2];                                  // descriptor of the producers' next chunk
+  // Descriptor ring: chunk c's descriptor sits in Dq[c % 8] from iteration c - 5 on (written
+  // by one consumer thread a full iteration after it loaded it) until iteration c + 3.
+  __shared__ int2 Dq[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool producer = wave < 4;
@@ -184,12 +194,12 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       }
       if (tid < kD) p.part[(int64_t)c * kD + tid] = Cs[i & 1][tid];
     };
-    __syncthreads();  // E(0) and Ds[0] are in place
+    __syncthreads();  // E(0) and the first descriptors are in place
 #pragma unroll 1
     for (int i = 0; i <= n + 1; ++i) {
       int2 d = make_int2(0, 0);
       if (i < n) {
-        d = Ds[i & 1];
+        d = Dq[i & 7];
         const int s = (d.y >> 8) / p.R;
         if (s != cur_s) {
           const bf16* Wgu = p.Wgu + (int64_t)s * p.wgu_gstride;
@@ -207,6 +217,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
           bs[lane] = bg;
           bs[64 + lane] = bu;
           cur_s = s;
+          wait_vm_all();
         }
         const int b = i & 1;
         // Tiles of 16 hidden units x 16 positions (MFMA 16x16x32): unit group q, gate (h = 0) or
@@ -281,7 +292,10 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
 
   // ---------------------------------------------------------------- consumers
   const int bt = tid - 256;  // 0..255
-  const int32_t* seq_ids = p.seq_ids_ref ? *p.seq_ids_ref : p.seq_ids;
+  // Global address space spelled out: a generic pointer would make these flat loads, which the
+  // compiler cannot order against the row gathers and so waits for every load before them.
+  typedef const __attribute__((address_space(1))) int32_t* gptr_i32;
+  const gptr_i32 seq_ids = (gptr_i32)(p.seq_ids_ref ? *p.seq_ids_ref : p.seq_ids);
   // Granule i of a consumer thread covers position (bt + 256 i) / 32 and columns
   // 4 * (bt % 32) .. +3, which sit in one sequence column (table, rows and width fixed).
   const float* gtab;
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   bool bad = false;
   auto load_ids = [&](int2 d, int32_t (&id)[4]) {
     const int np = d.y & 255;
-    const int32_t* chunk_ids = seq_ids + (int64_t)d.x * p.ncols;  // the same for every lane
+    const gptr_i32 chunk_ids = seq_ids + (int64_t)d.x * p.ncols;  // the same for every lane
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pos = gpos0 + 8 * i;
@@ -341,21 +355,33 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
   int cur_s = -1;
   const int ncol = rw * 32 + lr;
 
-  // Descriptors of chunks i-1 .. i+4 (relative to the iteration), loaded ahead; rows of i+1 and
-  // i+2 and ids of i+3 in flight at the start of iteration i.
-  int2 dprev = desc_of(0), d0 = desc_of(0), d1 = desc_of(1), d2 = desc_of(2), d3 = desc_of(3), d4 = desc_of(4);
-  int32_t ids[4];
+  // Rows of chunks i+1 and i+2 and ids of i+3 in flight at the start of iteration i.
+  // Descriptors come from the LDS ring: thread 0 loads chunk c's in iteration c - 6 and
+  // publishes it at the start of iteration c - 5, before that iteration's loads, so the wait for
+  // it never covers the gathers issued after it (vector-memory waits are in issue order).
+  int32_t idsA[4], idsB[4];
   float4 rowA[4], rowB[4];
-  load_ids(d0, ids);
-  load_rows(ids, rowA);
-  load_ids(d1, ids);
-  convert(rowA, 0);
-  load_rows(ids, rowA);
-  load_ids(d2, ids);
-  load_rows(ids, rowB);
-  load_ids(d3, ids);
-  if (bt == 0) Ds[0] = d0;
-  __syncthreads();  // E(0) and Ds[0] complete (pairs with the producers' first wait)
+  int2 dload = make_int2(0, 0);  // thread 0: the descriptor of chunk i+5, loaded in iteration i-1
+  {
+    const int2 e0 = desc_of(0), e1 = desc_of(1), e2 = desc_of(2), e3 = desc_of(3);
+    if (bt == 0) {
+      Dq[0] = e0;
+      Dq[1] = e1;
+      Dq[2] = e2;
+      Dq[3] = e3;
+      Dq[4] = desc_of(4);
+      dload = desc_of(5);
+    }
+    load_ids(e0, idsA);
+    load_rows(idsA, rowA);
+    load_ids(e1, idsA);
+    convert(rowA, 0);
+    load_rows(idsA, rowA);
+    load_ids(e2, idsA);
+    load_rows(idsA, rowB);
+    load_ids(e3, idsA);
+  }
+  __syncthreads();  // E(0) and the ring complete (pairs with the producers' first wait)
 
   // Chunk c's H (the two accumulator chains h2) rounded to bf16 and staged in Hs[buf] for the
   // producers; its column sums over the chunk's positions go to Cs[buf].  Lane holds rows
@@ -399,18 +425,26 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
     }
   };
 
-  // One pipeline iteration; `cur` holds the rows of chunk i+1 and is refilled with i+3.
-  auto step = [&](int i, float4 (&cur)[4]) {
+  // One pipeline iteration; `cur` holds the rows of chunk i+1 and is refilled with i+3 from the
+  // ids in `use` (loaded the iteration before); `fill` receives the ids of chunk i+4.
+  // Vector-memory waits are in issue order, so the loads go out as ids first, rows last: the
+  // wait for this iteration's ids (next iteration, before its row loads) then does not cover
+  // the rows issued after them, and rows keep two iterations to arrive.
+  auto step = [&](int i, float4 (&cur)[4], int32_t (&use)[4], int32_t (&fill)[4]) {
     // E(i+1) and the gathers further ahead first: VALU work while the producer on this SIMD
     // runs its gate|up matrix instructions
-    int2 d5 = d4;
-    if (i + 1 < n) {
-      convert(cur, (i + 1) & 1);
-      load_rows(ids, cur);
-      load_ids(d4, ids);
-      d5 = desc_of(i + 5);
-      if (bt == 0) Ds[(i + 1) & 1] = d1;
+    // The loads go out on every iteration (past the last chunk they repeat it, and what they
+    // produce is not read), so that every path through the loop has the same vector-memory
+    // operations in the same order and the compiler's waits count exactly how many are younger.
+    if (bt == 0) {
+      Dq[(i + 5) & 7] = dload;  // loaded an iteration ago; visible to all after this iteration's barrier
+      dload = desc_of(i + 6);
     }
+    const int2 d4 = Dq[(i + 4) & 7], dprev = Dq[(i - 1) & 7];
+    load_ids(d4, fill);
+    __builtin_amdgcn_sched_barrier(0);  // ids before rows
+    convert(cur, (i + 1) & 1);
+    load_rows(use, cur);
     if (i >= 1 && i <= n) {
       // chunk i-1: down projection on the SiLU tile, while the producer runs its SiLU
       const int s = (dprev.y >> 8) / p.R;
@@ -420,6 +454,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
         for (int k = 0; k < kHid / 16; ++k) wd[k] = *reinterpret_cast<const V8*>(Wd + (int64_t)ncol * kHid + k * 16 + lk);
         bd = (p.bd + (int64_t)s * p.bd_gstride)[ncol];
         cur_s = s;
+        wait_vm_all();
       }
       const bf16* A = As[(i - 1) & 1];
       f32x16 hacc[2];
@@ -445,18 +480,12 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
       __builtin_amdgcn_sched_barrier(0);
       epilogue(hacc, dprev.y & 255, (i - 1) & 1);
     }
-    dprev = d0;
-    d0 = d1;
-    d1 = d2;
-    d2 = d3;
-    d3 = d4;
-    d4 = d5;
     __syncthreads();
   };
 #pragma unroll 1
   for (int i = 0; i <= n + 1; i += 2) {
-    step(i, rowA);
-    if (i + 1 <= n + 1) step(i + 1, rowB);
+    step(i, rowA, idsA, idsB);
+    if (i + 1 <= n + 1) step(i + 1, rowB, idsB, idsA);
   }
   if (bad) raise_flag(p.flag, ERRF_SEQ_ID_RANGE);
 }
