@@ -1074,6 +1074,12 @@ extern "C" cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value
         return fail(h, CVR_ERR_UNSUPPORTED, "the user block needs a DLRM spec with both sides, runs of 32 columns");
       h->opt_user_block = (int)value;
       break;
+    case CVR_OPT_HEADS_FUSED:
+      if (value < -1 || value > 1) return fail(h, CVR_ERR_ARG, "fused heads must be -1, 0 or 1");
+      if (value == 1 && (h->spec.model != CVR_MODEL_HYFORMER || !heads_fusable(h->spec.expert_dim, h->spec.head_hidden, h->spec.n_experts, h->spec.n_tasks)))
+        return fail(h, CVR_ERR_UNSUPPORTED, "fused heads need a CVR spec with expert and head widths of at most 256, at most 4 experts and 4 tasks");
+      h->opt_heads_fused = (int)value;
+      break;
     default: return fail(h, CVR_ERR_ARG, "unknown option");
   }
   h->graph.reset();  // a captured graph baked in the previous choice

@@ -383,6 +383,33 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     e = L(STAGE_PLE_GEMM, [&] { return launch_gemm(g, lowp, s); });
     if (e != hipSuccess) return e;
   }
+  if (m->opt_heads_fused != 0 && heads_fusable(ed, hh, E, K)) {
+    // the gate mixture, the heads' two Linears and the sigmoid in one launch
+    HeadsParams p{};
+    p.g.experts = (const float*)(ws + w.experts);
+    p.g.ld = ld;
+    p.g.n = n;
+    p.g.E = E;
+    p.g.K = K;
+    p.g.edim = ed;
+    p.g.gate0 = E * ed;
+    for (int k = 0; k < K; ++k) {
+      p.g.goff[k] = goff[k];
+      p.g.emask[k] = m->task_mask[k];
+      p.b2[k] = (const float*)m->wptr("head." + S_(k) + ".fc2.bias");
+    }
+    p.W1 = (const __bf16*)m->wptr("head.0.fc1.weight");
+    p.w1_stride = group_stride(m, [](int i) { return "head." + S_(i) + ".fc1.weight"; }, K, 2);
+    p.b1 = (const float*)m->wptr("head.0.fc1.bias");
+    p.b1_stride = group_stride(m, [](int i) { return "head." + S_(i) + ".fc1.bias"; }, K, 4);
+    p.hdim = hh;
+    p.w2 = (const __bf16*)m->wptr("head.0.fc2.weight");
+    p.w2_stride = group_stride(m, [](int i) { return "head." + S_(i) + ".fc2.weight"; }, K, 2);
+    if (p.w1_stride < 0 || p.b1_stride < 0 || (K > 1 && p.w2_stride < 0)) return hipErrorInvalidValue;
+    p.logits = (float*)(ws + w.logits);
+    p.out = out;
+    return L(STAGE_HEAD_GEMM, [&] { return launch_heads(p, s); });
+  }
   {
     PleGateParams p{};
     p.experts = (const float*)(ws + w.experts);

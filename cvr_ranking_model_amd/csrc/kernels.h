@@ -350,6 +350,29 @@ struct HeadOutParams {
 };
 hipError_t launch_head_out(const HeadOutParams& p, hipStream_t st);
 
+// The gate mixtures, the heads' first Linear + ReLU and their output Linear + sigmoid in one
+// launch (32 candidates per block, the intermediate rows in LDS); the values of the three
+// separate kernels.  Needs edim and hdim multiples of 32 and at most kHeadsMaxDim, at most
+// kHeadsMaxExperts experts and kHeadsMaxTasks tasks.
+constexpr int kHeadsMaxDim = 256;
+constexpr int kHeadsMaxExperts = 4;
+constexpr int kHeadsMaxTasks = 4;
+struct HeadsParams {
+  PleGateParams g;              // task_in unused
+  const __bf16* W1;             // task k: W1 + k*w1_stride, [hdim][edim]
+  int64_t w1_stride;
+  const float* b1;              // task k: b1 + k*b1_stride, [hdim]
+  int64_t b1_stride;
+  int32_t hdim;
+  const __bf16* w2;             // task k: w2 + k*w2_stride, [hdim]
+  int64_t w2_stride;
+  const float* b2[kMaxTasks];
+  float* logits;                // [n][K]
+  float* out;                   // [n][K]
+};
+bool heads_fusable(int32_t edim, int32_t hdim, int32_t n_experts, int32_t n_tasks);
+hipError_t launch_heads(const HeadsParams& p, hipStream_t st);
+
 // ---------------------------------------------------------------- fill (input generator)
 hipError_t launch_fill_table(float* t, int64_t total, uint64_t seed, double step, hipStream_t st);
 

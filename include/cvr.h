@@ -279,8 +279,19 @@ cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures)
  *                           section 3.4.5).  -1 (default) and 0: off; 1: on (CVR_ERR_UNSUPPORTED
  *                           unless the spec has request-side and item-side features in runs of
  *                           multiples of 32 columns).
+ *   CVR_OPT_HEADS_FUSED     CVR: the PLE gate mixture, the heads' two Linears and the sigmoid in
+ *                           one launch (CVR article section 3.2.4), with the values of the
+ *                           three separate launches.  -1 (default) and 1: fused when expert_dim
+ *                           and head_hidden are at most 256, with at most 4 experts and 4 tasks
+ *                           (1 beyond that: CVR_ERR_UNSUPPORTED); 0: three launches.
  * Unknown options and values outside these ranges return CVR_ERR_ARG. */
-enum { CVR_OPT_DLRM_PASS_ROWS = 0, CVR_OPT_TOK_SHARE = 1, CVR_OPT_ATTN_MQ = 2, CVR_OPT_DLRM_USER_BLOCK = 3 };
+enum {
+  CVR_OPT_DLRM_PASS_ROWS = 0,
+  CVR_OPT_TOK_SHARE = 1,
+  CVR_OPT_ATTN_MQ = 2,
+  CVR_OPT_DLRM_USER_BLOCK = 3,
+  CVR_OPT_HEADS_FUSED = 4
+};
 cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value);
 
 /* Wait for the stream and report the device error flag of the last

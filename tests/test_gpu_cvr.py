@@ -314,6 +314,32 @@ def test_tokenizer_request_side_once(share):
     check_cvr(spec, m, b, "stress")
 
 
+@pytest.mark.parametrize("experts", [None, "task"])
+def test_heads_fused_equals_separate(experts):
+    """The gate mixture, head Linears and sigmoid in one launch against the three separate
+    launches: bit-identical logits and scores (the same arithmetic in the same order), on a
+    ragged batch whose size is not a multiple of the fused kernel's 32 rows; then against the
+    oracle.  With task-specific experts each task mixes its own expert and the shared ones."""
+    spec = synth.load_spec("c3")
+    if experts:
+        spec["ple_task_experts"] = [[0, 1], [0, 2]]
+    banner(f"c3 stress, fused heads against separate launches, experts {experts or 'shared'}")
+    m, _ = build_model(spec, "stress")
+    b = synth.make_batch(spec, cand_counts=[7, 0, 40, 1, 3, 22])
+    m.set_option(cv.CVR_OPT_HEADS_FUSED, 0)
+    _, o_sep, st = run(m, b)
+    assert st == cv.CVR_OK
+    n = int(o_sep.numel()) // spec["n_tasks"]
+    z_sep = m.export(cv.CVR_DBG_LOGITS, torch.float32, (n, spec["n_tasks"])).cpu().numpy()
+    s_sep = o_sep.cpu().numpy().copy()
+    m.set_option(cv.CVR_OPT_HEADS_FUSED, 1)
+    _, o_fus, st = run(m, b)
+    assert st == cv.CVR_OK
+    z_fus = m.export(cv.CVR_DBG_LOGITS, torch.float32, (n, spec["n_tasks"])).cpu().numpy()
+    assert np.array_equal(z_sep, z_fus) and np.array_equal(s_sep, o_fus.cpu().numpy())
+    check_cvr(spec, m, b, "stress")
+
+
 def test_ragged_multi_candidate():
     spec = synth.load_spec("c3")
     banner("c3 ragged: several candidates per request, empty and length-1 sequences, empty bags")
