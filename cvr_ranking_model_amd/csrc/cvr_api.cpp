@@ -410,6 +410,12 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t lp = 2;
   w.flag = take(256);
+  {
+    int64_t bags = 0;
+    for (int f = 0; f < s.n_features; ++f) bags += m->feats[f].side == CVR_SIDE_ITEM ? n : R;
+    w.expand_blocks = expand_blocks(n, bags, R, s.model == CVR_MODEL_HYFORMER ? s.n_seq : 0);
+    w.expand_err = take((size_t)w.expand_blocks * 4);
+  }
   w.cand_req = take((size_t)n * 4);
   w.x_req = take((size_t)R * m->ld_req * lp);
   w.x_item = take((size_t)n * m->ld_item * lp);
@@ -579,8 +585,6 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
   int32_t* flag = (int32_t*)(ws + w.flag);
   int64_t total_bags = 0;
   for (int f = 0; f < sp.n_features; ++f) total_bags += sp.features[f].side == CVR_SIDE_ITEM ? b->n_candidates : b->n_requests;
-  hipError_t e = L(STAGE_EXPAND, [&] { return launch_clear_flag(flag, s); });
-  if (e != hipSuccess) return e;
   ExpandParams ep{};
   ep.cand_offsets = b->cand_offsets;
   ep.R = b->n_requests;
@@ -593,8 +597,9 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
   ep.n_positions = b->n_positions;
   ep.cand_req = (int32_t*)(ws + w.cand_req);
   ep.flag = flag;
+  ep.block_err = (int32_t*)(ws + w.expand_err);
   ep.ids_capacity = bucket ? 1 : 0;
-  e = L(STAGE_EXPAND, [&] { return launch_expand(ep, s); });
+  hipError_t e = L(STAGE_EXPAND, [&] { return launch_expand(ep, w.expand_blocks, s); });
   if (e != hipSuccess) return e;
 
   GatherParams gp{};
@@ -1036,9 +1041,13 @@ extern "C" cvr_status cvr_sync_status(cvr_handle h, void* hip_stream) {
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("stream sync: ") + hipGetErrorString(e));
   if (!h->last_ws) return CVR_OK;
-  int32_t flag = 0;
-  e = hipMemcpy(&flag, h->last_ws + h->last_plan.flag, 4, hipMemcpyDeviceToHost);
+  // the status word and the expand launch's per-block words, which sit right after it
+  const WsPlan& lp = h->last_plan;
+  std::vector<int32_t> words((lp.expand_err - lp.flag) / 4 + (size_t)lp.expand_blocks);
+  e = hipMemcpy(words.data(), h->last_ws + lp.flag, words.size() * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(h, CVR_ERR_HIP, std::string("reading status: ") + hipGetErrorString(e));
+  int32_t flag = words[0];
+  for (int64_t b = 0; b < lp.expand_blocks; ++b) flag |= words[(lp.expand_err - lp.flag) / 4 + b];
   if (flag) {
     std::string why = "device check failed:";
     if (flag & ERRF_CAND_OFFSETS) why += " cand_offsets malformed;";

@@ -4,20 +4,20 @@
 
 namespace cvr {
 
-__global__ void clear_flag_kernel(int32_t* flag) {
-  if (threadIdx.x == 0) flag[0] = 0;
-}
-
-hipError_t launch_clear_flag(int32_t* flag, hipStream_t st) {
-  launch_k(clear_flag_kernel, dim3(1), dim3(64), 0, st, flag);
-  return hipGetLastError();
-}
-
 // One thread per index i over max(n, total_bags+1, S*(R+1), R+1):
 //  - i < n: cand_req[i] = the request owning candidate i (largest r with cand_offsets[r] <= i);
 //  - offsets checks: monotone, first 0, last equal to the declared totals.
-// Every read stays inside the arrays whatever their contents.
-__global__ void expand_kernel(ExpandParams p) {
+// Every read stays inside the arrays whatever their contents.  The call's status word starts
+// here: block 0 sets it to zero (no other kernel of the call has run yet, and none of this
+// launch writes it), and each block stores the OR of its own checks in its block_err word, so
+// the status read ORs the word and those of this launch.
+__global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
+  __shared__ int32_t block_bad;
+  if (threadIdx.x == 0) {
+    block_bad = 0;
+    if (blockIdx.x == 0) p.flag[0] = 0;
+  }
+  __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int32_t bad = 0;
   if (i < p.n) {
@@ -49,17 +49,23 @@ __global__ void expand_kernel(ExpandParams p) {
     if (v < 0 || v > p.n_positions) bad |= ERRF_SEQ_OFFSETS;
     if (i + 1 < (int64_t)p.S * (p.R + 1) && (int64_t)p.seq_offsets[i + 1] < v) bad |= ERRF_SEQ_OFFSETS;
   }
-  if (bad) raise_flag(p.flag, bad);
+  if (bad) atomicOr(&block_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) p.block_err[blockIdx.x] = block_bad;
 }
 
-hipError_t launch_expand(const ExpandParams& p, hipStream_t st) {
-  int64_t work = p.n;
-  if (p.total_bags + 1 > work) work = p.total_bags + 1;
-  if ((int64_t)p.R + 1 > work) work = (int64_t)p.R + 1;
-  if (p.seq_offsets && (int64_t)p.S * (p.R + 1) > work) work = (int64_t)p.S * (p.R + 1);
-  const int threads = 256;
-  const int64_t blocks = (work + threads - 1) / threads;
-  launch_k(expand_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, p);
+int64_t expand_blocks(int64_t n, int64_t total_bags, int64_t R, int64_t S) {
+  int64_t work = n;
+  if (total_bags + 1 > work) work = total_bags + 1;
+  if (R + 1 > work) work = R + 1;
+  if (S * (R + 1) > work) work = S * (R + 1);
+  return (work + 255) / 256;
+}
+
+hipError_t launch_expand(const ExpandParams& p, int64_t blocks, hipStream_t st) {
+  const int64_t need = expand_blocks(p.n, p.total_bags, p.R, p.seq_offsets ? p.S : 0);
+  if (blocks < need || blocks > INT32_MAX) return hipErrorInvalidValue;
+  launch_k(expand_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

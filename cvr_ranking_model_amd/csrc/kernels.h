@@ -52,11 +52,14 @@ struct ExpandParams {
   int32_t S;
   int64_t n_positions;
   int32_t* cand_req;            // [n] out
-  int32_t* flag;                // status word (cleared by this launch's first block before use)
+  int32_t* flag;                // status word: set to zero by block 0 (later kernels of the call raise into it)
+  int32_t* block_err;           // [blocks] out: each block's own check results (0 or ERRF_ bits)
   int32_t ids_capacity;         // 1: n_ids is a capacity, the last bag may end before it (bucket replay)
 };
-hipError_t launch_clear_flag(int32_t* flag, hipStream_t st);
-hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
+// Blocks of the expand launch for these sizes (one thread per index, 256 per block).
+int64_t expand_blocks(int64_t n, int64_t total_bags, int64_t R, int64_t S);
+// blocks: expand_blocks() of the batch (the block_err words the status read covers).
+hipError_t launch_expand(const ExpandParams& p, int64_t blocks, hipStream_t st);
 
 // ---------------------------------------------------------------- graph replay per batch bucket
 // Written by bucket_pad_kernel before each replay, read by the replayed graph's last kernel.

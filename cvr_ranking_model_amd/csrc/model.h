@@ -53,6 +53,8 @@ struct InputSeg {
 // Byte offsets of every buffer inside one call's workspace.
 struct WsPlan {
   size_t flag = 0, cand_req = 0, x_req = 0, x_item = 0, logits = 0, pooled = 0, pooled_bytes = 0;
+  size_t expand_err = 0;      // [expand_blocks] int32: the expand launch's per-block check results
+  int64_t expand_blocks = 0;
   size_t h[2] = {0, 0};
   size_t opart = 0;  // DLRM: output-layer partials of a fused last hidden layer
   size_t u_req = 0;  // DLRM with the user block once per request: [R][width 0] fp32
