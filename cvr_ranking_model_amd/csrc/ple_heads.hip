@@ -14,6 +14,8 @@
 // head_out_kernel (eight lanes per candidate and task): y = w2 . u + b2 with fp32
 //   accumulation and the fp32 sigmoid; writes out[c * n_tasks + k].
 // heads_kernel: the gate mixture, the head's first Linear and head_out in one launch.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -281,12 +283,17 @@ bool heads_fusable(int32_t edim, int32_t hdim, int32_t n_experts, int32_t n_task
 hipError_t launch_heads(const HeadsParams& p, hipStream_t st) {
   if (p.g.n <= 0) return hipSuccess;
   if (!heads_fusable(p.g.edim, p.hdim, p.g.E, p.g.K)) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)heads_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)heads_lds_bytes(kHeadsMaxTasks));
+  // the LDS limit is raised once per device (above the default for dynamic LDS)
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_done.load() & bit)) {
+    e = hipFuncSetAttribute((const void*)heads_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)heads_lds_bytes(kHeadsMaxTasks));
     if (e != hipSuccess) return e;
-    attr = true;
+    attr_done.fetch_or(bit);
   }
   launch_k(heads_kernel, dim3((unsigned)((p.g.n + kHeadsRows - 1) / kHeadsRows)), dim3(64 * kHeadsWaves),
            heads_lds_bytes(p.g.K), st, p);
