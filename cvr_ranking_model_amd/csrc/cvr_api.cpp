@@ -599,7 +599,17 @@ static hipError_t run_front(cvr_model* m, const cvr_batch* b, char* ws, const Ws
   ep.flag = flag;
   ep.block_err = (int32_t*)(ws + w.expand_err);
   ep.ids_capacity = bucket ? 1 : 0;
-  hipError_t e = L(STAGE_EXPAND, [&] { return launch_expand(ep, w.expand_blocks, s); });
+  hipError_t e;
+  if (sp.model == CVR_MODEL_HYFORMER && seq_plan_in_front(sp.n_seq, b->n_requests)) {
+    // the sequence chunk plan reads only the sequence offsets: it runs beside the expansion
+    const int64_t max_chunks = b->n_positions / kSeqChunk + (int64_t)sp.n_seq * b->n_requests;
+    if (max_chunks > INT32_MAX) return hipErrorInvalidValue;
+    PlanParams q{b->seq_offsets, b->n_requests, sp.n_seq, b->n_positions, (int32_t)max_chunks,
+                 (int32_t*)(ws + w.chunk_off), (int2*)(ws + w.chunk_desc)};
+    e = L(STAGE_EXPAND, [&] { return launch_front(ep, w.expand_blocks, q, s); });
+  } else {
+    e = L(STAGE_EXPAND, [&] { return launch_expand(ep, w.expand_blocks, s); });
+  }
   if (e != hipSuccess) return e;
 
   GatherParams gp{};

@@ -1,24 +1,24 @@
 // Batch expansion and validation (step A0/B0), weight conversion and the synthetic table fill.
+#include "chunk_plan.h"
 #include "device_common.h"
 #include "kernels.h"
 
 namespace cvr {
 
-// One thread per index i over max(n, total_bags+1, S*(R+1), R+1):
+// One thread per index i over max(n, total_bags+1, S*(R+1), R+1), 1024 per block:
 //  - i < n: cand_req[i] = the request owning candidate i (largest r with cand_offsets[r] <= i);
 //  - offsets checks: monotone, first 0, last equal to the declared totals.
 // Every read stays inside the arrays whatever their contents.  The call's status word starts
 // here: block 0 sets it to zero (no other kernel of the call has run yet, and none of this
 // launch writes it), and each block stores the OR of its own checks in its block_err word, so
 // the status read ORs the word and those of this launch.
-__global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
-  __shared__ int32_t block_bad;
+__device__ __forceinline__ void expand_block(const ExpandParams& p, int64_t b, int32_t* block_bad) {
   if (threadIdx.x == 0) {
-    block_bad = 0;
-    if (blockIdx.x == 0) p.flag[0] = 0;
+    *block_bad = 0;
+    if (b == 0) p.flag[0] = 0;
   }
   __syncthreads();
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = b * 1024 + threadIdx.x;
   int32_t bad = 0;
   if (i < p.n) {
     int lo = 0, hi = p.R - 1;
@@ -49,9 +49,25 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandParams p) {
     if (v < 0 || v > p.n_positions) bad |= ERRF_SEQ_OFFSETS;
     if (i + 1 < (int64_t)p.S * (p.R + 1) && (int64_t)p.seq_offsets[i + 1] < v) bad |= ERRF_SEQ_OFFSETS;
   }
-  if (bad) atomicOr(&block_bad, bad);
+  if (bad) atomicOr(block_bad, bad);
   __syncthreads();
-  if (threadIdx.x == 0) p.block_err[blockIdx.x] = block_bad;
+  if (threadIdx.x == 0) p.block_err[b] = *block_bad;
+}
+
+__global__ __launch_bounds__(1024) void expand_kernel(const ExpandParams p) {
+  __shared__ int32_t block_bad;
+  expand_block(p, blockIdx.x, &block_bad);
+}
+
+// Expansion and chunk plan side by side: blocks [0, nexp) expand, the rest plan (they read only
+// the sequence offsets, which no kernel of the call writes).  The plan's offset table sits in
+// dynamic LDS (S*R+1 entries).
+__global__ __launch_bounds__(1024) void front_kernel(const ExpandParams p, int32_t nexp, const PlanParams q) {
+  extern __shared__ int32_t plan_off[];
+  __shared__ int32_t block_bad;
+  __shared__ long long wsum[16];
+  if ((int)blockIdx.x < nexp) expand_block(p, blockIdx.x, &block_bad);
+  else chunk_plan_block(q, (int)blockIdx.x - nexp, (int)gridDim.x - nexp, plan_off, wsum);
 }
 
 int64_t expand_blocks(int64_t n, int64_t total_bags, int64_t R, int64_t S) {
@@ -59,13 +75,23 @@ int64_t expand_blocks(int64_t n, int64_t total_bags, int64_t R, int64_t S) {
   if (total_bags + 1 > work) work = total_bags + 1;
   if (R + 1 > work) work = R + 1;
   if (S * (R + 1) > work) work = S * (R + 1);
-  return (work + 255) / 256;
+  return (work + 1023) / 1024;
 }
 
 hipError_t launch_expand(const ExpandParams& p, int64_t blocks, hipStream_t st) {
   const int64_t need = expand_blocks(p.n, p.total_bags, p.R, p.seq_offsets ? p.S : 0);
   if (blocks < need || blocks > INT32_MAX) return hipErrorInvalidValue;
-  launch_k(expand_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  launch_k(expand_kernel, dim3((unsigned)blocks), dim3(1024), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_front(const ExpandParams& p, int64_t blocks, const PlanParams& q, hipStream_t st) {
+  const int64_t need = expand_blocks(p.n, p.total_bags, p.R, p.seq_offsets ? p.S : 0);
+  if (blocks < need || (int64_t)q.S * q.R > kPlanMaxSegs) return hipErrorInvalidValue;
+  const int64_t total = blocks + chunk_plan_blocks(q.max_chunks);
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  launch_k(front_kernel, dim3((unsigned)total), dim3(1024), (size_t)((int64_t)q.S * q.R + 1) * 4, st, p,
+           (int32_t)blocks, q);
   return hipGetLastError();
 }
 

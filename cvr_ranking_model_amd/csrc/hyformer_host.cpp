@@ -175,8 +175,10 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   // every segment adds at most one partial chunk; the workspace holds this many
   const int max_chunks = (int)(P / kSeqChunk) + S * R;
   int2* chunk_desc = (int2*)(ws + w.chunk_desc);
-  e = L(STAGE_SEQ_CHUNKS, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, chunk_desc, s); });
-  if (e != hipSuccess) return e;
+  if (!seq_plan_in_front(S, R)) {  // else the expand launch made the plan
+    e = L(STAGE_SEQ_CHUNKS, [&] { return launch_chunk_table(b->seq_offsets, R, S, P, chunk_off, chunk_desc, s); });
+    if (e != hipSuccess) return e;
+  }
   {
     SwigluParams p{};
     p.seq_offsets = b->seq_offsets;

@@ -56,10 +56,27 @@ struct ExpandParams {
   int32_t* block_err;           // [blocks] out: each block's own check results (0 or ERRF_ bits)
   int32_t ids_capacity;         // 1: n_ids is a capacity, the last bag may end before it (bucket replay)
 };
-// Blocks of the expand launch for these sizes (one thread per index, 256 per block).
+// Blocks of the expand launch for these sizes (one thread per index, 1024 per block).
 int64_t expand_blocks(int64_t n, int64_t total_bags, int64_t R, int64_t S);
 // blocks: expand_blocks() of the batch (the block_err words the status read covers).
 hipError_t launch_expand(const ExpandParams& p, int64_t blocks, hipStream_t st);
+
+// The sequence chunk plan (chunk_plan.h): segment chunk offsets [S*R+1] and chunk descriptors.
+struct PlanParams {
+  const int32_t* seq_offsets;   // [S][R+1]
+  int32_t R, S;
+  int64_t n_positions;
+  int32_t max_chunks;           // n_positions / 32 + S * R: what the workspace holds
+  int32_t* chunk_off;           // [S*R+1] out
+  int2* desc;                   // [max_chunks] out
+};
+constexpr int kPlanMaxSegs = 16000;  // segments whose offset table fits (with the rest) in 64 KB of LDS
+int64_t chunk_plan_blocks(int64_t max_chunks);  // about two chunks per thread, at most 256 blocks
+// The batch expansion and the chunk plan in one launch (the expand blocks first, then
+// chunk_plan_blocks plan blocks); needs S * R <= kPlanMaxSegs.
+hipError_t launch_front(const ExpandParams& p, int64_t expand_blocks, const PlanParams& plan, hipStream_t st);
+// Whether the CVR path makes its chunk plan in the expand launch (the table fits LDS).
+inline bool seq_plan_in_front(int64_t S, int64_t R) { return S * R <= kPlanMaxSegs; }
 
 // ---------------------------------------------------------------- graph replay per batch bucket
 // Written by bucket_pad_kernel before each replay, read by the replayed graph's last kernel.

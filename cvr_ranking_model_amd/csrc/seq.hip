@@ -18,20 +18,11 @@
 //      rounded to bf16, staged through LDS and stored as rows; the rounded values are summed
 //      per column over the chunk's positions for the mean pool (for a full chunk on the matrix
 //      unit, as a product with a matrix of ones).
+#include "chunk_plan.h"
 #include "device_common.h"
 #include "kernels.h"
 
 namespace cvr {
-
-// Positions of segment g = s * R + r, clamped to [0, n_positions] and non-decreasing.
-__device__ __forceinline__ void segment_range(const int32_t* __restrict__ seq_offsets, int R, int g, int64_t n_positions,
-                                              int64_t& a, int64_t& e) {
-  const int s = g / R, r = g % R;
-  a = seq_offsets[(int64_t)s * (R + 1) + r];
-  e = seq_offsets[(int64_t)s * (R + 1) + r + 1];
-  a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
-  e = e < a ? a : (e > n_positions ? n_positions : e);
-}
 
 // Exclusive scan of ceil(len / kSeqChunk) over the S*R segments (one block of 1024 threads):
 // thread t owns a run of consecutive segments; the run totals are scanned within each wave by
@@ -103,73 +94,16 @@ __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restri
   desc[c] = make_int2((int)p0, (lo << 8) | np);
 }
 
-// Both steps in one launch while the table fits in LDS: every block runs the scan above into LDS
-// (the offsets are few and sit in L2 after the first block reads them), block 0 writes the
-// table out for the kernels that follow, and each block then writes the descriptors of its
-// share of the chunks, searching the table in LDS.  The values are those of the two kernels.
-constexpr int kPlanMaxSegs = 16384;
-__global__ __launch_bounds__(1024) void chunk_plan_kernel(const int32_t* __restrict__ seq_offsets, int R, int S,
-                                                          int64_t n_positions, int32_t max_chunks,
-                                                          int32_t* __restrict__ chunk_off, int2* __restrict__ desc) {
+// Both steps in one launch while the table fits in LDS (chunk_plan_block).
+__global__ __launch_bounds__(1024) void chunk_plan_kernel(const PlanParams q) {
   __shared__ int32_t off[kPlanMaxSegs + 1];
   __shared__ long long wsum[16];
-  const int SR = S * R;
-  const int per = (SR + 1023) / 1024;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g0 = t * per;
-  long long local = 0;
-  for (int g = g0; g < g0 + per && g < SR; ++g) {
-    int64_t a, e;
-    segment_range(seq_offsets, R, g, n_positions, a, e);
-    local += (e - a + kSeqChunk - 1) / kSeqChunk;
-  }
-  long long incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const long long v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    long long x = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const long long v = __shfl_up(x, o);
-      if (lane >= o) x += v;
-    }
-    if (lane < 16) wsum[lane] = x;
-  }
-  __syncthreads();
-  long long run = (w > 0 ? wsum[w - 1] : 0) + incl - local;
-  for (int g = g0; g < g0 + per && g < SR; ++g) {
-    off[g] = (int32_t)(run < max_chunks ? run : max_chunks);
-    int64_t a, e;
-    segment_range(seq_offsets, R, g, n_positions, a, e);
-    run += (e - a + kSeqChunk - 1) / kSeqChunk;
-  }
-  if (t == 1023) off[SR] = (int32_t)(wsum[15] < max_chunks ? wsum[15] : max_chunks);
-  __syncthreads();
-  if (blockIdx.x == 0)
-    for (int g = t; g <= SR; g += 1024) chunk_off[g] = off[g];
-  const int total = off[SR];
-  const int share = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int c0 = (int)blockIdx.x * share;
-  const int c1 = c0 + share < total ? c0 + share : total;
-  for (int c = c0 + t; c < c1; c += 1024) {
-    int lo = 0, hi = SR;  // off[lo] <= c < off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= c) lo = mid;
-      else hi = mid;
-    }
-    int64_t a, e;
-    segment_range(seq_offsets, R, lo, n_positions, a, e);
-    const int64_t p0 = a + (int64_t)(c - off[lo]) * kSeqChunk;
-    const int64_t left = e - p0;
-    const int np = left > kSeqChunk ? kSeqChunk : (int)left;
-    desc[c] = make_int2((int)p0, (lo << 8) | np);
-  }
+  chunk_plan_block(q, blockIdx.x, gridDim.x, off, wsum);
+}
+
+int64_t chunk_plan_blocks(int64_t max_chunks) {
+  const int64_t b = (max_chunks + 2047) / 2048;
+  return b < 1 ? 1 : (b > 256 ? 256 : b);
 }
 
 hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t n_positions, int32_t* chunk_off,
@@ -178,11 +112,8 @@ hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t 
   const int64_t max_chunks = n_positions / kSeqChunk + (int64_t)S * R;
   if (max_chunks > INT32_MAX) return hipErrorInvalidValue;
   if ((int64_t)S * R <= kPlanMaxSegs) {
-    // about two chunks per thread, at most one block per CU
-    int64_t blocks = (max_chunks + 2047) / 2048;
-    blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
-    launch_k(chunk_plan_kernel, dim3((unsigned)blocks), dim3(1024), 0, st, seq_offsets, R, S, n_positions,
-             (int32_t)max_chunks, chunk_off, desc);
+    PlanParams q{seq_offsets, R, S, n_positions, (int32_t)max_chunks, chunk_off, desc};
+    launch_k(chunk_plan_kernel, dim3((unsigned)chunk_plan_blocks(max_chunks)), dim3(1024), 0, st, q);
     return hipGetLastError();
   }
   launch_k(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, (int32_t)max_chunks,
