@@ -94,13 +94,6 @@ __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restri
   desc[c] = make_int2((int)p0, (lo << 8) | np);
 }
 
-// Both steps in one launch while the table fits in LDS (chunk_plan_block).
-__global__ __launch_bounds__(1024) void chunk_plan_kernel(const PlanParams q) {
-  __shared__ int32_t off[kPlanMaxSegs + 1];
-  __shared__ long long wsum[16];
-  chunk_plan_block(q, blockIdx.x, gridDim.x, off, wsum);
-}
-
 int64_t chunk_plan_blocks(int64_t max_chunks) {
   const int64_t b = (max_chunks + 2047) / 2048;
   return b < 1 ? 1 : (b > 256 ? 256 : b);
@@ -111,11 +104,6 @@ hipError_t launch_chunk_table(const int32_t* seq_offsets, int R, int S, int64_t 
   // every segment adds at most one partial chunk; the workspace holds this many
   const int64_t max_chunks = n_positions / kSeqChunk + (int64_t)S * R;
   if (max_chunks > INT32_MAX) return hipErrorInvalidValue;
-  if ((int64_t)S * R <= kPlanMaxSegs) {
-    PlanParams q{seq_offsets, R, S, n_positions, (int32_t)max_chunks, chunk_off, desc};
-    launch_k(chunk_plan_kernel, dim3((unsigned)chunk_plan_blocks(max_chunks)), dim3(1024), 0, st, q);
-    return hipGetLastError();
-  }
   launch_k(chunk_table_kernel, dim3(1), dim3(1024), 0, st, seq_offsets, R, S, n_positions, (int32_t)max_chunks,
            chunk_off);
   hipError_t e = hipGetLastError();

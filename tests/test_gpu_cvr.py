@@ -278,6 +278,20 @@ def test_c4_two_layers_small(variant):
     check_cvr(spec, m, synth.make_batch(spec, requests=6), variant)
 
 
+def test_many_segments_plan_of_its_own():
+    """More sequence segments (3 x 5,400) than the expand launch's chunk plan takes: the plan
+    runs as its own scan and descriptor launches.  Short ragged sequences (0-40 positions)
+    with full, partial and empty chunks; against the oracle on three requests."""
+    spec = synth.load_spec("c3")
+    R = 5400
+    rng = np.random.default_rng(5400)
+    lens = [[int(x) for x in rng.integers(0, 41, R)] for _ in spec["seq"]["lengths"]]
+    lens[0][0], lens[1][2700], lens[2][5399] = 0, 32, 33
+    banner(f"c3 stress, {R} requests ({3 * R} segments), sequences of 0-40 positions")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec, requests=R, seq_lengths=lens), "stress", requests=[0, 2700, 5399])
+
+
 def test_one_user_many_candidates():
     spec = synth.load_spec("c3")
     banner("c3 1 user + 500 candidates: 2 requests x 500, sequences once per request, oracle on request 1")
