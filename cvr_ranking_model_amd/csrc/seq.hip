@@ -495,38 +495,66 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) 
   return hipGetLastError();
 }
 
-// Mean pool per segment: the chunk partials summed in eight interleaved chains (chunk c goes to
-// chain c % 8, each chain in chunk order), the chains added in chain order, divided by the length.
-// The order depends only on the segment's chunk count, so a request's pools do not depend on the
-// rest of the batch.  Lane t reads four columns of every eighth chunk (16-byte loads).
+// One wave per segment, four segments per block.  Lane l takes columns 4(l%32) .. +3 of chains
+// 4(l/32) .. +3 (chunk c of the segment in chain c % 8, each chain summed in chunk order from
+// zero), the four chains' next chunks in flight together; lane l then adds chains 0-3 in order
+// and chains 4-7, fetched from lane l+32, after them: the order depends only on the segment's
+// chunk count, so pools do not depend on the rest of the batch.
 __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ seq_offsets, int R, int S,
                                                        int64_t n_positions, int32_t max_chunks,
                                                        float* __restrict__ pool) {
-  constexpr int kChains = 8;
-  __shared__ float4 sm[kChains][kD / 4];
-  const int g = blockIdx.x;
-  const int t = threadIdx.x, q = t % (kD / 4), chain = t / (kD / 4);
+  const int lane = threadIdx.x & 63;
+  // the last sequence's segments (the longest) first
+  const int g = R * S - 1 - (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (g < 0) return;
+  const int q = lane & 31, h = lane >> 5;
   const int s = g / R, r = g % R;
   int64_t a = seq_offsets[(int64_t)s * (R + 1) + r], e = seq_offsets[(int64_t)s * (R + 1) + r + 1];
   a = a < 0 ? 0 : (a > n_positions ? n_positions : a);
   e = e < a ? a : (e > n_positions ? n_positions : e);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // chunk offsets past the workspace's chunk count come only from offsets the expand kernel flags
+  const int c_lo = chunk_off[g] < max_chunks ? chunk_off[g] : max_chunks;
   const int c_hi = chunk_off[g + 1] < max_chunks ? chunk_off[g + 1] : max_chunks;
-  for (int c = chunk_off[g] + chain; c < c_hi; c += kChains) {
-    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)c * kD + 4 * q);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  sm[chain][q] = acc;
-  __syncthreads();
-  if (chain == 0) {
+  float4 ch[4];
 #pragma unroll
-    for (int k = 1; k < kChains; ++k) {
-      const float4 v = sm[k][q];
+  for (int k = 0; k < 4; ++k) ch[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // four rounds of eight chunks at a time: sixteen loads in flight per lane
+  for (int c = c_lo + 4 * h; c < c_hi; c += 32) {
+    float4 v[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int cc = c + 8 * j + k;
+        v[j][k] = cc < c_hi ? *reinterpret_cast<const float4*>(part + (int64_t)cc * kD + 4 * q)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c + 8 * j + k < c_hi) {
+          ch[k].x += v[j][k].x;
+          ch[k].y += v[j][k].y;
+          ch[k].z += v[j][k].z;
+          ch[k].w += v[j][k].w;
+        }
+  }
+  // chains 4-7 from the upper half-wave
+  float4 up[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    up[k].x = __shfl(ch[k].x, q + 32);
+    up[k].y = __shfl(ch[k].y, q + 32);
+    up[k].z = __shfl(ch[k].z, q + 32);
+    up[k].w = __shfl(ch[k].w, q + 32);
+  }
+  if (h == 0) {
+    float4 acc = ch[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      const float4 v = k < 4 ? ch[k] : up[k - 4];
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -541,8 +569,8 @@ __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
                            int64_t n_positions, int32_t max_chunks, float* pool, hipStream_t st) {
   if (R * S <= 0) return hipSuccess;
-  launch_k(seq_pool_kernel, dim3(R * S), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S, n_positions, max_chunks,
-           pool);
+  launch_k(seq_pool_kernel, dim3((R * S + 3) / 4), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S, n_positions,
+           max_chunks, pool);
   return hipGetLastError();
 }
 
