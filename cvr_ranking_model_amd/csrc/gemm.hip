@@ -415,9 +415,9 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
   constexpr int WTM = 128, WTN = 64;       // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int kSlot = (BM + BN) * BK;   // elements per ring slot: BM A rows, then BN W rows
-  constexpr int kStagePitch = WTN * 2 + 8;  // bytes per staged output row (odd multiple of 8)
-  constexpr int RPS = 512 / (WTN * 2);      // staged rows written back per wave instruction
-  constexpr int LPR = WTN / 4;              // lanes per staged row on the way out (8 bytes each)
+  constexpr int kStagePitch = WTN * 2 + 16;  // bytes per staged output row (odd multiple of 16)
+  constexpr int RPS = 1024 / (WTN * 2);      // staged rows written back per wave instruction
+  constexpr int LPR = WTN / 8;               // lanes per staged row on the way out (16 bytes each)
   static_assert(BK == 32 || BK == 64, "slice width");
   static_assert(BM == 256, "two 128-row wave tiles along M");
   static_assert(TPA >= 1 && TPB >= 1 && BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "loader shape");
@@ -686,11 +686,11 @@ __global__ __launch_bounds__(BN / 64 * 128, MINB) void gemm_big_kernel(const Gem
 #pragma unroll
         for (int rr = 0; rr < SR / RPS; ++rr) {
           const int r = rr * RPS + lane / LPR;
-          const uint2 v = *reinterpret_cast<const uint2*>(stage + r * kStagePitch + (lane % LPR) * 8);
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kStagePitch + (lane % LPR) * 16);
           const int m = mrow0 + h * SR + r;
           if (m < p.M)
-            *reinterpret_cast<uint2*>(reinterpret_cast<T*>(p.C) + (int64_t)g * p.c_gstride + (int64_t)m * p.ldc +
-                                      ncol0 + 4 * (lane % LPR)) = v;
+            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.C) + (int64_t)g * p.c_gstride + (int64_t)m * p.ldc +
+                                      ncol0 + 8 * (lane % LPR)) = v;
         }
       }
     }
