@@ -292,6 +292,23 @@ def test_many_segments_plan_of_its_own():
     check_cvr(spec, m, synth.make_batch(spec, requests=R, seq_lengths=lens), "stress", requests=[0, 2700, 5399])
 
 
+def test_six_sequence_columns():
+    """Six sequence columns of widths 64 + 32 + 16 + 8 + 4 + 4 = 128 (two of them 4 wide, so a
+    position's row quarters straddle more column boundaries than the four-column specs have):
+    the encoder's gather against the oracle."""
+    spec = synth.load_spec("c3")
+    cols = spec["seq"]["columns"]
+    item, action, side = cols[0]["table"], cols[1]["table"], cols[3]["table"]
+    nt = len(spec["tables"])
+    tabs = list(spec["tables"]) + [dict(name=f"seq_w{w}_{i}", rows=16, dim=w) for i, w in enumerate([8, 4, 4])]
+    new_cols = [dict(table=item, ids="zipf"), dict(table=side, ids="zipf"), dict(table=action, ids="uniform")]
+    new_cols += [dict(table=nt + i, ids="uniform") for i in range(3)]
+    spec = dict(spec, tables=tabs, seq=dict(spec["seq"], columns=new_cols))
+    banner("c3 stress with six sequence columns (64, 32, 16, 8, 4, 4): 6 samples")
+    m, _ = build_model(spec, "stress")
+    check_cvr(spec, m, synth.make_batch(spec, requests=6), "stress")
+
+
 def test_one_user_many_candidates():
     spec = synth.load_spec("c3")
     banner("c3 1 user + 500 candidates: 2 requests x 500, sequences once per request, oracle on request 1")
