@@ -43,6 +43,7 @@ __device__ __forceinline__ void shfl_state(SoftState& dst, const SoftState& src,
   for (int j = 0; j < 16; ++j) dst.o[j] = __shfl_xor(src.o[j], mask);
 }
 
+template <bool kNT>
 __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
   const int c = blockIdx.x;
   const int s = p.S - 1 - (int)blockIdx.y;  // the last (longest) sequence first: a shorter tail
@@ -77,11 +78,17 @@ __global__ __launch_bounds__(256) void attention_kernel(const AttnParams p) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) st.o[j] = 0.f;
 
-  // the row of position t: columns 8*sub.. and 64 + 8*sub..
+  // the row of position t: columns 8*sub.. and 64 + 8*sub..  (kNT: nontemporal loads, for
+  // states that outsize the last-level cache)
   auto load_row = [&](int64_t t, bf16x8& h0, bf16x8& h1) {
-    const bf16* hp = p.H + t * 128 + sub * 8;
-    h0 = *reinterpret_cast<const bf16x8*>(hp);
-    h1 = *reinterpret_cast<const bf16x8*>(hp + 64);
+    const bf16x8* hp = reinterpret_cast<const bf16x8*>(p.H + t * 128 + sub * 8);
+    if constexpr (kNT) {
+      h0 = __builtin_nontemporal_load(hp);
+      h1 = __builtin_nontemporal_load(hp + 8);
+    } else {
+      h0 = hp[0];
+      h1 = hp[8];
+    }
   };
   int64_t t = a + wave * 8 + grp;
   bf16x8 n0, n1;
@@ -350,7 +357,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t st) {
     const int64_t tasks = (int64_t)((p.n + 31) / 32) * p.S;
     launch_k(attention_mq_kernel, dim3((unsigned)tasks), dim3(256), 0, st, p);
   } else {
-    launch_k(attention_kernel, dim3(p.n, p.S), dim3(256), 0, st, p);
+    if (p.nt)
+      launch_k(attention_kernel<true>, dim3(p.n, p.S), dim3(256), 0, st, p);
+    else
+      launch_k(attention_kernel<false>, dim3(p.n, p.S), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }

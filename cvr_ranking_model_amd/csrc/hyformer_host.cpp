@@ -213,12 +213,13 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     p.H = (__bf16*)(ws + w.hseq);
     p.part = (float*)(ws + w.pool_part);
     p.flag = flag;
+    p.nt = seq_states_stream(P);
     e = L(STAGE_SWIGLU, [&] { return launch_swiglu(p, max_chunks, s); });
     if (e != hipSuccess) return e;
   }
   e = L(STAGE_SEQ_POOL, [&] {
     return launch_seq_pool((const float*)(ws + w.pool_part), chunk_off, b->seq_offsets, R, S, P, max_chunks,
-                           (float*)(ws + w.seq_pool), s);
+                           (float*)(ws + w.seq_pool), seq_states_stream(P), s);
   });
   if (e != hipSuccess) return e;
 
@@ -267,6 +268,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       a.T = T;
       a.N = N;
       a.mq = m->opt_attn_mq < 0 ? attention_many_candidates(n, R) : m->opt_attn_mq != 0;
+      a.nt = seq_states_stream(P);
       e = L(STAGE_ATTENTION, [&] { return launch_attention(a, s); });
       if (e != hipSuccess) return e;
     }

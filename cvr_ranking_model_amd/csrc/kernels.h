@@ -281,10 +281,17 @@ struct SwigluParams {
   __bf16* H;                    // [n_positions][128]
   float* part;                  // [chunks][128] column sums
   int32_t* flag;
+  int32_t nt;                   // 1: H and the partials leave as nontemporal stores (seq_states_stream)
 };
 hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st);
+// Encoded states that outsize the last-level cache (256 MB on MI355X) are written, and read by the
+// pool and the per-candidate attention, with nontemporal hints: they cannot stay cached between
+// the launches anyway, and a streaming read runs at about 7.0 TB/s with the hint against 6.3
+// without.  Smaller ones are kept cacheable, since the attention then finds them in that cache.
+constexpr int64_t kStateStreamBytes = 256LL << 20;
+inline bool seq_states_stream(int64_t n_positions) { return n_positions * 128 * 2 >= kStateStreamBytes; }
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
-                           int64_t n_positions, int32_t max_chunks, float* pool, hipStream_t st);
+                           int64_t n_positions, int32_t max_chunks, float* pool, bool nt, hipStream_t st);
 
 // ---------------------------------------------------------------- attention (B7)
 struct AttnParams {
@@ -299,6 +306,7 @@ struct AttnParams {
   float* Y;                     // [n][T][128]: writes token N+s
   int32_t T, N;
   int32_t mq;                   // 1: MFMA products per request (attention_mq_kernel), 0: per candidate
+  int32_t nt;                   // per candidate: 1 reads H with nontemporal loads (seq_states_stream)
 };
 hipError_t launch_attention(const AttnParams& p, hipStream_t st);
 // Default choice of the MFMA form: requests carry 16 or more candidates on average.

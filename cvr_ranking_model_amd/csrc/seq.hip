@@ -177,6 +177,7 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
     int cur_s = -1;
     int2 dm1 = make_int2(0, 0), dm2 = make_int2(0, 0);  // descriptors of chunks i-1, i-2
     // chunk i-2 out: 32 rows x 128 columns of H (16 bytes per thread, twice) and partials
+    // (nontemporal stores when the states outsize the last-level cache)
     auto store_out = [&](int i) {
       const int c = c_begin + i - 2;
       const int np = dm2.y & 255;
@@ -184,11 +185,17 @@ __global__ __launch_bounds__(512, 1) void swiglu_kernel(const SwigluParams p) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int r = (tid >> 4) + 16 * q, ch = tid & 15;
-        if (r < np)
-          *reinterpret_cast<V8*>(p.H + ((int64_t)dm2.x + r) * kD + ch * 8) =
-              *reinterpret_cast<const V8*>(&hsrc[r * kEPitch + ch * 8]);
+        if (r < np) {
+          const V8 v = *reinterpret_cast<const V8*>(&hsrc[r * kEPitch + ch * 8]);
+          V8* dst = reinterpret_cast<V8*>(p.H + ((int64_t)dm2.x + r) * kD + ch * 8);
+          if (p.nt) __builtin_nontemporal_store(v, dst);
+          else *dst = v;
+        }
       }
-      if (tid < kD) p.part[(int64_t)c * kD + tid] = Cs[i & 1][tid];
+      if (tid < kD) {
+        if (p.nt) __builtin_nontemporal_store(Cs[i & 1][tid], p.part + (int64_t)c * kD + tid);
+        else p.part[(int64_t)c * kD + tid] = Cs[i & 1][tid];
+      }
     };
     __syncthreads();  // E(0) and the first descriptors are in place
 #pragma unroll 1
@@ -500,6 +507,7 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st) 
 // zero), the four chains' next chunks in flight together; lane l then adds chains 0-3 in order
 // and chains 4-7, fetched from lane l+32, after them: the order depends only on the segment's
 // chunk count, so pools do not depend on the rest of the batch.
+template <bool kNT>
 __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ seq_offsets, int R, int S,
                                                        int64_t n_positions, int32_t max_chunks,
@@ -527,8 +535,13 @@ __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int cc = c + 8 * j + k;
-        v[j][k] = cc < c_hi ? *reinterpret_cast<const float4*>(part + (int64_t)cc * kD + 4 * q)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (cc < c_hi) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(part + (int64_t)cc * kD + 4 * q);
+          if constexpr (kNT) x = __builtin_nontemporal_load(src);
+          else x = *src;
+        }
+        v[j][k] = make_float4(x[0], x[1], x[2], x[3]);
       }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -567,10 +580,14 @@ __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__
 }
 
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
-                           int64_t n_positions, int32_t max_chunks, float* pool, hipStream_t st) {
+                           int64_t n_positions, int32_t max_chunks, float* pool, bool nt, hipStream_t st) {
   if (R * S <= 0) return hipSuccess;
-  launch_k(seq_pool_kernel, dim3((R * S + 3) / 4), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S, n_positions,
-           max_chunks, pool);
+  if (nt)
+    launch_k(seq_pool_kernel<true>, dim3((R * S + 3) / 4), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S,
+             n_positions, max_chunks, pool);
+  else
+    launch_k(seq_pool_kernel<false>, dim3((R * S + 3) / 4), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S,
+             n_positions, max_chunks, pool);
   return hipGetLastError();
 }
 

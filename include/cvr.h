@@ -395,9 +395,10 @@ cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed
  * dropped; the value means nothing else.  Both enqueue one kernel of
  * `blocks` blocks of 256 threads (1 <= blocks <= 2^20) on hip_stream and
  * return CVR_ERR_ARG on a null pointer or a size outside the stated range.
+ * Both load with the nontemporal hint (the faster form for data read once).
  * cvr_probe_stream_read: reads `bytes` (a multiple of 16) of device memory
  *   at src (16-byte aligned) once, front to back, 16 bytes per lane and
- *   four loads in flight per lane -- the access pattern of the cross-
+ *   eight loads in flight per lane -- the access pattern of the cross-
  *   attention over encoded states (CVR article, section 3.2.3).
  * cvr_probe_row_read: for each of the n_ids int32 ids (device), reads the
  *   whole row of row_bytes (64, 128 or 256) of the device table at table
