@@ -434,7 +434,8 @@ def read_ceilings(reps=10):
                    gather: fp32 rows of 32 or 64 columns, tables of 1.28 GB and 25.6 GB), 8M
                    ids per launch for 128-byte rows and 4M for 256-byte rows.
     Bytes counted: the buffer, or rows plus the 4-byte ids.  Each shape is timed over `reps`
-    launches (HIP events on the launching stream) at several grid sizes; the best is the ceiling."""
+    launches (HIP events on the launching stream) at several grid sizes, with plain loads and
+    with nontemporal ones; the best is the ceiling ("nt" in "best" marks the hinted form)."""
     import torch
     from cvr_ranking_model_amd import cvr as cv
     C = cv.C
@@ -457,13 +458,14 @@ def read_ceilings(reps=10):
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sweep = {}
-    for blocks in [4096, 16384, 65536, 262144]:
-        ms = timed(lambda: cv.cvr_probe_stream_read(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
-                                                    blocks, C.c_void_p(st.cuda_stream)))
-        sweep[blocks] = round(nbytes / ms / 1e6, 1)
+    for nt in (0, 1):
+        for blocks in [4096, 16384, 65536, 262144]:
+            ms = timed(lambda: cv.cvr_probe_stream_read(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(sink.data_ptr()),
+                                                        blocks, C.c_void_p(st.cuda_stream), nontemporal=nt))
+            sweep[f"{blocks}{'nt' if nt else ''}"] = round(nbytes / ms / 1e6, 1)
     best = max(sweep, key=sweep.get)
     out["stream"] = {"GB/s": sweep[best], "frac": round(sweep[best] / HBM_PEAK_GBS, 4), "bytes": nbytes,
-                     "blocks": best, "sweep_GB/s": sweep}
+                     "best": best, "sweep_GB/s": sweep}
     del buf
     torch.cuda.empty_cache()
     gen = torch.Generator(device="cuda")
@@ -477,16 +479,17 @@ def read_ceilings(reps=10):
             ids = torch.randint(0, n_rows, (n_ids,), generator=gen, device="cuda", dtype=torch.int32)
             moved = n_ids * (row_bytes + 4)
             sweep = {}
-            for blocks in [2048, 8192, 32768]:
-                ms = timed(lambda: cv.cvr_probe_row_read(C.c_void_p(table.data_ptr()), n_rows, row_bytes,
-                                                         C.c_void_p(ids.data_ptr()), n_ids,
-                                                         C.c_void_p(sink.data_ptr()), blocks,
-                                                         C.c_void_p(st.cuda_stream)))
-                sweep[blocks] = round(moved / ms / 1e6, 1)
+            for nt in (0, 1):
+                for blocks in [2048, 8192, 32768]:
+                    ms = timed(lambda: cv.cvr_probe_row_read(C.c_void_p(table.data_ptr()), n_rows, row_bytes,
+                                                             C.c_void_p(ids.data_ptr()), n_ids,
+                                                             C.c_void_p(sink.data_ptr()), blocks,
+                                                             C.c_void_p(st.cuda_stream), nontemporal=nt))
+                    sweep[f"{blocks}{'nt' if nt else ''}"] = round(moved / ms / 1e6, 1)
             best = max(sweep, key=sweep.get)
             out[f"rows_{row_bytes}B_{foot / 1e9:g}GB"] = {
                 "GB/s": sweep[best], "frac": round(sweep[best] / HBM_PEAK_GBS, 4), "bytes": moved,
-                "n_ids": n_ids, "blocks": best, "sweep_GB/s": sweep}
+                "n_ids": n_ids, "best": best, "sweep_GB/s": sweep}
             del table, ids
             torch.cuda.empty_cache()
     torch.cuda.synchronize()

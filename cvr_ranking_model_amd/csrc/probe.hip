@@ -6,11 +6,11 @@
 //   row_read_kernel     reads whole rows of a table at given ids (the access pattern of the
 //                       embedding gather: the CTR article, section 二, keeps the hot embedding rows in
 //                       HBM and reads them directly from the kernel).
-// Each block writes one 32-bit xor of what it read, so the compiler cannot drop a load.  Both use
-// nontemporal loads, the fastest form measured for data read once (a plain streaming read of
-// 4 GiB runs at about 6.3 TB/s, with the hint at about 7.0; uniform random 128- and 256-byte
-// rows of a 4 GiB table about 7% faster with the hint).  They are measurement tools, not part of
-// scoring.
+// Each block writes one 32-bit xor of what it read, so the compiler cannot drop a load.  Both
+// load plainly or with the nontemporal hint (NT), which is the faster form for data that cannot
+// stay cached (a streaming read of 4 GiB: about 6.3 TB/s plain, 7.0 with the hint) and the
+// slower one for a table part of which the last-level cache holds.  They are measurement tools,
+// not part of scoring.
 #include "../../include/cvr.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -38,6 +38,7 @@ __device__ __forceinline__ void block_xor_store(uint32_t x, uint32_t* sink) {
 
 // n16: number of 16-byte vectors.  Each lane takes kStreamUnroll vectors a block-width apart per
 // step, so every load instruction of a wave covers 1 KiB of consecutive bytes.
+template <bool NT>
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                                    uint32_t* __restrict__ sink) {
   const int64_t stride = (int64_t)gridDim.x * kProbeThreads * kStreamUnroll;
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4*
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) {
       const int64_t i = base + (int64_t)u * kProbeThreads;
-      v[u] = i < n16 ? __builtin_nontemporal_load(&src[i]) : u32x4{0, 0, 0, 0};
+      v[u] = u32x4{0, 0, 0, 0};
+      if (i < n16) v[u] = NT ? __builtin_nontemporal_load(&src[i]) : src[i];
     }
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) x ^= fold(v[u]);
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4*
 
 // LPR lanes read one row of LPR * 16 bytes; a group keeps kRowUnroll rows in flight.  An id
 // outside [0, n_rows) reads row 0 (the probe takes no error path).
-template <int LPR>
+template <int LPR, bool NT>
 __global__ __launch_bounds__(kProbeThreads) void row_read_kernel(const u32x4* __restrict__ table, int64_t n_rows,
                                                                 const int32_t* __restrict__ ids, int64_t n_ids,
                                                                 uint32_t* __restrict__ sink) {
@@ -77,8 +79,10 @@ __global__ __launch_bounds__(kProbeThreads) void row_read_kernel(const u32x4* __
     }
     u32x4 v[kRowUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-      v[u] = row[u] >= 0 ? __builtin_nontemporal_load(&table[row[u] * LPR + lane]) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < kRowUnroll; ++u) {
+      v[u] = u32x4{0, 0, 0, 0};
+      if (row[u] >= 0) v[u] = NT ? __builtin_nontemporal_load(&table[row[u] * LPR + lane]) : table[row[u] * LPR + lane];
+    }
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) x ^= fold(v[u]);
   }
@@ -88,28 +92,39 @@ __global__ __launch_bounds__(kProbeThreads) void row_read_kernel(const u32x4* __
 }  // namespace cvr
 
 extern "C" cvr_status cvr_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks,
-                                            void* hip_stream) {
+                                            int32_t nontemporal, void* hip_stream) {
   if (!src || !sink) return cvr::fail(nullptr, CVR_ERR_ARG, "null pointer");
   if (((uintptr_t)src & 15) || bytes < 0 || (bytes & 15)) return cvr::fail(nullptr, CVR_ERR_ARG, "src must be 16-byte aligned, bytes a multiple of 16");
   if (blocks < 1 || blocks > (1 << 20)) return cvr::fail(nullptr, CVR_ERR_ARG, "blocks outside [1, 2^20]");
-  cvr::launch_k(cvr::stream_read_kernel, dim3(blocks), dim3(cvr::kProbeThreads), 0, (hipStream_t)hip_stream,
-                (const u32x4*)src, bytes / 16, sink);
+  if (nontemporal != 0 && nontemporal != 1) return cvr::fail(nullptr, CVR_ERR_ARG, "nontemporal must be 0 or 1");
+  if (nontemporal)
+    cvr::launch_k(cvr::stream_read_kernel<true>, dim3(blocks), dim3(cvr::kProbeThreads), 0, (hipStream_t)hip_stream,
+                  (const u32x4*)src, bytes / 16, sink);
+  else
+    cvr::launch_k(cvr::stream_read_kernel<false>, dim3(blocks), dim3(cvr::kProbeThreads), 0, (hipStream_t)hip_stream,
+                  (const u32x4*)src, bytes / 16, sink);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? CVR_OK : cvr::fail(nullptr, CVR_ERR_HIP, hipGetErrorString(e));
 }
 
 extern "C" cvr_status cvr_probe_row_read(const void* table, int64_t n_rows, int32_t row_bytes, const int32_t* ids,
-                                         int64_t n_ids, uint32_t* sink, int32_t blocks, void* hip_stream) {
+                                         int64_t n_ids, uint32_t* sink, int32_t blocks, int32_t nontemporal,
+                                         void* hip_stream) {
   if (!table || !ids || !sink) return cvr::fail(nullptr, CVR_ERR_ARG, "null pointer");
   if (((uintptr_t)table & 15) || n_rows < 1 || n_ids < 0) return cvr::fail(nullptr, CVR_ERR_ARG, "bad table or sizes");
   if (blocks < 1 || blocks > (1 << 20)) return cvr::fail(nullptr, CVR_ERR_ARG, "blocks outside [1, 2^20]");
+  if (nontemporal != 0 && nontemporal != 1) return cvr::fail(nullptr, CVR_ERR_ARG, "nontemporal must be 0 or 1");
   const hipStream_t st = (hipStream_t)hip_stream;
   const dim3 grid(blocks), block(cvr::kProbeThreads);
   const u32x4* t = (const u32x4*)table;
-  switch (row_bytes) {
-    case 64: cvr::launch_k(cvr::row_read_kernel<4>, grid, block, 0, st, t, n_rows, ids, n_ids, sink); break;
-    case 128: cvr::launch_k(cvr::row_read_kernel<8>, grid, block, 0, st, t, n_rows, ids, n_ids, sink); break;
-    case 256: cvr::launch_k(cvr::row_read_kernel<16>, grid, block, 0, st, t, n_rows, ids, n_ids, sink); break;
+  auto go = [&](auto k) { cvr::launch_k(k, grid, block, 0, st, t, n_rows, ids, n_ids, sink); };
+  switch (row_bytes * 2 + nontemporal) {
+    case 128: go(cvr::row_read_kernel<4, false>); break;
+    case 129: go(cvr::row_read_kernel<4, true>); break;
+    case 256: go(cvr::row_read_kernel<8, false>); break;
+    case 257: go(cvr::row_read_kernel<8, true>); break;
+    case 512: go(cvr::row_read_kernel<16, false>); break;
+    case 513: go(cvr::row_read_kernel<16, true>); break;
     default: return cvr::fail(nullptr, CVR_ERR_ARG, "row_bytes must be 64, 128 or 256");
   }
   const hipError_t e = hipGetLastError();

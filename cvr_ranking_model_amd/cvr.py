@@ -82,9 +82,9 @@ _PROTOS = {
     "cvr_cache_attach": (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "cvr_cache_stats": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int64), C.c_void_p]),
     "cvr_cache_export": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_void_p]),
-    "cvr_probe_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_void_p]),
+    "cvr_probe_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "cvr_probe_row_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p, C.c_int32,
-                                     C.c_void_p]),
+                                     C.c_int32, C.c_void_p]),
     "cvr_last_error": (C.c_char_p, [C.c_void_p]),
     "cvr_status_string": (C.c_char_p, [C.c_int]),
     "cvr_destroy": (None, [C.c_void_p]),
@@ -234,12 +234,12 @@ def cvr_fill_table(ptr, rows, dim, seed, halfwidth, stream):
     _check(lib().cvr_fill_table(ptr, rows, dim, C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), halfwidth, stream))
 
 
-def cvr_probe_stream_read(src, nbytes, sink, blocks, stream):
-    _check(lib().cvr_probe_stream_read(src, nbytes, sink, blocks, stream))
+def cvr_probe_stream_read(src, nbytes, sink, blocks, stream, nontemporal=0):
+    _check(lib().cvr_probe_stream_read(src, nbytes, sink, blocks, nontemporal, stream))
 
 
-def cvr_probe_row_read(table, n_rows, row_bytes, ids, n_ids, sink, blocks, stream):
-    _check(lib().cvr_probe_row_read(table, n_rows, row_bytes, ids, n_ids, sink, blocks, stream))
+def cvr_probe_row_read(table, n_rows, row_bytes, ids, n_ids, sink, blocks, stream, nontemporal=0):
+    _check(lib().cvr_probe_row_read(table, n_rows, row_bytes, ids, n_ids, sink, blocks, nontemporal, stream))
 
 
 def cvr_destroy(h):

@@ -395,7 +395,9 @@ cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed
  * dropped; the value means nothing else.  Both enqueue one kernel of
  * `blocks` blocks of 256 threads (1 <= blocks <= 2^20) on hip_stream and
  * return CVR_ERR_ARG on a null pointer or a size outside the stated range.
- * Both load with the nontemporal hint (the faster form for data read once).
+ * nontemporal: 0 loads plainly, 1 with the nontemporal hint (faster for data
+ * that cannot stay cached, slower where the last-level cache holds part of
+ * it); other values are CVR_ERR_ARG.
  * cvr_probe_stream_read: reads `bytes` (a multiple of 16) of device memory
  *   at src (16-byte aligned) once, front to back, 16 bytes per lane and
  *   eight loads in flight per lane -- the access pattern of the cross-
@@ -406,9 +408,10 @@ cvr_status cvr_fill_table(float* table, int64_t rows, int32_t dim, uint64_t seed
  *   in flight per lane group -- the access pattern of the embedding gather
  *   over HBM-resident rows (CTR article, section 二).  An id outside
  *   [0, n_rows) reads row 0. */
-cvr_status cvr_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, void* hip_stream);
+cvr_status cvr_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks, int32_t nontemporal,
+                                 void* hip_stream);
 cvr_status cvr_probe_row_read(const void* table, int64_t n_rows, int32_t row_bytes, const int32_t* ids,
-                              int64_t n_ids, uint32_t* sink, int32_t blocks, void* hip_stream);
+                              int64_t n_ids, uint32_t* sink, int32_t blocks, int32_t nontemporal, void* hip_stream);
 
 const char* cvr_last_error(cvr_handle h);
 const char* cvr_status_string(cvr_status s);

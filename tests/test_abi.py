@@ -172,7 +172,8 @@ def test_cache_state_bytes_host_checks():
 
 def test_probe_argument_checks():
     """The bandwidth probes refuse null pointers, misaligned or ragged sizes, grids outside
-    [1, 2^20] and row widths other than 64/128/256 bytes before any device work."""
+    [1, 2^20], row widths other than 64/128/256 bytes and load forms other than 0/1 before any
+    device work."""
     import ctypes as C
     fake = C.c_void_p(1 << 20)    # aligned non-null stand-in; never dereferenced on these paths
     cases = [
@@ -187,6 +188,8 @@ def test_probe_argument_checks():
         lambda: cv.cvr_probe_row_read(None, 100, 128, fake, 10, fake, 64, None),
         lambda: cv.cvr_probe_row_read(fake, 100, 128, fake, -1, fake, 64, None),
         lambda: cv.cvr_probe_row_read(fake, 100, 128, fake, 10, fake, 0, None),
+        lambda: cv.cvr_probe_stream_read(fake, 1024, fake, 64, None, nontemporal=2),
+        lambda: cv.cvr_probe_row_read(fake, 100, 128, fake, 10, fake, 64, None, nontemporal=-1),
     ]
     for call in cases:
         with pytest.raises(cv.CvrError) as e:
