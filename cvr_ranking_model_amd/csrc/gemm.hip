@@ -29,7 +29,7 @@ namespace cvr {
 // so LDS latency overlaps them.  A-segment boundaries fall on slice boundaries, so each
 // slice reads one segment: per-thread row pointers are rebuilt only when the loop enters a
 // new segment (the row map is read there, not in the steady state).  AF32 selects fp32 A
-// sources, rounded to the low-precision type as they are loaded.
+// sources, rounded to the low-precision type as they move from registers to LDS.
 template <typename T, int BM, int BN, int WGM, int WGN, bool AF32, int kBK = 32>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   typedef typename Lowp<T>::vec8 V8;
@@ -108,24 +108,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     }
   };
 
-  // Two register staging sets: the slice two steps ahead is in flight while the next one
-  // waits in registers for its turn in LDS, so each global load has two slices of MFMA work
-  // to complete.
-  u32x4 ra[2][AQ], rb[2][BQ];
+  // NSET register staging sets: the slices up to NSET steps ahead are in flight while the next
+  // one waits in registers for its turn in LDS, so each global load has NSET slices of MFMA
+  // work to complete.  Three sets for the small tiles, whose short slices (and few waves per
+  // CU) leave the loads too little time otherwise (C3, 512 samples: step -2.5%); two for
+  // 128 x 128, where a third set costs occupancy and gained nothing.  An fp32 A chunk stays
+  // fp32 in its set (rf) and is rounded on its way to LDS: rounding at the load would wait for
+  // the load there.
+  constexpr int NSET = BM * BN <= 64 * 128 ? 3 : 2;
+  u32x4 ra[NSET][AQ], rb[NSET][BQ];
+  f32x4 rf[NSET][AQ][2];
   auto load_slice = [&](int k0, int set) {
     if (k0 >= seg_end) enter_segment(k0);
     const int64_t off = (int64_t)((k0 - seg_kb) >> 3) * seg_kstride;
 #pragma unroll
     for (int i = 0; i < AQ; ++i) {
       if constexpr (AF32) {
-        const float4* src = reinterpret_cast<const float4*>(aptr[i] + off);
-        const float4 x0 = src[0], x1 = src[1];
-        V8 v;
-        v[0] = Lowp<T>::from_f32(x0.x); v[1] = Lowp<T>::from_f32(x0.y);
-        v[2] = Lowp<T>::from_f32(x0.z); v[3] = Lowp<T>::from_f32(x0.w);
-        v[4] = Lowp<T>::from_f32(x1.x); v[5] = Lowp<T>::from_f32(x1.y);
-        v[6] = Lowp<T>::from_f32(x1.z); v[7] = Lowp<T>::from_f32(x1.w);
-        ra[set][i] = *reinterpret_cast<const u32x4*>(&v);
+        const f32x4* src = reinterpret_cast<const f32x4*>(aptr[i] + off);
+        rf[set][i][0] = src[0];
+        rf[set][i][1] = src[1];
       } else {
         ra[set][i] = *reinterpret_cast<const u32x4*>(aptr[i] + off);
       }
@@ -139,7 +140,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
       const int q = tid + i * 256;
       const int r = q / KC;
       const int c = kSwz ? ((q % KC) ^ ((r >> 1) & 3)) : (q % KC);
-      *reinterpret_cast<u32x4*>(As(buf) + r * kPitch + c * 8) = ra[set][i];
+      if constexpr (AF32) {
+        V8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = Lowp<T>::from_f32(rf[set][i][0][e]);
+          v[4 + e] = Lowp<T>::from_f32(rf[set][i][1][e]);
+        }
+        *reinterpret_cast<V8*>(As(buf) + r * kPitch + c * 8) = v;
+      } else {
+        *reinterpret_cast<u32x4*>(As(buf) + r * kPitch + c * 8) = ra[set][i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -190,30 +201,39 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = Lowp<T>::mfma32(a[cur][i], b[cur][j], acc[i][j]);
     }
   };
-  // One pipelined step: slice kt+2 (clamped to the last slice) loads into register set SET —
-  // a compile-time index and an unconditional load, so the loads stay in flight and the
-  // wait before the LDS store covers only the older set — while MFMAs run on buffer kt&1;
-  // then slice kt+1 moves from the other set into the other buffer.  Past the last slice the
-  // loads repeat it and land in a buffer that is not read again.
+  // One pipelined step: slice kt+NSET (clamped to the last slice) loads into register set
+  // SET = kt % NSET -- a compile-time index and an unconditional load, so the loads stay in
+  // flight and the wait before the LDS store covers only the oldest set -- while MFMAs run on
+  // buffer kt&1; then slice kt+1 moves from its set into the other buffer.  Past the last slice
+  // the loads repeat it and land in a buffer that is not read again.
   auto step = [&](int kt, auto set_c) {
     constexpr int SET = decltype(set_c)::value;
-    load_slice((kt + 2 < nk ? kt + 2 : nk - 1) * kBK, SET);
+    load_slice((kt + NSET < nk ? kt + NSET : nk - 1) * kBK, SET);
     compute(kt);
-    store_slice((kt & 1) ^ 1, SET ^ 1);
+    store_slice((kt & 1) ^ 1, (SET + 1) % NSET);
     __syncthreads();
   };
+  auto steps = [&](int kt, auto count_c) {  // steps kt .. kt+count-1, kt a multiple of NSET
+#pragma unroll
+    for (int j = 0; j < NSET; ++j)
+      if (j < decltype(count_c)::value) {
+        if (j == 0) step(kt, std::integral_constant<int, 0>{});
+        if (j == 1) step(kt + 1, std::integral_constant<int, 1>{});
+        if (j == 2) step(kt + 2, std::integral_constant<int, 2 % NSET>{});
+      }
+  };
 
-  load_slice(0, 0);
-  load_slice((nk > 1 ? 1 : 0) * kBK, 1);
+#pragma unroll
+  for (int j = 0; j < NSET; ++j) load_slice((j < nk ? j : nk - 1) * kBK, j);
   store_slice(0, 0);
   __syncthreads();
   int kt = 0;
 #pragma unroll 1
-  for (; kt + 2 <= nk; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-  }
-  if (kt < nk) compute(kt);
+  for (; kt + NSET < nk; kt += NSET) steps(kt, std::integral_constant<int, NSET>{});
+  // the last 1..NSET slices: a step for each but the last, which only computes
+  if (nk - kt == 2) steps(kt, std::integral_constant<int, 1>{});
+  if (NSET == 3 && nk - kt == 3) steps(kt, std::integral_constant<int, 2>{});
+  compute(nk - 1);
   __syncthreads();
 
   const float* bias = p.bias ? p.bias + (int64_t)g * p.bias_gstride : nullptr;
