@@ -445,6 +445,8 @@ WsPlan cvr::plan_workspace(const cvr_model* m, int64_t R, int64_t n, int64_t P) 
     w.pool_part = take((size_t)(P / kSeqChunk + S * R + 1) * d * 4);
     w.chunk_desc = take((size_t)(P / kSeqChunk + S * R + 1) * 8);
     w.seq_pool = take((size_t)S * R * d * 4);
+    w.pool_bf = take((size_t)S * R * d * lp);
+    w.xq = take((size_t)n * s.n_tokens * d * lp);
     w.query = take((size_t)S * n * d * 4);
     w.mixhid = take((size_t)s.mixer_heads * n * s.mixer_hidden * lp);
     w.experts = take((size_t)n * ((s.n_experts * s.expert_dim + s.n_tasks * s.n_experts + 31) / 32 * 32) * 4);

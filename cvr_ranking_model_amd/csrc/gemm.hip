@@ -286,11 +286,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
                 v.w += r4.w;
               }
               *reinterpret_cast<float4*>(dst) = v;
+              if (p.C2) {
+                typedef T T4 __attribute__((ext_vector_type(4)));
+                T4 vb;
+                vb[0] = Lowp<T>::from_f32(v.x);
+                vb[1] = Lowp<T>::from_f32(v.y);
+                vb[2] = Lowp<T>::from_f32(v.z);
+                vb[3] = Lowp<T>::from_f32(v.w);
+                *reinterpret_cast<T4*>(reinterpret_cast<T*>(p.C2) + (int64_t)m * p.ldc2 + n) = vb;
+              }
             } else {
               const int cnt = p.N - n;
-              dst[0] = res ? v.x + res[0] : v.x;
-              if (cnt > 1) dst[1] = res ? v.y + res[1] : v.y;
-              if (cnt > 2) dst[2] = res ? v.z + res[2] : v.z;
+              const float vv[3] = {v.x, v.y, v.z};
+#pragma unroll
+              for (int e = 0; e < 3; ++e)
+                if (e < cnt) {
+                  const float x = res ? vv[e] + res[e] : vv[e];
+                  dst[e] = x;
+                  if (p.C2) reinterpret_cast<T*>(p.C2)[(int64_t)m * p.ldc2 + n + e] = Lowp<T>::from_f32(x);
+                }
             }
           }
         }
@@ -360,10 +374,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         if (p.R) x += p.r_f32 ? reinterpret_cast<const float*>(p.R)[raddr]
                               : Lowp<T>::to_f32(reinterpret_cast<const T*>(p.R)[raddr]);
         if (p.relu && (p.relu_end == 0 || n < p.relu_end)) x = relu_f32(x);
-        if (p.out_f32)
+        if (p.out_f32) {
           reinterpret_cast<float*>(p.C)[addr] = x;
-        else
+          if (p.C2) reinterpret_cast<T*>(p.C2)[(int64_t)m * p.ldc2 + n] = Lowp<T>::from_f32(x);
+        } else {
           reinterpret_cast<T*>(p.C)[addr] = Lowp<T>::from_f32(x);
+        }
       }
     }
   }
@@ -767,6 +783,7 @@ static hipError_t launch_gemm_t(const GemmParams& p, hipStream_t st) {
   for (int s = 0; s < p.nseg; ++s) bk64 = bk64 && p.seg[s].k_end % 64 == 0;
   const int tile = choose_tile(p, AF32);
   if (p.ow && (tile != 256 || !p.opart || p.opart_ld < p.M)) return hipErrorInvalidValue;  // wide kernel only
+  if (p.C2 && (tile == 256 || !p.out_f32 || p.groups != 1)) return hipErrorInvalidValue;  // small-tile kernel only
   const dim3 blk(256);
   if (tile == 256) {
     if constexpr (AF32) return hipErrorInvalidValue;  // excluded above

@@ -134,6 +134,8 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     g.ldc = (int64_t)T * d;
     g.c_nstride8 = 8;
     g.out_f32 = 1;
+    g.C2 = ws + w.xq;  // the first layer's query input
+    g.ldc2 = (int64_t)N * d;
     e = L(STAGE_TOKENIZE_GEMM, [&] { return launch_gemm(g, lowp, s); });
     if (e != hipSuccess) return e;
   } else {
@@ -164,6 +166,8 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
         g.r_f32 = 1;
         g.r_rowmap = cand_req;
         g.r_ld = (int64_t)N * d;
+        g.C2 = ws + w.xq;  // the first layer's query input
+        g.ldc2 = (int64_t)N * d;
       }
       e = L(STAGE_TOKENIZE_GEMM, [&] { return launch_gemm(g, lowp, s); });
       if (e != hipSuccess) return e;
@@ -219,13 +223,16 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   }
   e = L(STAGE_SEQ_POOL, [&] {
     return launch_seq_pool((const float*)(ws + w.pool_part), chunk_off, b->seq_offsets, R, S, P, max_chunks,
-                           (float*)(ws + w.seq_pool), seq_states_stream(P), s);
+                           (float*)(ws + w.seq_pool), (__bf16*)(ws + w.pool_bf), seq_states_stream(P), s);
   });
   if (e != hipSuccess) return e;
 
   // ---- B6-B9: stacked interaction layers
   int cur = 0;
   bool last_bf16 = false;
+  // the current layer's tokens are in w.xq as bf16 (written by the tokenizer, then by the fused
+  // mixer of the layer before; the grouped-GEMM mixer writes fp32 only)
+  bool xq_ok = true;
   for (int l = 0; l < sp.n_layers; ++l) {
     const std::string Lp = "layer." + S_(l);
     {
@@ -235,8 +242,15 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       g.K = (N + 1) * d;
       g.groups = S;
       g.nseg = 2;
-      g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, N * d, 8, 0, 1};
-      g.seg[1] = ASeg{ws + w.seq_pool, cand_req, d, (int64_t)R * d, (N + 1) * d, 8, 0, 1};
+      // the input [X, pool] as bf16 copies when they exist (the same values the fp32 sources
+      // round to on loading, at half the bytes), else the fp32 sources
+      if (xq_ok) {
+        g.seg[0] = ASeg{ws + w.xq, nullptr, (int64_t)N * d, 0, N * d, 8, 0, 0};
+        g.seg[1] = ASeg{ws + w.pool_bf, cand_req, d, (int64_t)R * d, (N + 1) * d, 8, 0, 0};
+      } else {
+        g.seg[0] = ASeg{tok[cur], nullptr, (int64_t)T * d, 0, N * d, 8, 0, 1};
+        g.seg[1] = ASeg{ws + w.seq_pool, cand_req, d, (int64_t)R * d, (N + 1) * d, 8, 0, 1};
+      }
       g.W = m->wptr(Lp + ".query.0.weight");
       g.w_gstride = group_stride(m, [&](int i) { return Lp + ".query." + S_(i) + ".weight"; }, S, 2);
       g.bias = (const float*)m->wptr(Lp + ".query.0.bias");
@@ -282,6 +296,11 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       // keep fp32 so that the token matrix can be exported.
       if (l == sp.n_layers - 1 && !m->debug) t.Zb = (__bf16*)tok[1 - cur];
       last_bf16 = t.Zb != nullptr;
+      if (l < sp.n_layers - 1) {  // the next layer's query input
+        t.Xq = (__bf16*)(ws + w.xq);
+        t.Nq = N;
+      }
+      xq_ok = l < sp.n_layers - 1;
       t.n = n;
       t.T = T;
       t.d = d;
@@ -344,6 +363,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
         e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
         if (e != hipSuccess) return e;
       }
+      xq_ok = false;
     }
     m->last_attn_tok = cur;
     cur = 1 - cur;

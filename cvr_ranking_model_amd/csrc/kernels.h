@@ -230,6 +230,11 @@ struct GemmParams {
   // 1: when N <= 128, one 64 x 128 tile covers a group's whole width, so each group reads its
   // A rows once (pays when A is shared and cache-resident, e.g. many candidates per request)
   int32_t full_n;
+  // With an fp32 output (small-tile kernel, one group): if set, every output element is also
+  // written here rounded to the low-precision type, row m at C2 + m * ldc2 -- the input a later
+  // Linear would round it to on loading, at half the bytes.
+  void* C2;
+  int64_t ldc2;
 };
 hipError_t launch_gemm(const GemmParams& p, int lowp, hipStream_t st);
 // True when launch_gemm runs p on the wide kernel, which can take the output-layer fusion.
@@ -290,8 +295,10 @@ hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st);
 // without.  Smaller ones are kept cacheable, since the attention then finds them in that cache.
 constexpr int64_t kStateStreamBytes = 256LL << 20;
 inline bool seq_states_stream(int64_t n_positions) { return n_positions * 128 * 2 >= kStateStreamBytes; }
+// pool_bf: if set, the pools are also written there rounded to bf16 (the query Linear's input).
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
-                           int64_t n_positions, int32_t max_chunks, float* pool, bool nt, hipStream_t st);
+                           int64_t n_positions, int32_t max_chunks, float* pool, __bf16* pool_bf, bool nt,
+                           hipStream_t st);
 
 // ---------------------------------------------------------------- attention (B7)
 struct AttnParams {
@@ -319,6 +326,8 @@ struct TokenMixParams {
   const float* Y;               // [n][T][d] fp32
   float* Z;                     // [n][T][d] fp32
   __bf16* Zb;                   // if set: Z is written here as bf16 instead (Z unused)
+  __bf16* Xq;                   // if set (with Z): tokens t < Nq also written here as bf16, [n][Nq][d]
+  int32_t Nq;
   int32_t n, T, d, H;
   const __bf16* W1;             // head h: W1 + h*w1_gstride, [256][T*8] packed by launch_mix_pack
   int64_t w1_gstride;

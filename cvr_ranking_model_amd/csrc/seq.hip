@@ -511,7 +511,7 @@ template <bool kNT>
 __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_off,
                                                        const int32_t* __restrict__ seq_offsets, int R, int S,
                                                        int64_t n_positions, int32_t max_chunks,
-                                                       float* __restrict__ pool) {
+                                                       float* __restrict__ pool, bf16* __restrict__ pool_bf) {
   const int lane = threadIdx.x & 63;
   // the last sequence's segments (the longest) first
   const int g = R * S - 1 - (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -576,18 +576,27 @@ __global__ __launch_bounds__(256) void seq_pool_kernel(const float* __restrict__
     const float len = (float)(e - a);
     const float4 o = e > a ? make_float4(acc.x / len, acc.y / len, acc.z / len, acc.w / len) : make_float4(0.f, 0.f, 0.f, 0.f);
     *reinterpret_cast<float4*>(pool + (int64_t)g * kD + 4 * q) = o;
+    if (pool_bf) {
+      bf16x4 ob;
+      ob[0] = (bf16)o.x;
+      ob[1] = (bf16)o.y;
+      ob[2] = (bf16)o.z;
+      ob[3] = (bf16)o.w;
+      *reinterpret_cast<bf16x4*>(pool_bf + (int64_t)g * kD + 4 * q) = ob;
+    }
   }
 }
 
 hipError_t launch_seq_pool(const float* part, const int32_t* chunk_off, const int32_t* seq_offsets, int R, int S,
-                           int64_t n_positions, int32_t max_chunks, float* pool, bool nt, hipStream_t st) {
+                           int64_t n_positions, int32_t max_chunks, float* pool, __bf16* pool_bf, bool nt,
+                           hipStream_t st) {
   if (R * S <= 0) return hipSuccess;
   if (nt)
     launch_k(seq_pool_kernel<true>, dim3((R * S + 3) / 4), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S,
-             n_positions, max_chunks, pool);
+             n_positions, max_chunks, pool, pool_bf);
   else
     launch_k(seq_pool_kernel<false>, dim3((R * S + 3) / 4), dim3(256), 0, st, part, chunk_off, seq_offsets, R, S,
-             n_positions, max_chunks, pool);
+             n_positions, max_chunks, pool, pool_bf);
   return hipGetLastError();
 }
 
