@@ -230,9 +230,6 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   // ---- B6-B9: stacked interaction layers
   int cur = 0;
   bool last_bf16 = false;
-  // the current layer's tokens are in w.xq as bf16 (written by the tokenizer, then by the fused
-  // mixer of the layer before; the grouped-GEMM mixer writes fp32 only)
-  bool xq_ok = true;
   for (int l = 0; l < sp.n_layers; ++l) {
     const std::string Lp = "layer." + S_(l);
     {
@@ -242,9 +239,11 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       g.K = (N + 1) * d;
       g.groups = S;
       g.nseg = 2;
-      // the input [X, pool] as bf16 copies when they exist (the same values the fp32 sources
-      // round to on loading, at half the bytes), else the fp32 sources
-      if (xq_ok) {
+      // the first layer reads [X, pool] from the bf16 copies the tokenizer and the pool kernel
+      // wrote (the same values the fp32 sources round to on loading, at half the bytes); later
+      // layers read the mixer's fp32 tokens (a bf16 copy from the mixer cost it more than the
+      // query GEMM saved)
+      if (l == 0) {
         g.seg[0] = ASeg{ws + w.xq, nullptr, (int64_t)N * d, 0, N * d, 8, 0, 0};
         g.seg[1] = ASeg{ws + w.pool_bf, cand_req, d, (int64_t)R * d, (N + 1) * d, 8, 0, 0};
       } else {
@@ -296,11 +295,6 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       // keep fp32 so that the token matrix can be exported.
       if (l == sp.n_layers - 1 && !m->debug) t.Zb = (__bf16*)tok[1 - cur];
       last_bf16 = t.Zb != nullptr;
-      if (l < sp.n_layers - 1) {  // the next layer's query input
-        t.Xq = (__bf16*)(ws + w.xq);
-        t.Nq = N;
-      }
-      xq_ok = l < sp.n_layers - 1;
       t.n = n;
       t.T = T;
       t.d = d;
@@ -363,7 +357,6 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
         e = L(STAGE_MIXER_GEMM, [&] { return launch_gemm(g, lowp, s); });
         if (e != hipSuccess) return e;
       }
-      xq_ok = false;
     }
     m->last_attn_tok = cur;
     cur = 1 - cur;

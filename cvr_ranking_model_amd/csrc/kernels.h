@@ -326,8 +326,6 @@ struct TokenMixParams {
   const float* Y;               // [n][T][d] fp32
   float* Z;                     // [n][T][d] fp32
   __bf16* Zb;                   // if set: Z is written here as bf16 instead (Z unused)
-  __bf16* Xq;                   // if set (with Z): tokens t < Nq also written here as bf16, [n][Nq][d]
-  int32_t Nq;
   int32_t n, T, d, H;
   const __bf16* W1;             // head h: W1 + h*w1_gstride, [256][T*8] packed by launch_mix_pack
   int64_t w1_gstride;

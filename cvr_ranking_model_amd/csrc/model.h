@@ -61,8 +61,8 @@ struct WsPlan {
   size_t tok[2] = {0, 0}, hseq = 0, chunk_off = 0, chunk_desc = 0, pool_part = 0, seq_pool = 0, query = 0,
          mixhid = 0, experts = 0, gates = 0, task_in = 0, head_hid = 0, tok_req = 0;
   size_t ep_h = 0, ep_g = 0, x_ep = 0;  // CVR with EPNet: gate hidden, gate pre-activations, scaled input
-  // CVR: the query Linear's inputs as bf16 -- the current layer's N tokens [n][N][d] and the
-  // pools [S][R][d] -- written beside their fp32 forms by the stages that produce them
+  // CVR: the first layer's query Linear inputs as bf16 -- the tokenizer's N tokens [n][N][d] and
+  // the pools [S][R][d] -- written beside their fp32 forms by the stages that produce them
   size_t xq = 0, pool_bf = 0;
   size_t total = 0;
 };

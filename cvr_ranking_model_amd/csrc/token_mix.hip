@@ -180,11 +180,6 @@ __global__ __launch_bounds__(512) void token_mix_kernel(const TokenMixParams p, 
             *reinterpret_cast<bf16x4*>(p.Zb + zo) = zb;
           } else {
             *reinterpret_cast<float4*>(p.Z + zo) = z;
-            if (p.Xq && t < p.Nq) {  // the next layer's query input, rounded as it would round it
-              bf16x4 zb;
-              zb[0] = (bf16)z.x; zb[1] = (bf16)z.y; zb[2] = (bf16)z.z; zb[3] = (bf16)z.w;
-              *reinterpret_cast<bf16x4*>(p.Xq + ((int64_t)c * p.Nq + t) * p.d + h * hw + j) = zb;
-            }
           }
         }
       }
