@@ -1101,6 +1101,10 @@ extern "C" cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value
         return fail(h, CVR_ERR_UNSUPPORTED, "fused heads need a CVR spec with expert and head widths of at most 256, at most 4 experts and 4 tasks");
       h->opt_heads_fused = (int)value;
       break;
+    case CVR_OPT_STATE_STREAM:
+      if (value < -1 || value > 1) return fail(h, CVR_ERR_ARG, "state streaming must be -1, 0 or 1");
+      h->opt_state_stream = (int)value;
+      break;
     default: return fail(h, CVR_ERR_ARG, "unknown option");
   }
   h->graph.reset();  // a captured graph baked in the previous choice

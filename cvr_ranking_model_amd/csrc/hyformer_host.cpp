@@ -175,6 +175,8 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
   }
 
   // ---- B3-B5: sequence encoding and mean pools (per request)
+  // encoded states larger than the last-level cache go out and come back with nontemporal hints
+  const bool stream_states = m->opt_state_stream < 0 ? seq_states_stream(P) : m->opt_state_stream != 0;
   int32_t* chunk_off = (int32_t*)(ws + w.chunk_off);
   // every segment adds at most one partial chunk; the workspace holds this many
   const int max_chunks = (int)(P / kSeqChunk) + S * R;
@@ -217,13 +219,13 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
     p.H = (__bf16*)(ws + w.hseq);
     p.part = (float*)(ws + w.pool_part);
     p.flag = flag;
-    p.nt = seq_states_stream(P);
+    p.nt = stream_states;
     e = L(STAGE_SWIGLU, [&] { return launch_swiglu(p, max_chunks, s); });
     if (e != hipSuccess) return e;
   }
   e = L(STAGE_SEQ_POOL, [&] {
     return launch_seq_pool((const float*)(ws + w.pool_part), chunk_off, b->seq_offsets, R, S, P, max_chunks,
-                           (float*)(ws + w.seq_pool), (__bf16*)(ws + w.pool_bf), seq_states_stream(P), s);
+                           (float*)(ws + w.seq_pool), (__bf16*)(ws + w.pool_bf), stream_states, s);
   });
   if (e != hipSuccess) return e;
 
@@ -281,7 +283,7 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       a.T = T;
       a.N = N;
       a.mq = m->opt_attn_mq < 0 ? attention_many_candidates(n, R) : m->opt_attn_mq != 0;
-      a.nt = seq_states_stream(P);
+      a.nt = stream_states;
       e = L(STAGE_ATTENTION, [&] { return launch_attention(a, s); });
       if (e != hipSuccess) return e;
     }

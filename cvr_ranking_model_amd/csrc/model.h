@@ -153,6 +153,7 @@ struct cvr_model {
   int opt_attn_mq = -1;    // CVR_OPT_ATTN_MQ: -1 auto, 0 per candidate, 1 MFMA per request
   int opt_user_block = -1; // CVR_OPT_DLRM_USER_BLOCK: -1 auto (off), 0 off, 1 on
   int opt_heads_fused = -1; // CVR_OPT_HEADS_FUSED: -1 auto (fused when the widths allow), 0 off, 1 on
+  int opt_state_stream = -1; // CVR_OPT_STATE_STREAM: -1 auto (seq_states_stream), 0 off, 1 on
   std::string err;
   char* last_ws = nullptr;
   cvr::WsPlan last_plan;

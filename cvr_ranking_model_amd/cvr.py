@@ -24,7 +24,8 @@ CVR_SIDE_USER, CVR_SIDE_ITEM, CVR_SIDE_CONTEXT = 0, 1, 2
 CVR_LOWP_FP16, CVR_LOWP_BF16 = 0, 1
 (CVR_DBG_CAND_REQ, CVR_DBG_POOLED, CVR_DBG_INPUT_REQ, CVR_DBG_INPUT_ITEM, CVR_DBG_LOGITS, CVR_DBG_HSEQ,
  CVR_DBG_SEQ_POOL, CVR_DBG_TOKENS, CVR_DBG_QUERY, CVR_DBG_ATTN, CVR_DBG_HIDDEN, CVR_DBG_EPNET) = range(12)
-CVR_OPT_DLRM_PASS_ROWS, CVR_OPT_TOK_SHARE, CVR_OPT_ATTN_MQ, CVR_OPT_DLRM_USER_BLOCK, CVR_OPT_HEADS_FUSED = range(5)
+(CVR_OPT_DLRM_PASS_ROWS, CVR_OPT_TOK_SHARE, CVR_OPT_ATTN_MQ, CVR_OPT_DLRM_USER_BLOCK, CVR_OPT_HEADS_FUSED,
+ CVR_OPT_STATE_STREAM) = range(6)
 SIDES = {"user": CVR_SIDE_USER, "item": CVR_SIDE_ITEM, "context": CVR_SIDE_CONTEXT}
 
 

@@ -262,8 +262,8 @@ cvr_status cvr_graph_workspace_bytes(cvr_handle h, int32_t max_requests, int32_t
 cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures);
 
 /* Kernel-selection options of a model.  Each has a default that scoring uses unless the option
- * is set; scores do not depend on them beyond the order of fp32 additions (DLRM_PASS_ROWS: not
- * at all).  Setting an option discards a graph captured by cvr_score_graph.  Values:
+ * is set; scores do not depend on them beyond the order of fp32 additions (DLRM_PASS_ROWS and
+ * STATE_STREAM: not at all).  Setting an option discards a graph captured by cvr_score_graph.  Values:
  *   CVR_OPT_DLRM_PASS_ROWS  DLRM: candidates per MLP pass (each pass through every layer before
  *                           the next).  -1 (default): as many as fill 128 MB per activation
  *                           buffer (65536 at width 1024); 0: one pass; k > 0: k candidates.
@@ -284,13 +284,19 @@ cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures)
  *                           three separate launches.  -1 (default) and 1: fused when expert_dim
  *                           and head_hidden are at most 256, with at most 4 experts and 4 tasks
  *                           (1 beyond that: CVR_ERR_UNSUPPORTED); 0: three launches.
+ *   CVR_OPT_STATE_STREAM    CVR: the encoded sequence states (and the encoder's per-chunk pool
+ *                           partials) written, and read by the pool and the per-candidate
+ *                           attention, with nontemporal hints.  A cache policy only: results do
+ *                           not depend on it at all.  -1 (default): when the states take 256 MB
+ *                           or more (they then outsize the last-level cache); 0: never; 1: always.
  * Unknown options and values outside these ranges return CVR_ERR_ARG. */
 enum {
   CVR_OPT_DLRM_PASS_ROWS = 0,
   CVR_OPT_TOK_SHARE = 1,
   CVR_OPT_ATTN_MQ = 2,
   CVR_OPT_DLRM_USER_BLOCK = 3,
-  CVR_OPT_HEADS_FUSED = 4
+  CVR_OPT_HEADS_FUSED = 4,
+  CVR_OPT_STATE_STREAM = 5
 };
 cvr_status cvr_set_option(cvr_handle h, int32_t option, int64_t value);
 

@@ -309,6 +309,33 @@ def test_six_sequence_columns():
     check_cvr(spec, m, synth.make_batch(spec, requests=6), "stress")
 
 
+@pytest.mark.parametrize("name,requests", [("c3", 16), ("c4", 4096)])
+def test_state_streaming_is_a_cache_policy_only(name, requests):
+    """Nontemporal hints on the encoded states (CVR_OPT_STATE_STREAM) change where the states are
+    cached, never a value: scores (and at C3 the states and pools) are bit-identical with the
+    hints by default, forced off and forced on.  C4 at 4,096 samples uses them by default, C3
+    does not."""
+    spec = synth.load_spec(name)
+    debug = name == "c3"
+    banner(f"{name} stress, {requests} samples: state streaming default / off / on")
+    m, _ = build_model(spec, "stress", debug=debug)
+    b = synth.make_batch(spec, requests=requests)
+    P = int(b["seq_ids"].shape[0])
+    got = []
+    for v in (-1, 0, 1):
+        m.set_option(cv.CVR_OPT_STATE_STREAM, v)
+        db, out, st = run(m, b)
+        assert st == cv.CVR_OK
+        bits = [out.cpu().numpy().view(np.uint32).copy()]
+        if debug:
+            bits.append(m.export(cv.CVR_DBG_HSEQ, torch.bfloat16, (P, spec["d"])).cpu().view(torch.int16).numpy().copy())
+            bits.append(m.export(cv.CVR_DBG_SEQ_POOL, torch.float32, (3, db.n_requests, spec["d"])).cpu().numpy().view(np.uint32).copy())
+        got.append(bits)
+    for other in got[1:]:
+        assert all(np.array_equal(a, o) for a, o in zip(got[0], other))
+    m.close()
+
+
 def test_one_user_many_candidates():
     spec = synth.load_spec("c3")
     banner("c3 1 user + 500 candidates: 2 requests x 500, sequences once per request, oracle on request 1")
