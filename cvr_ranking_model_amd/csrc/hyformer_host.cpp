@@ -283,7 +283,10 @@ hipError_t run_hyformer(cvr_model* m, const cvr_batch* b, char* ws, const WsPlan
       a.T = T;
       a.N = N;
       a.mq = m->opt_attn_mq < 0 ? attention_many_candidates(n, R) : m->opt_attn_mq != 0;
-      a.nt = stream_states;
+      // nontemporal loads from the second layer on: the first layer reads the states right after
+      // the encoder wrote them, and there plain loads measured faster (C4: 607 against 643 us;
+      // the second layer 522 us with the hint)
+      a.nt = stream_states && l > 0;
       e = L(STAGE_ATTENTION, [&] { return launch_attention(a, s); });
       if (e != hipSuccess) return e;
     }

@@ -290,9 +290,10 @@ struct SwigluParams {
 };
 hipError_t launch_swiglu(const SwigluParams& p, int max_chunks, hipStream_t st);
 // Encoded states that outsize the last-level cache (256 MB on MI355X) are written, and read by the
-// pool and the per-candidate attention, with nontemporal hints: they cannot stay cached between
-// the launches anyway, and a streaming read runs at about 7.0 TB/s with the hint against 6.3
-// without.  Smaller ones are kept cacheable, since the attention then finds them in that cache.
+// pool and the per-candidate attention of the second and later layers, with nontemporal hints:
+// they cannot stay cached between the launches anyway, and a streaming read runs at about
+// 7.0 TB/s with the hint against 6.3 without.  Smaller ones are kept cacheable, since the
+// attention then finds them in that cache.
 constexpr int64_t kStateStreamBytes = 256LL << 20;
 inline bool seq_states_stream(int64_t n_positions) { return n_positions * 128 * 2 >= kStateStreamBytes; }
 // pool_bf: if set, the pools are also written there rounded to bf16 (the query Linear's input).

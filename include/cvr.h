@@ -285,8 +285,8 @@ cvr_status cvr_graph_info(cvr_handle h, int64_t* graphs_held, int64_t* captures)
  *                           and head_hidden are at most 256, with at most 4 experts and 4 tasks
  *                           (1 beyond that: CVR_ERR_UNSUPPORTED); 0: three launches.
  *   CVR_OPT_STATE_STREAM    CVR: the encoded sequence states (and the encoder's per-chunk pool
- *                           partials) written, and read by the pool and the per-candidate
- *                           attention, with nontemporal hints.  A cache policy only: results do
+ *                           partials) written, and read by the pool and by the per-candidate
+ *                           attention of the second and later layers, with nontemporal hints.  A cache policy only: results do
  *                           not depend on it at all.  -1 (default): when the states take 256 MB
  *                           or more (they then outsize the last-level cache); 0: never; 1: always.
  * Unknown options and values outside these ranges return CVR_ERR_ARG. */
